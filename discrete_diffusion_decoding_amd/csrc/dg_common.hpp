@@ -1,0 +1,78 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels of libdg.
+//
+// bf16 values travel as raw uint16_t bit patterns; arithmetic is fp32.
+// MFMA: v_mfma_f32_16x16x32_bf16.  Operand convention used everywhere:
+//   A (16 x 32): lane l holds row (l % 16), k-slots 8*(l/16) .. +7
+//   B (32 x 16): lane l holds col (l % 16), k-slots 8*(l/16) .. +7
+//   D (16 x 16): lane l holds rows 4*(l/16) + i (i = 0..3), col (l % 16)
+// Only the pairing of A's and B's k-slots matters for the contraction, so a
+// kernel may map any 32 contraction indices onto the slots as long as A and
+// B use the same map.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;
+
+#define DG_WAVE 64
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const bf16_t* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, DG_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, DG_WAVE));
+  return v;
+}
+
+// block-wide sum for blockDim.x a multiple of 64 (<= 1024); deterministic order.
+__device__ __forceinline__ float block_sum(float v, float* red /* >= 16 floats */) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / DG_WAVE, l = threadIdx.x % DG_WAVE;
+  const int nw = blockDim.x / DG_WAVE;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = k0 * (x + 0.044715f * x * x * x);
+  // tanh(u) = 1 - 2 / (exp(2u) + 1), saturating correctly at both ends
+  float t = 1.0f - 2.0f / (__expf(2.0f * u) + 1.0f);
+  return 0.5f * x * (1.0f + t);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }

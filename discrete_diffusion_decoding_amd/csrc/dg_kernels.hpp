@@ -1,0 +1,117 @@
+// Launch interface of libdg's HIP kernels (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dg_common.hpp"
+
+namespace dg {
+
+enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_ADD_F32 = 2, EPI_ADD_GATED_F32 = 3, EPI_GEGLU_BF16 = 4 };
+
+// C[r, n] (op)= sum_k A[row(r), k] * W_g[n, k] for r in the rows of group g.
+// A: bf16 rows of pitch lda; row(r) = a_rows ? a_rows[r] : r.
+// W: bf16 [N, ldw] per group, groups w_gstride elements apart (W2 likewise for GEGLU).
+// Groups: rows [group_off[g], group_off[g+1]) (or [0, M) with one group).
+// Rows are processed in chunks of 16*MF; `m_split` lanes of work share a group's
+// chunks.  Split-K: `k_split` ranges of `k_chunk`, partial outputs c_kstride apart.
+struct GemmArgs {
+  const bf16_t* A;
+  long lda;
+  const int32_t* a_rows;
+  const bf16_t* W;
+  const bf16_t* W2;
+  long ldw;
+  long w_gstride;
+  int K, N;
+  int k_chunk;
+  const int32_t* group_off;
+  int M;
+  int G;
+  int m_split;
+  int k_split;
+  void* C;
+  long ldc;
+  long c_kstride;
+  const bf16_t* col_gate;
+  const int32_t* flag;
+};
+
+hipError_t gemm(int epi, int mf, const GemmArgs& a, hipStream_t s);
+
+// ---- elementwise / reduction kernels (k_elem.hip) ----
+struct RowsCtx {
+  int rows;        // token rows in this pass
+  int per_batch;   // rows per batch element (T for the canvas, chunk for prefill)
+  int pos0;        // absolute position of the first row of each batch element
+};
+
+hipError_t embed_rows(const int32_t* tokens, const bf16_t* E, int rows, int d, float* h,
+                      const int32_t* flag, hipStream_t s);
+// out = bf16(rms(h) * w); optional hi/lo split rows for the router, optional dump of h
+hipError_t rmsnorm_rows(const float* h, const bf16_t* w, int rows, int d, float eps, bf16_t* out,
+                        bf16_t* split_hi_lo, float* dump, const int32_t* flag, hipStream_t s);
+// per-head RMSNorm + RoPE of q and k, scatter of k / v into the attention caches
+struct QkRopeArgs {
+  const bf16_t* qkv; int rows; int H, Hkv, hd; float eps; float theta;
+  const bf16_t* qnorm; const bf16_t* knorm;
+  bf16_t* q;                        // [rows][H][hd]
+  int per_batch, pos0;              // position of row r = pos0 + (r % per_batch)
+  bf16_t* kdst; long k_bstride, k_hstride;            // K rows [.][Hkv][pitch][hd]
+  bf16_t* vtdst; long v_bstride, v_hstride, v_pitch;  // V^T [.][Hkv][hd][pitch]
+  int t_offset;                     // index of row 0 within the destination sequence
+  const int32_t* flag;
+};
+hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const bf16_t* q; int H, Hkv, hd; float scale;
+  int rows_per_batch; int B;
+  // key source 1 (cache) and 2 (canvas); batch b reads source-1 element b1 = (nb1 == 1 ? 0 : b)
+  const bf16_t* k1; const bf16_t* vt1; long k1_bstride, k1_hstride, v1_bstride, v1_hstride, v1_pitch; int n1; int nb1;
+  const bf16_t* k2; const bf16_t* vt2; long k2_bstride, k2_hstride, v2_bstride, v2_hstride, v2_pitch; int n2;
+  int causal; int qpos0;            // causal: query row r (within batch) sits at qpos0 + r
+  int splits; int split_len;        // key splits (split_len multiple of 32)
+  float* opart; float* mlpart;      // [splits][B*rows][H][hd], [splits][B*rows][H][2]
+  const int32_t* flag;
+};
+hipError_t attention(const AttnArgs& a, hipStream_t s);
+hipError_t attention_merge(const float* opart, const float* mlpart, int splits, int rows, int H, int hd,
+                           bf16_t* out, const int32_t* flag, hipStream_t s);
+
+hipError_t router_topk(const float* rlog, int rows, int E, int k, int32_t* idx, float* gate,
+                       int32_t* idx_dump, float* gate_dump, const int32_t* flag, hipStream_t s);
+hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* counts, int32_t* offsets,
+                       int32_t* slot_of, int32_t* slot_row, const int32_t* flag, hipStream_t s);
+// h[r] += ys[r] + sum_j gate[r,j] * Y[slot_of[r,j]]; then optional next RMSNorm -> xn, dump of h
+hipError_t moe_combine(float* h, const float* ys, const float* Y, const int32_t* slot_of, const float* gate,
+                       int rows, int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump,
+                       const int32_t* flag, hipStream_t s);
+
+// ---- LM head / sampler (k_head.hip) ----
+struct SampleArgs {
+  const float* logits; int B, T, V; long ldl;
+  int step_arg;                     // >= 0: this step; < 0: read steps[b]
+  float tau_start, tau_end; int max_steps;
+  int lock_rule; float lock_thresh; int stop_rule; float stop_thresh;
+  uint64_t seeds[16];
+  int vsplit;                       // vocab slices per row
+  float* part;                      // [B*T][vsplit][8]
+  float* rowstat;                   // [B*T][2]: max, Z (softmax of the logits)
+  int32_t* tokens; uint8_t* locked; float* entropy; int32_t* xhat; int32_t* argmax;
+  int32_t* stopped; int32_t* steps; int32_t* all_stopped;
+  const int32_t* flag;
+};
+hipError_t sample_partial(const SampleArgs& a, hipStream_t s);
+hipError_t sample_finish(const SampleArgs& a, hipStream_t s);
+hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,
+                         const int32_t* flag, hipStream_t s);
+hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out,
+                             const int32_t* stopped, int T, const int32_t* flag, hipStream_t s);
+hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* seeds, hipStream_t s);
+hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
+hipError_t fill_u16(uint16_t* p, uint16_t v, long n, hipStream_t s);
+hipError_t set_step(int32_t* steps, int B, int step, hipStream_t s);
+hipError_t transpose_bf16(const bf16_t* in, bf16_t* out, long rows, long cols, hipStream_t s);
+
+}  // namespace dg

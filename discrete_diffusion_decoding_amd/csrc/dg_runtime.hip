@@ -1,0 +1,679 @@
+// libdg host runtime: argument checks, workspace planning and the launch
+// sequence of the denoising step (C ABI declared in include/dg.h).
+//
+// Step structure (DiffusionGemma, laozijiushiniubi article sections 2 and 4):
+//   embed canvas tokens (+ gated self-conditioning projection of s_prev)
+//   for each layer: RMSNorm -> QKV -> QK-norm + RoPE -> attention over
+//     (cached prefix, bidirectional canvas) -> O projection + residual ->
+//     RMSNorm -> router top-k -> expert permutation -> grouped expert FFNs
+//     (+ shared FFN) -> weighted combine + residual (fused with the next norm)
+//   final norm -> LM head -> entropy / Gumbel-max / lock / re-randomise / stop
+//   -> soft-prediction embedding s_next = softmax(logits) E
+// Nothing here allocates device memory; every buffer is carved out of the
+// caller's workspace.
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "dg.h"
+#include "dg_kernels.hpp"
+#include "dg_rng.hpp"
+
+using namespace dg;
+
+struct dg_model {
+  dg_model_desc d;
+  dg_weights w;
+  std::vector<const bf16_t*> layers;
+  dg_layer_layout lay;
+};
+
+#define DG_CK(x)                                                        \
+  do {                                                                  \
+    hipError_t e_ = (x);                                                \
+    if (e_ != hipSuccess) {                                             \
+      fprintf(stderr, "libdg: %s failed: %s\n", #x, hipGetErrorString(e_)); \
+      return DG_ERR_HIP;                                                \
+    }                                                                   \
+  } while (0)
+
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+static size_t al128e(size_t x) { return (x + 127) & ~(size_t)127; }
+static int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+extern "C" const char* dg_status_string(dg_status s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_ARG: return "invalid argument";
+    case DG_ERR_SHAPE: return "unsupported shape";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_HIP: return "HIP error";
+    case DG_ERR_UNSUPPORTED: return "unsupported request";
+  }
+  return "unknown status";
+}
+
+static dg_status check_desc(const dg_model_desc* d) {
+  if (!d) return DG_ERR_ARG;
+  if (d->n_layers < 1 || d->d_model < 64 || d->n_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 ||
+      d->n_experts < 1 || d->top_k < 1 || d->d_expert < 1 || d->d_shared < 0 || d->vocab < 0 ||
+      (d->self_cond != 0 && d->self_cond != 1) || !(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f))
+    return DG_ERR_ARG;
+  const int gq = d->n_heads % d->n_kv_heads == 0 ? d->n_heads / d->n_kv_heads : 0;
+  if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256) return DG_ERR_SHAPE;
+  if (gq != 1 && gq != 2 && gq != 4) return DG_ERR_SHAPE;
+  if (d->d_model % 64 || d->d_model > 4096 || d->d_expert % 64 || d->d_shared % 64 ||
+      (d->n_heads * d->head_dim) % 64)
+    return DG_ERR_SHAPE;
+  if (d->n_experts > 255 || d->top_k > 16 || d->top_k > d->n_experts) return DG_ERR_SHAPE;
+  if (d->vocab % 128) return DG_ERR_SHAPE;
+  if (d->self_cond && d->vocab == 0) return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+extern "C" dg_status dg_layer_layout_get(const dg_model_desc* d, dg_layer_layout* o) {
+  dg_status st = check_desc(d);
+  if (st != DG_OK) return st;
+  if (!o) return DG_ERR_ARG;
+  const size_t D = d->d_model, hd = d->head_dim, E = d->n_experts, fe = d->d_expert, fs = d->d_shared;
+  const size_t qkv = (size_t)(d->n_heads + 2 * d->n_kv_heads) * hd;
+  size_t p = 0;
+  auto take = [&](size_t n) { size_t r = p; p = al128e(p + n); return r; };
+  o->attn_norm = take(D);
+  o->w_qkv = take(qkv * D);
+  o->q_norm = take(hd);
+  o->k_norm = take(hd);
+  o->w_o = take(D * d->n_heads * hd);
+  o->ffn_norm = take(D);
+  o->w_router = take(E * D);
+  o->w_gate = take(E * fe * D);
+  o->w_up = take(E * fe * D);
+  o->w_down = take(E * D * fe);
+  o->w_gate_sh = take(fs * D);
+  o->w_up_sh = take(fs * D);
+  o->w_down_sh = take(D * fs);
+  o->total = p;
+  return DG_OK;
+}
+
+extern "C" dg_status dg_model_create(const dg_model_desc* d, const dg_weights* w, dg_model** out) {
+  dg_status st = check_desc(d);
+  if (st != DG_OK) return st;
+  if (!w || !out || !w->layers) return DG_ERR_ARG;
+  if (d->vocab && (!w->embed || !w->final_norm)) return DG_ERR_ARG;
+  if (d->self_cond && (!w->self_cond_w || !w->self_cond_gate || !w->embed_t)) return DG_ERR_ARG;
+  for (int l = 0; l < d->n_layers; ++l)
+    if (!w->layers[l]) return DG_ERR_ARG;
+  dg_model* m = new dg_model();
+  m->d = *d;
+  m->w = *w;
+  m->layers.resize(d->n_layers);
+  for (int l = 0; l < d->n_layers; ++l) m->layers[l] = (const bf16_t*)w->layers[l];
+  m->w.layers = nullptr;
+  dg_layer_layout_get(d, &m->lay);
+  *out = m;
+  return DG_OK;
+}
+
+extern "C" void dg_model_destroy(dg_model* m) { delete m; }
+
+extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
+  if (!m || Bp < 1 || P_max < 0) return 0;
+  const dg_model_desc& d = m->d;
+  return (size_t)d.n_layers * 2 * Bp * d.n_kv_heads * (size_t)P_max * d.head_dim * sizeof(bf16_t);
+}
+
+// ---------------------------------------------------------------------------
+// workspace plan
+struct Plan {
+  size_t h, xn, qkv, q, kc, vc, opart, ml, o, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, hbuf, ybuf,
+      hs, ys, logits, spart, rowstat, P, separt, flag, total;
+  int splits_max, vsplit, ksplit, kchunk;
+};
+
+static const int kMaxSplits = 16;
+
+static void soft_split(const dg_model_desc& d, int rows, int* ksplit, int* kchunk) {
+  const int items = cdiv(d.d_model, 128) * cdiv(rows, 64);
+  int ks = std::max(1, std::min(32, cdiv(1024, items)));
+  int kc = cdiv(cdiv(d.vocab, ks), 64) * 64;
+  *kchunk = kc;
+  *ksplit = cdiv(d.vocab, kc);
+}
+
+static int vsplit_of(int rows, int V) {
+  const int groups = std::max(1, rows / 4);
+  int vs = std::max(1, std::min(64, cdiv(2048, groups)));
+  while (vs > 1 && V / vs < 1024) vs >>= 1;
+  return vs;
+}
+
+static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
+  Plan p{};
+  const size_t R = rows, D = d.d_model, hd = d.head_dim, H = d.n_heads, Hkv = d.n_kv_heads, E = d.n_experts,
+               k = d.top_k, V = d.vocab;
+  const size_t qkvd = (H + 2 * Hkv) * hd;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = al256(o + bytes); return r; };
+  (void)keys;
+  p.splits_max = kMaxSplits;
+  p.h = take(R * D * 4);
+  p.xn = take(R * D * 2);
+  p.qkv = take(R * qkvd * 2);
+  p.q = take(R * H * hd * 2);
+  p.kc = take(R * Hkv * hd * 2);
+  p.vc = take(R * Hkv * hd * 2);
+  p.opart = take((size_t)kMaxSplits * R * H * hd * 4);
+  p.ml = take((size_t)kMaxSplits * R * H * 2 * 4);
+  p.o = take(R * H * hd * 2);
+  p.xn2 = take(R * D * 2);
+  p.xr = take(2 * R * D * 2);
+  p.rlog = take(2 * R * E * 4);
+  p.eidx = take(R * k * 4);
+  p.egate = take(R * k * 4);
+  p.cnt = take((E + 1) * 4);
+  p.off = take((E + 1) * 4);
+  p.slot_of = take(R * k * 4);
+  p.slot_row = take(R * k * 4);
+  p.hbuf = take(R * k * d.d_expert * 2);
+  p.ybuf = take(R * k * D * 4);
+  p.hs = take(R * std::max(d.d_shared, 1) * 2);
+  p.ys = take(d.d_shared ? R * D * 4 : 0);
+  if (V) {
+    p.vsplit = vsplit_of(rows, (int)V);
+    p.logits = take(R * V * 4);
+    p.spart = take(R * p.vsplit * 8 * 4);
+    p.rowstat = take(R * 2 * 4);
+    if (d.self_cond) {
+      soft_split(d, rows, &p.ksplit, &p.kchunk);
+      p.P = take(R * V * 2);
+      p.separt = take((size_t)p.ksplit * R * D * 4);
+    }
+  }
+  p.flag = take(64);
+  p.total = o;
+  return p;
+}
+
+extern "C" size_t dg_workspace_bytes(const dg_model* m, int32_t rows, int32_t keys) {
+  if (!m || rows < 1 || keys < 0) return 0;
+  return make_plan(m->d, rows, keys).total;
+}
+
+template <class T>
+static T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+// ---------------------------------------------------------------------------
+struct Pass {
+  int rows, B, per_batch, pos0;
+  bool prefill;
+  int bp, q0;                 // prefill: prefix index, first position of the chunk
+  const bf16_t* kv;           // cache base
+  int kv_Bp;                  // prefixes held by the cache (layer stride)
+  int Bp, P, P_max;           // step: prefix batch, prefix length, capacity
+  float* hidden_dump;
+  int32_t* expert_dump;
+  float* gate_dump;
+  bool final_norm;            // last combine writes the final-normed hidden into xn
+  const int32_t* flag;
+};
+
+static const bf16_t* lw(const dg_model* m, int l, size_t off) { return m->layers[l] + off; }
+
+static GemmArgs gargs() {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.G = 1;
+  g.m_split = 1;
+  g.k_split = 1;
+  return g;
+}
+
+static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pass& ps, hipStream_t st) {
+  const dg_model_desc& d = m->d;
+  const int R = ps.rows, D = d.d_model, H = d.n_heads, Hkv = d.n_kv_heads, hd = d.head_dim, E = d.n_experts,
+            k = d.top_k, fe = d.d_expert, fs = d.d_shared;
+  const int qkvd = (H + 2 * Hkv) * hd;
+  // cache of one layer: K [kv_Bp][Hkv][P_max][hd], then V^T [kv_Bp][Hkv][hd][P_max]
+  const size_t kv_one = (size_t)Hkv * ps.P_max * hd;  // elements of one prefix, K or V
+  const size_t layer_kv = (size_t)2 * ps.kv_Bp * kv_one;
+  float* h = at<float>(ws, p.h);
+  bf16_t* xn = at<bf16_t>(ws, p.xn);
+  bf16_t* qkv = at<bf16_t>(ws, p.qkv);
+  bf16_t* q = at<bf16_t>(ws, p.q);
+  bf16_t* o = at<bf16_t>(ws, p.o);
+  bf16_t* xn2 = at<bf16_t>(ws, p.xn2);
+  bf16_t* xr = at<bf16_t>(ws, p.xr);
+  float* rlog = at<float>(ws, p.rlog);
+  int32_t* eidx = at<int32_t>(ws, p.eidx);
+  float* egate = at<float>(ws, p.egate);
+  int32_t* cnt = at<int32_t>(ws, p.cnt);
+  int32_t* off = at<int32_t>(ws, p.off);
+  int32_t* slot_of = at<int32_t>(ws, p.slot_of);
+  int32_t* slot_row = at<int32_t>(ws, p.slot_row);
+  bf16_t* hbuf = at<bf16_t>(ws, p.hbuf);
+  float* ybuf = at<float>(ws, p.ybuf);
+  bf16_t* hs = at<bf16_t>(ws, p.hs);
+  float* ys = fs ? at<float>(ws, p.ys) : nullptr;
+  const int msplit = cdiv(R, 64);
+
+  // attention split choice: about one workgroup per CU
+  const int GQ = H / Hkv;
+  const int nkeys = ps.prefill ? ps.q0 + R : ps.P + ps.per_batch;
+  const int base_wg = cdiv(ps.per_batch, 16 * (4 / GQ)) * Hkv * ps.B;
+  int splits = std::max(1, std::min(p.splits_max, cdiv(256, base_wg)));
+  const int split_len = cdiv(cdiv(nkeys, splits), 32) * 32;
+  splits = cdiv(nkeys, split_len);
+
+  for (int l = 0; l < d.n_layers; ++l) {
+    const bf16_t* kvl = ps.kv ? ps.kv + (size_t)l * layer_kv : nullptr;
+    const size_t bpo = ps.prefill ? (size_t)ps.bp * kv_one : 0;   // prefill: this prefix only
+    const bf16_t* Kc = kvl ? kvl + bpo : nullptr;
+    const bf16_t* Vc = kvl ? kvl + (size_t)ps.kv_Bp * kv_one + bpo : nullptr;
+    // QKV
+    {
+      GemmArgs g = gargs();
+      g.A = xn; g.lda = D; g.W = lw(m, l, m->lay.w_qkv); g.ldw = D; g.K = D; g.N = qkvd; g.k_chunk = D;
+      g.M = R; g.m_split = msplit; g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
+      DG_CK(gemm(EPI_STORE_BF16, 4, g, st));
+    }
+    // QK norm + RoPE; K / V^T scatter
+    {
+      QkRopeArgs a;
+      memset(&a, 0, sizeof(a));
+      a.qkv = qkv; a.rows = R; a.H = H; a.Hkv = Hkv; a.hd = hd; a.eps = d.rms_eps; a.theta = d.rope_theta;
+      a.qnorm = lw(m, l, m->lay.q_norm); a.knorm = lw(m, l, m->lay.k_norm); a.q = q;
+      a.per_batch = ps.per_batch; a.pos0 = ps.pos0; a.flag = ps.flag;
+      if (ps.prefill) {
+        a.kdst = const_cast<bf16_t*>(Kc); a.k_bstride = 0; a.k_hstride = (long)ps.P_max * hd;
+        a.vtdst = const_cast<bf16_t*>(Vc); a.v_bstride = 0; a.v_hstride = (long)hd * ps.P_max; a.v_pitch = ps.P_max;
+        a.t_offset = ps.q0;
+      } else {
+        const int T = ps.per_batch;
+        a.kdst = at<bf16_t>(ws, p.kc); a.k_bstride = (long)Hkv * T * hd; a.k_hstride = (long)T * hd;
+        a.vtdst = at<bf16_t>(ws, p.vc); a.v_bstride = (long)Hkv * hd * T; a.v_hstride = (long)hd * T; a.v_pitch = T;
+        a.t_offset = 0;
+      }
+      DG_CK(qk_norm_rope(a, st));
+    }
+    // attention
+    {
+      AttnArgs a;
+      memset(&a, 0, sizeof(a));
+      a.q = q; a.H = H; a.Hkv = Hkv; a.hd = hd; a.scale = 1.0f / sqrtf((float)hd);
+      a.rows_per_batch = ps.per_batch; a.B = ps.B;
+      a.splits = splits; a.split_len = split_len;
+      a.opart = at<float>(ws, p.opart); a.mlpart = at<float>(ws, p.ml); a.flag = ps.flag;
+      if (ps.prefill) {
+        a.k1 = Kc; a.vt1 = Vc; a.k1_bstride = 0; a.k1_hstride = (long)ps.P_max * hd;
+        a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max; a.n1 = ps.q0 + R; a.nb1 = 1;
+        a.n2 = 0; a.causal = 1; a.qpos0 = ps.q0;
+      } else {
+        const int T = ps.per_batch;
+        if (ps.P > 0) {
+          a.k1 = Kc; a.vt1 = Vc; a.k1_bstride = (long)Hkv * ps.P_max * hd; a.k1_hstride = (long)ps.P_max * hd;
+          a.v1_bstride = (long)Hkv * hd * ps.P_max; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max;
+        } else {
+          a.k1 = at<bf16_t>(ws, p.kc); a.vt1 = at<bf16_t>(ws, p.vc);
+        }
+        a.n1 = ps.P; a.nb1 = ps.Bp;
+        a.k2 = at<bf16_t>(ws, p.kc); a.vt2 = at<bf16_t>(ws, p.vc);
+        a.k2_bstride = (long)Hkv * T * hd; a.k2_hstride = (long)T * hd;
+        a.v2_bstride = (long)Hkv * hd * T; a.v2_hstride = (long)hd * T; a.v2_pitch = T; a.n2 = T;
+        a.causal = 0; a.qpos0 = ps.P;
+      }
+      DG_CK(attention(a, st));
+      DG_CK(attention_merge(at<float>(ws, p.opart), at<float>(ws, p.ml), splits, R, H, hd, o, ps.flag, st));
+    }
+    // O projection + residual
+    {
+      GemmArgs g = gargs();
+      g.A = o; g.lda = H * hd; g.W = lw(m, l, m->lay.w_o); g.ldw = H * hd; g.K = H * hd; g.N = D;
+      g.k_chunk = H * hd; g.M = R; g.m_split = msplit; g.C = h; g.ldc = D; g.flag = ps.flag;
+      DG_CK(gemm(EPI_ADD_F32, 4, g, st));
+    }
+    DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, ps.flag, st));
+    // router logits (hi and lo rows) and top-k
+    {
+      GemmArgs g = gargs();
+      g.A = xr; g.lda = D; g.W = lw(m, l, m->lay.w_router); g.ldw = D; g.K = D; g.N = E; g.k_chunk = D;
+      g.M = 2 * R; g.m_split = cdiv(2 * R, 64); g.C = rlog; g.ldc = E; g.flag = ps.flag;
+      DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+    }
+    DG_CK(router_topk(rlog, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
+                      ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
+    DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, ps.flag, st));
+    // experts: gate/up (GEGLU) then down, grouped by expert over the permuted slots
+    {
+      GemmArgs g = gargs();
+      g.A = xn2; g.lda = D; g.a_rows = slot_row; g.W = lw(m, l, m->lay.w_gate); g.W2 = lw(m, l, m->lay.w_up);
+      g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D; g.group_off = off; g.G = E;
+      g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
+      DG_CK(gemm(EPI_GEGLU_BF16, 4, g, st));
+    }
+    {
+      GemmArgs g = gargs();
+      g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
+      g.N = D; g.k_chunk = fe; g.group_off = off; g.G = E; g.C = ybuf; g.ldc = D; g.flag = ps.flag;
+      DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+    }
+    if (fs) {
+      GemmArgs g = gargs();
+      g.A = xn2; g.lda = D; g.W = lw(m, l, m->lay.w_gate_sh); g.W2 = lw(m, l, m->lay.w_up_sh); g.ldw = D;
+      g.K = D; g.N = fs; g.k_chunk = D; g.M = R; g.m_split = msplit; g.C = hs; g.ldc = fs; g.flag = ps.flag;
+      DG_CK(gemm(EPI_GEGLU_BF16, 4, g, st));
+      GemmArgs g2 = gargs();
+      g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D; g2.k_chunk = fs;
+      g2.M = R; g2.m_split = msplit; g2.C = ys; g2.ldc = D; g2.flag = ps.flag;
+      DG_CK(gemm(EPI_STORE_F32, 4, g2, st));
+    }
+    const bf16_t* nw = nullptr;
+    if (l + 1 < d.n_layers) nw = lw(m, l + 1, m->lay.attn_norm);
+    else if (ps.final_norm) nw = (const bf16_t*)m->w.final_norm;
+    DG_CK(moe_combine(h, ys, ybuf, slot_of, egate, R, D, k, nw, d.rms_eps, xn,
+                      ps.hidden_dump ? ps.hidden_dump + (size_t)(l + 1) * R * D : nullptr, ps.flag, st));
+  }
+  return DG_OK;
+}
+
+// ---------------------------------------------------------------------------
+static dg_status check_step_shapes(const dg_model* m, int Bp, int P, int P_max, int B, int T) {
+  if (!m) return DG_ERR_ARG;
+  if (B < 1 || T < 1 || P < 0 || P_max < P || Bp < 1) return DG_ERR_ARG;
+  if (Bp != 1 && Bp != B) return DG_ERR_ARG;
+  if (T % 32 || T > 1024 || P % 32 || P_max % 32 || B > 16) return DG_ERR_SHAPE;
+  return DG_OK;
+}
+
+extern "C" dg_status dg_forward_hidden(dg_model* m, const void* kv, int32_t Bp, int32_t P, int32_t P_max,
+                                       int32_t B, int32_t T, float* hidden, float* hidden_dump,
+                                       int32_t* expert_dump, float* gate_dump, void* ws, size_t ws_bytes,
+                                       dg_stream_t stream) {
+  dg_status s = check_step_shapes(m, Bp, P, P_max, B, T);
+  if (s != DG_OK) return s;
+  if (!hidden || !ws || (P > 0 && !kv)) return DG_ERR_ARG;
+  const int R = B * T;
+  const Plan p = make_plan(m->d, R, P + T);
+  if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  // the caller's hidden buffer is the residual stream
+  DG_CK(hipMemcpyAsync(at<float>(ws, p.h), hidden, (size_t)R * m->d.d_model * 4, hipMemcpyDeviceToDevice, st));
+  DG_CK(rmsnorm_rows(at<float>(ws, p.h), m->layers[0] + m->lay.attn_norm, R, m->d.d_model, m->d.rms_eps,
+                     at<bf16_t>(ws, p.xn), nullptr, hidden_dump, nullptr, st));
+  Pass ps{};
+  ps.rows = R; ps.B = B; ps.per_batch = T; ps.pos0 = P; ps.prefill = false;
+  ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = Bp; ps.P = P; ps.P_max = P_max;
+  ps.hidden_dump = hidden_dump; ps.expert_dump = expert_dump; ps.gate_dump = gate_dump;
+  ps.final_norm = false; ps.flag = nullptr;
+  s = run_layers(m, p, ws, ps, st);
+  if (s != DG_OK) return s;
+  DG_CK(hipMemcpyAsync(hidden, at<float>(ws, p.h), (size_t)R * m->d.d_model * 4, hipMemcpyDeviceToDevice, st));
+  return DG_OK;
+}
+
+static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* hidden, int Bp, int P, int P_max,
+                              void* kv, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (!m || !kv || !ws || (!tokens && !hidden)) return DG_ERR_ARG;
+  if (Bp < 1 || P < 1 || P_max < P) return DG_ERR_ARG;
+  if (P % 32 || P_max % 32) return DG_ERR_SHAPE;
+  if (tokens && m->d.vocab == 0) return DG_ERR_ARG;
+  // largest chunk (multiple of 32 rows) whose workspace fits
+  int chunk = 0;
+  for (int c = std::min(P, 4096); c >= 32; c -= 32)
+    if (make_plan(m->d, c, P).total <= ws_bytes) { chunk = c; break; }
+  if (chunk == 0) return DG_ERR_WORKSPACE;
+  const Plan p = make_plan(m->d, chunk, P);
+  const dg_model_desc& d = m->d;
+  for (int bp = 0; bp < Bp; ++bp) {
+    for (int q0 = 0; q0 < P; q0 += chunk) {
+      const int R = std::min(chunk, P - q0);
+      if (tokens) {
+        DG_CK(embed_rows(tokens + (size_t)bp * P + q0, (const bf16_t*)m->w.embed, R, d.d_model,
+                         at<float>(ws, p.h), nullptr, st));
+      } else {
+        DG_CK(hipMemcpyAsync(at<float>(ws, p.h), hidden + ((size_t)bp * P + q0) * d.d_model,
+                             (size_t)R * d.d_model * 4, hipMemcpyDeviceToDevice, st));
+      }
+      DG_CK(rmsnorm_rows(at<float>(ws, p.h), m->layers[0] + m->lay.attn_norm, R, d.d_model, d.rms_eps,
+                         at<bf16_t>(ws, p.xn), nullptr, nullptr, nullptr, st));
+      Pass ps{};
+      ps.rows = R; ps.B = 1; ps.per_batch = R; ps.pos0 = q0; ps.prefill = true; ps.bp = bp; ps.q0 = q0;
+      ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = 1; ps.P = 0; ps.P_max = P_max;
+      ps.final_norm = false; ps.flag = nullptr;
+      dg_status s = run_layers(m, p, ws, ps, st);
+      if (s != DG_OK) return s;
+    }
+  }
+  return DG_OK;
+}
+
+extern "C" dg_status dg_prefill_prefix(dg_model* m, const int32_t* prefix, int32_t Bp, int32_t P, int32_t P_max,
+                                       void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
+  if (!prefix) return DG_ERR_ARG;
+  return prefill_impl(m, prefix, nullptr, Bp, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, int32_t Bp, int32_t P,
+                                       int32_t P_max, void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
+  if (!prefix_hidden) return DG_ERR_ARG;
+  return prefill_impl(m, nullptr, prefix_hidden, Bp, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+static dg_status check_sampler(const dg_sampler* sp, int B) {
+  if (!sp || !sp->row_seeds) return DG_ERR_ARG;
+  if (sp->max_steps < 1 || (sp->lock_rule != 0 && sp->lock_rule != 1) || (sp->stop_rule != 0 && sp->stop_rule != 1))
+    return DG_ERR_ARG;
+  if (!(sp->tau_start > 0.f) || !(sp->tau_end > 0.f)) return DG_ERR_ARG;
+  (void)B;
+  return DG_OK;
+}
+
+static dg_status check_canvas(const dg_canvas* c, bool need_sc) {
+  if (!c || !c->tokens || !c->locked || !c->entropy || !c->xhat || !c->argmax || !c->stopped || !c->steps)
+    return DG_ERR_ARG;
+  if (need_sc && !c->self_cond) return DG_ERR_ARG;
+  return DG_OK;
+}
+
+static SampleArgs sample_args(const float* logits, int B, int T, int V, dg_canvas* c, int step_arg,
+                              const dg_sampler* sp, float* part, int vsplit, float* rowstat, int32_t* all_stopped,
+                              const int32_t* flag) {
+  SampleArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = logits; a.B = B; a.T = T; a.V = V; a.ldl = V; a.step_arg = step_arg;
+  a.tau_start = sp->tau_start; a.tau_end = sp->tau_end; a.max_steps = sp->max_steps;
+  a.lock_rule = sp->lock_rule; a.lock_thresh = sp->lock_thresh; a.stop_rule = sp->stop_rule;
+  a.stop_thresh = sp->stop_thresh;
+  for (int b = 0; b < B && b < 16; ++b) a.seeds[b] = sp->row_seeds[b];
+  a.vsplit = vsplit; a.part = part; a.rowstat = rowstat;
+  a.tokens = c->tokens; a.locked = c->locked; a.entropy = c->entropy; a.xhat = c->xhat; a.argmax = c->argmax;
+  a.stopped = c->stopped; a.steps = c->steps; a.all_stopped = all_stopped; a.flag = flag;
+  return a;
+}
+
+// one full step; step_arg < 0: step index read from canvas->steps on the device
+static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max, int B, int T, dg_canvas* c,
+                           int step_arg, const dg_sampler* sp, void* ws, const Plan& p, const int32_t* flag,
+                           int32_t* all_stopped, hipStream_t st) {
+  const dg_model_desc& d = m->d;
+  const int R = B * T, D = d.d_model, V = d.vocab;
+  float* h = at<float>(ws, p.h);
+  bf16_t* xn = at<bf16_t>(ws, p.xn);
+  DG_CK(embed_rows(c->tokens, (const bf16_t*)m->w.embed, R, D, h, flag, st));
+  if (d.self_cond) {
+    GemmArgs g = gargs();
+    g.A = (const bf16_t*)c->self_cond; g.lda = D; g.W = (const bf16_t*)m->w.self_cond_w; g.ldw = D; g.K = D;
+    g.N = D; g.k_chunk = D; g.M = R; g.m_split = cdiv(R, 64); g.C = h; g.ldc = D;
+    g.col_gate = (const bf16_t*)m->w.self_cond_gate; g.flag = flag;
+    DG_CK(gemm(EPI_ADD_GATED_F32, 4, g, st));
+  }
+  DG_CK(rmsnorm_rows(h, m->layers[0] + m->lay.attn_norm, R, D, d.rms_eps, xn, nullptr, c->hidden_dump, flag, st));
+  Pass ps{};
+  ps.rows = R; ps.B = B; ps.per_batch = T; ps.pos0 = P; ps.prefill = false;
+  ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = Bp; ps.P = P; ps.P_max = P_max;
+  ps.hidden_dump = c->hidden_dump; ps.expert_dump = c->expert_dump; ps.gate_dump = c->gate_dump;
+  ps.final_norm = true; ps.flag = flag;
+  dg_status s = run_layers(m, p, ws, ps, st);
+  if (s != DG_OK) return s;
+  // LM head: logits = rms(h) E^T
+  float* logits = c->logits_dump ? c->logits_dump : at<float>(ws, p.logits);
+  {
+    GemmArgs g = gargs();
+    g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D; g.M = R;
+    g.m_split = cdiv(R, 64); g.C = logits; g.ldc = V; g.flag = flag;
+    DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+  }
+  float* rowstat = at<float>(ws, p.rowstat);
+  SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, rowstat,
+                              nullptr, flag);
+  DG_CK(sample_partial(sa, st));
+  DG_CK(sample_finish(sa, st));
+  if (d.self_cond) {
+    bf16_t* P_ = at<bf16_t>(ws, p.P);
+    DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, flag, st));
+    GemmArgs g = gargs();
+    g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
+    g.k_split = p.ksplit; g.M = R; g.m_split = cdiv(R, 64); g.C = at<float>(ws, p.separt); g.ldc = D;
+    g.c_kstride = (long)R * D; g.flag = flag;
+    DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+    DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, c->stopped, T, flag,
+                            st));
+  }
+  (void)all_stopped;
+  return DG_OK;
+}
+
+extern "C" dg_status dg_denoise_step(dg_model* m, const void* kv, int32_t Bp, int32_t P, int32_t P_max, int32_t B,
+                                     int32_t T, dg_canvas* canvas, int32_t step, const dg_sampler* sp, void* ws,
+                                     size_t ws_bytes, dg_stream_t stream) {
+  dg_status s = check_step_shapes(m, Bp, P, P_max, B, T);
+  if (s != DG_OK) return s;
+  if (m->d.vocab == 0) return DG_ERR_UNSUPPORTED;
+  if ((s = check_sampler(sp, B)) != DG_OK) return s;
+  if ((s = check_canvas(canvas, m->d.self_cond != 0)) != DG_OK) return s;
+  if (step < 0 || !ws || (P > 0 && !kv)) return DG_ERR_ARG;
+  const Plan p = make_plan(m->d, B * T, P + T);
+  if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
+  return step_impl(m, kv, Bp, P, P_max, B, T, canvas, step, sp, ws, p, nullptr, nullptr, (hipStream_t)stream);
+}
+
+__global__ void dg_all_stopped_kernel(const int32_t* stopped, int B, int32_t* flag) {
+  if (threadIdx.x == 0) {
+    int all = 1;
+    for (int b = 0; b < B; ++b) all &= (stopped[b] != 0);
+    *flag = all;
+  }
+}
+
+extern "C" dg_status dg_generate_block(dg_model* m, const void* kv, int32_t Bp, int32_t P, int32_t P_max,
+                                       int32_t B, int32_t T, dg_canvas* canvas, const dg_sampler* sp,
+                                       int32_t poll_every, void* ws, size_t ws_bytes, dg_stream_t stream) {
+  dg_status s = check_step_shapes(m, Bp, P, P_max, B, T);
+  if (s != DG_OK) return s;
+  if (m->d.vocab == 0) return DG_ERR_UNSUPPORTED;
+  if ((s = check_sampler(sp, B)) != DG_OK) return s;
+  if ((s = check_canvas(canvas, m->d.self_cond != 0)) != DG_OK) return s;
+  if (poll_every < 0 || !ws || (P > 0 && !kv)) return DG_ERR_ARG;
+  const Plan p = make_plan(m->d, B * T, P + T);
+  if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* flag = at<int32_t>(ws, p.flag);
+  DG_CK(fill_i32(flag, 0, 1, st));
+  DG_CK(fill_i32(canvas->stopped, 0, B, st));
+  DG_CK(fill_i32(canvas->steps, 0, B, st));
+  if (m->d.self_cond)
+    DG_CK(fill_u16((uint16_t*)canvas->self_cond, 0, (long)B * T * m->d.d_model, st));
+  for (int step = 0; step < sp->max_steps; ++step) {
+    s = step_impl(m, kv, Bp, P, P_max, B, T, canvas, -1, sp, ws, p, flag, nullptr, st);
+    if (s != DG_OK) return s;
+    hipLaunchKernelGGL(dg_all_stopped_kernel, dim3(1), dim3(64), 0, st, canvas->stopped, B, flag);
+    DG_CK(hipGetLastError());
+    if (poll_every > 0 && (step + 1) % poll_every == 0 && step + 1 < sp->max_steps) {
+      int32_t hf = 0;
+      DG_CK(hipMemcpyAsync(&hf, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+      DG_CK(hipStreamSynchronize(st));
+      if (hf) break;
+    }
+  }
+  return DG_OK;
+}
+
+// ---------------------------------------------------------------------------
+extern "C" size_t dg_sample_workspace_bytes(int32_t B, int32_t T, int32_t V) {
+  if (B < 1 || T < 1 || V < 1) return 0;
+  const int rows = B * T;
+  return al256((size_t)rows * vsplit_of(rows, V) * 8 * 4) + al256((size_t)rows * 2 * 4);
+}
+
+extern "C" dg_status dg_sample_logits(const float* logits, int32_t B, int32_t T, int32_t V, dg_canvas* canvas,
+                                      int32_t step, const dg_sampler* sp, void* ws, size_t ws_bytes,
+                                      dg_stream_t stream) {
+  if (!logits || !ws || step < 0) return DG_ERR_ARG;
+  if (B < 1 || T < 1 || V < 1) return DG_ERR_ARG;
+  if (B > 16 || T % 4 || T > 1024) return DG_ERR_SHAPE;
+  dg_status s = check_sampler(sp, B);
+  if (s != DG_OK) return s;
+  if ((s = check_canvas(canvas, false)) != DG_OK) return s;
+  if (ws_bytes < dg_sample_workspace_bytes(B, T, V)) return DG_ERR_WORKSPACE;
+  const int rows = B * T;
+  const int vs = vsplit_of(rows, V);
+  float* part = (float*)ws;
+  float* rowstat = at<float>(ws, al256((size_t)rows * vs * 8 * 4));
+  SampleArgs sa = sample_args(logits, B, T, V, canvas, step, sp, part, vs, rowstat, nullptr, nullptr);
+  hipStream_t st = (hipStream_t)stream;
+  DG_CK(sample_partial(sa, st));
+  DG_CK(sample_finish(sa, st));
+  return DG_OK;
+}
+
+extern "C" dg_status dg_init_canvas(const dg_model* m, dg_canvas* c, int32_t B, int32_t T,
+                                    const uint64_t* row_seeds, dg_stream_t stream) {
+  if (!m || !c || !c->tokens || !c->stopped || !c->steps || !c->argmax || !row_seeds) return DG_ERR_ARG;
+  if (B < 1 || T < 1) return DG_ERR_ARG;
+  if (B > 16) return DG_ERR_SHAPE;
+  if (m->d.vocab == 0) return DG_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  DG_CK(init_canvas(c->tokens, B, T, m->d.vocab, row_seeds, st));
+  DG_CK(fill_i32(c->stopped, 0, B, st));
+  DG_CK(fill_i32(c->steps, 0, B, st));
+  DG_CK(fill_i32(c->argmax, 0, (long)B * T, st));
+  if (c->self_cond) DG_CK(fill_u16((uint16_t*)c->self_cond, 0, (long)B * T * m->d.d_model, st));
+  return DG_OK;
+}
+
+extern "C" dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t M, int32_t N,
+                                  int32_t K, float* Cm, int64_t ldc, dg_stream_t stream) {
+  if (!A || !W || !Cm || M < 1 || N < 1 || K < 1 || lda < K || ldw < K || ldc < N) return DG_ERR_ARG;
+  if (K % 64) return DG_ERR_SHAPE;
+  GemmArgs g = gargs();
+  g.A = (const bf16_t*)A; g.lda = lda; g.W = (const bf16_t*)W; g.ldw = ldw; g.K = K; g.N = N; g.k_chunk = K;
+  g.M = M; g.m_split = cdiv(M, 64); g.C = Cm; g.ldc = ldc;
+  DG_CK(gemm(EPI_STORE_F32, 4, g, (hipStream_t)stream));
+  return DG_OK;
+}
+
+extern "C" dg_status dg_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, dg_stream_t stream) {
+  if (!in || !out || rows < 1 || cols < 1) return DG_ERR_ARG;
+  DG_CK(transpose_bf16((const bf16_t*)in, (bf16_t*)out, rows, cols, (hipStream_t)stream));
+  return DG_OK;
+}
+
+// host-side reference entry points of the sampler arithmetic
+extern "C" void dg_host_philox(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  const dg_u32x4 r = dg_philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1]);
+  for (int i = 0; i < 4; ++i) out[i] = r.x[i];
+}
+extern "C" float dg_host_ln(float x) { return dg_ln(x); }
+extern "C" float dg_host_gumbel_of_word(uint32_t w) { return dg_gumbel(dg_uniform_open01(w)); }
+extern "C" float dg_host_inv_tau(float t0, float t1, int32_t S, int32_t s) { return dg_inv_tau(t0, t1, S, s); }
+extern "C" void dg_host_ln_batch(const float* x, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = dg_ln(x[i]);
+}
+extern "C" void dg_host_gumbel_batch(const uint32_t* w, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = dg_gumbel(dg_uniform_open01(w[i]));
+}

@@ -1,0 +1,289 @@
+// Sampler of the denoising step (gfx950): per-position entropy, Gumbel-max
+// sample, argmax, entropy lock, re-randomisation of unlocked positions and the
+// adaptive stop (laozijiushiniubi article section 4; multinomial noise and
+// editable locked tokens, section 1), plus the softmax probabilities used by
+// the self-conditioning soft-prediction embedding (section 2).
+//
+// sample_partial: one workgroup per (4 canvas positions, vocab slice).  The
+// four positions share every Philox block: block (v, i >> 2, s, 0) gives word
+// i & 3 to position i, so one 10-round Philox call feeds four Gumbel scores.
+// Each thread keeps an online (max, sum exp, sum exp * shifted logit) triple,
+// the argmax and the best Gumbel score; the workgroup reduces them per position.
+// sample_finish: one workgroup per canvas row merges the slices in vocab order
+// (ties -> lowest index), takes the lock / stop decisions and writes tokens.
+#include <math.h>
+
+#include "dg_kernels.hpp"
+#include "dg_rng.hpp"
+
+namespace dg {
+
+struct Stat {
+  float m, Z, A;   // max logit, sum e^(l-m), sum e^(l-m)(l-m)
+  float av; int ai;  // argmax
+  float gv; int gi;  // best Gumbel score
+};
+
+__device__ __forceinline__ void stat_merge(Stat& x, const Stat& y) {
+  if (y.m != -INFINITY) {
+    if (x.m == -INFINITY) {
+      x.m = y.m; x.Z = y.Z; x.A = y.A;
+    } else {
+      const float M = fmaxf(x.m, y.m);
+      const float fx = __expf(x.m - M), fy = __expf(y.m - M);
+      x.A = fx * (x.A + (x.m - M) * x.Z) + fy * (y.A + (y.m - M) * y.Z);
+      x.Z = fx * x.Z + fy * y.Z;
+      x.m = M;
+    }
+  }
+  if (y.av > x.av || (y.av == x.av && y.ai < x.ai)) { x.av = y.av; x.ai = y.ai; }
+  if (y.gv > x.gv || (y.gv == x.gv && y.gi < x.gi)) { x.gv = y.gv; x.gi = y.gi; }
+}
+
+__device__ __forceinline__ int row_step(const SampleArgs& a, int b) {
+  return a.step_arg >= 0 ? a.step_arg : a.steps[b];
+}
+
+__global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
+  if (a.flag && *a.flag) return;
+  __shared__ Stat red[4][4];
+  const int groups = a.T / 4;
+  const int grp = blockIdx.x / a.vsplit;       // (b, position group)
+  const int sl = blockIdx.x % a.vsplit;
+  const int b = grp / groups, pg = grp % groups;
+  if (a.stopped && a.stopped[b]) return;
+  const int s = row_step(a, b);
+  const float inv_tau = dg_inv_tau(a.tau_start, a.tau_end, a.max_steps, s);
+  const uint64_t seed = a.seeds[b];
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int per = (a.V + a.vsplit - 1) / a.vsplit;
+  const int v0 = sl * per, v1 = min(a.V, v0 + per);
+  const float* l0 = a.logits + (long)(b * a.T + pg * 4) * a.ldl;
+
+  Stat st[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st[j] = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
+  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+    const dg_u32x4 w = dg_philox4x32_10((uint32_t)v, (uint32_t)pg, (uint32_t)s, 0u, k0, k1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float l = l0[(long)j * a.ldl + v];
+      Stat& t = st[j];
+      if (l > t.m) {
+        if (t.m == -INFINITY) {
+          t.Z = 1.f; t.A = 0.f;
+        } else {
+          const float f = __expf(t.m - l);
+          t.A = f * (t.A + (t.m - l) * t.Z);
+          t.Z = f * t.Z + 1.f;
+        }
+        t.m = l;
+      } else {
+        const float e = __expf(l - t.m);
+        t.Z += e;
+        t.A += e * (l - t.m);
+      }
+      if (l > t.av) { t.av = l; t.ai = v; }   // v increasing per thread: ties keep the lower index
+      float sc;
+      {
+#pragma clang fp contract(off)
+        const float scaled = l * inv_tau;
+        sc = scaled + dg_gumbel(dg_uniform_open01(w.x[j]));
+      }
+      if (sc > t.gv) { t.gv = sc; t.gi = v; }
+    }
+  }
+  // wavefront reduction
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      Stat y;
+      y.m = __shfl_xor(st[j].m, o, 64); y.Z = __shfl_xor(st[j].Z, o, 64); y.A = __shfl_xor(st[j].A, o, 64);
+      y.av = __shfl_xor(st[j].av, o, 64); y.ai = __shfl_xor(st[j].ai, o, 64);
+      y.gv = __shfl_xor(st[j].gv, o, 64); y.gi = __shfl_xor(st[j].gi, o, 64);
+      stat_merge(st[j], y);
+    }
+    if (lane == 0) red[wave][j] = st[j];
+  }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    const int j = threadIdx.x;
+    Stat t = red[0][j];
+    for (int w = 1; w < 4; ++w) stat_merge(t, red[w][j]);
+    float* o = a.part + ((long)(b * a.T + pg * 4 + j) * a.vsplit + sl) * 8;
+    o[0] = t.m; o[1] = t.Z; o[2] = t.A; o[3] = t.av;
+    o[4] = __int_as_float(t.ai); o[5] = t.gv; o[6] = __int_as_float(t.gi); o[7] = 0.f;
+  }
+}
+
+hipError_t sample_partial(const SampleArgs& a, hipStream_t s) {
+  if (a.T % 4 != 0 || a.B > 16) return hipErrorInvalidValue;
+  const int blocks = a.B * (a.T / 4) * a.vsplit;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sample_partial_kernel, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void sample_finish_kernel(SampleArgs a) {
+  if (a.flag && *a.flag) return;
+  __shared__ float Hs[1024];
+  __shared__ float red[16];
+  __shared__ int unstable;
+  const int b = blockIdx.x;
+  if (a.stopped && a.stopped[b]) return;
+  const int s = row_step(a, b);
+  const uint64_t seed = a.seeds[b];
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int i = threadIdx.x;
+  if (i == 0) unstable = 0;
+  Stat t = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
+  float H = 0.f;
+  const long r = (long)b * a.T + i;
+  if (i < a.T) {
+    for (int sl = 0; sl < a.vsplit; ++sl) {
+      const float* p = a.part + (r * a.vsplit + sl) * 8;
+      Stat y{p[0], p[1], p[2], p[3], __float_as_int(p[4]), p[5], __float_as_int(p[6])};
+      stat_merge(t, y);
+    }
+    H = logf(t.Z) - t.A / t.Z;
+    Hs[i] = H;
+  }
+  __syncthreads();
+  const float meanH = block_sum(i < a.T ? H : 0.f, red) / (float)a.T;
+  bool lock = false;
+  if (i < a.T) {
+    if (a.lock_rule == 0) {
+      lock = H < a.lock_thresh;
+    } else {
+      // sorted cumulative entropy: sum of H_j over positions ordered before or at i
+      float cum = 0.f;
+      for (int j = 0; j < a.T; ++j) {
+        const float hj = Hs[j];
+        if (hj < H || (hj == H && j <= i)) cum += hj;
+      }
+      lock = cum <= a.lock_thresh;
+    }
+    if (a.argmax[r] != t.ai) atomicOr(&unstable, 1);
+  }
+  __syncthreads();
+  bool stop;
+  if (a.stop_rule == 0) stop = meanH < a.stop_thresh;
+  else stop = (meanH < a.stop_thresh) && (s > 0) && (unstable == 0);
+  stop = stop || (s + 1 >= a.max_steps);
+  if (i < a.T) {
+    int tok;
+    if (stop || lock) {
+      tok = t.gi;
+    } else {
+      const dg_u32x4 w = dg_philox4x32_10((uint32_t)i, 0u, (uint32_t)s, 1u, k0, k1);
+      tok = (int)dg_uniform_index(w.x[0], (uint32_t)a.V);
+    }
+    a.tokens[r] = tok;
+    a.xhat[r] = t.gi;
+    a.argmax[r] = t.ai;
+    a.entropy[r] = H;
+    a.locked[r] = lock ? 1 : 0;
+    if (a.rowstat) {
+      a.rowstat[r * 2] = t.m;
+      a.rowstat[r * 2 + 1] = t.Z;
+    }
+  }
+  if (i == 0) {
+    a.stopped[b] = stop ? 1 : 0;
+    a.steps[b] = s + 1;
+  }
+}
+
+__global__ void all_stopped_kernel(const int32_t* stopped, int B, int32_t* flag) {
+  if (threadIdx.x == 0) {
+    int all = 1;
+    for (int b = 0; b < B; ++b) all &= (stopped[b] != 0);
+    *flag = all;
+  }
+}
+
+hipError_t sample_finish(const SampleArgs& a, hipStream_t s) {
+  if (a.T > 1024 || a.B > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sample_finish_kernel, dim3(a.B), dim3(a.T <= 256 ? 256 : 1024), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.all_stopped) return e;
+  hipLaunchKernelGGL(all_stopped_kernel, dim3(1), dim3(64), 0, s, a.stopped, a.B, a.all_stopped);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void probs_kernel(const float* logits, const float* rowstat, int V, long ldl,
+                                                    bf16_t* P, const int32_t* flag) {
+  if (flag && *flag) return;
+  const int r = blockIdx.y;
+  const float m = rowstat[r * 2], iz = 1.0f / rowstat[r * 2 + 1];
+  const long v = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (v >= V) return;
+  const float4 l = *reinterpret_cast<const float4*>(logits + r * ldl + v);
+  uint2 o;
+  o.x = (uint32_t)f2bf(__expf(l.x - m) * iz) | ((uint32_t)f2bf(__expf(l.y - m) * iz) << 16);
+  o.y = (uint32_t)f2bf(__expf(l.z - m) * iz) | ((uint32_t)f2bf(__expf(l.w - m) * iz) << 16);
+  *reinterpret_cast<uint2*>(P + (long)r * V + v) = o;
+}
+
+hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,
+                         const int32_t* flag, hipStream_t s) {
+  if (V % 4 != 0 || ldl % 4 != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((V / 4 + 255) / 256), rows);
+  hipLaunchKernelGGL(probs_kernel, grid, dim3(256), 0, s, logits, rowstat, V, ldl, P, flag);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void reduce_soft_kernel(const float* part, int ksplit, int rows, int d,
+                                                          bf16_t* out, const int32_t* flag) {
+  if (flag && *flag) return;
+  const long n = (long)rows * d;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float acc = 0.f;
+  for (int k = 0; k < ksplit; ++k) acc += part[k * n + i];
+  out[i] = f2bf(acc);
+}
+
+hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out, const int32_t* stopped,
+                             int T, const int32_t* flag, hipStream_t s) {
+  (void)stopped; (void)T;
+  const long n = (long)rows * d;
+  hipLaunchKernelGGL(reduce_soft_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, ksplit, rows, d,
+                     out, flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+struct Seeds16 { uint64_t s[16]; };
+
+__global__ void init_canvas_kernel(int32_t* tokens, int B, int T, int V, Seeds16 sd) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * T) return;
+  const int b = idx / T, i = idx % T;
+  const uint64_t seed = sd.s[b];
+  const dg_u32x4 w = dg_philox4x32_10((uint32_t)i, 0u, 0xFFFFFFFFu, 1u, (uint32_t)seed, (uint32_t)(seed >> 32));
+  tokens[idx] = (int32_t)dg_uniform_index(w.x[0], (uint32_t)V);
+}
+
+hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* seeds, hipStream_t s) {
+  if (B > 16) return hipErrorInvalidValue;
+  Seeds16 sd{};
+  for (int b = 0; b < B; ++b) sd.s[b] = seeds[b];
+  hipLaunchKernelGGL(init_canvas_kernel, dim3((B * T + 255) / 256), dim3(256), 0, s, tokens, B, T, V, sd);
+  return hipGetLastError();
+}
+
+__global__ void set_step_kernel(int32_t* steps, int B, int step) {
+  if (threadIdx.x < B) steps[threadIdx.x] = step;
+}
+
+hipError_t set_step(int32_t* steps, int B, int step, hipStream_t s) {
+  hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(64), 0, s, steps, B, step);
+  return hipGetLastError();
+}
+
+}  // namespace dg
