@@ -1,0 +1,285 @@
+"""Benchmark of one denoising step on one MI355X.
+
+Workload (default "full_step"): the 30-layer random-init MoE model (d_model
+2816, 16/8 heads of 256, 128 experts top-8 of width 704 plus a shared FFN of
+2112, vocabulary 262144, tied embedding, self-conditioning; ~25.2B params in
+bf16), one shared 2048-token prefix already encoded in the KV cache, one
+256-token canvas.  A step is one full pass of the hot path: embedding +
+self-conditioning, 30 layers, LM head, entropy, Gumbel-max sampling, lock /
+re-randomise / stop, soft-prediction embedding.
+
+Prints ONE JSON line: output tokens/s (= B * 256 / (steps per block * time per
+step), steps per block measured with dg_generate_block), ms per step, the
+roofline of the dominant kernel (grouped expert gate/up GEMM, timed with HIP
+events inside libdg during a profiled pass right after the timed region) and
+the CPU oracle timed on a bounded sample on this machine's host cores."""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "output tok/s at batch 1 (256-tok canvas), ms per denoising step, % roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(m, B, T, P, touched):
+    """HBM bytes a step must move at minimum: every touched weight once, the
+    embedding table once, the prefix KV once, canvas activations ignored."""
+    d, hd = m.d_model, m.head_dim
+    dense = (m.qkv_dim * d + d * m.n_heads * hd + m.n_experts * d + 3 * d * m.d_shared) * 2
+    expert = 3 * m.d_expert * d * 2
+    kv = 2 * P * m.n_kv_heads * hd * 2
+    per_layer = [dense + t * expert + kv for t in touched]
+    glob = m.vocab * d * 2 + (d * d * 2 if m.self_cond else 0)
+    return sum(per_layer) + glob
+
+
+def algorithmic_flops(m, B, T, P):
+    R = B * T
+    d, hd = m.d_model, m.head_dim
+    per_layer = 2 * R * (m.qkv_dim * d + d * m.n_heads * hd + m.n_experts * d)
+    per_layer += 2 * R * m.top_k * 3 * d * m.d_expert + 2 * R * 3 * d * m.d_shared
+    per_layer += 4 * R * (P + T) * m.n_heads * hd
+    head = 2 * R * m.vocab * d * (2 if m.self_cond else 1) + (2 * R * d * d if m.self_cond else 0)
+    return m.n_layers * per_layer + head
+
+
+def gateup_bytes(m, R, touched_mean):
+    """Algorithmic bytes of one grouped gate/up launch: touched experts' W_gate
+    and W_up, the gathered activation rows, the GELU-gated outputs."""
+    return touched_mean * 2 * m.d_expert * m.d_model * 2 + R * m.top_k * (m.d_model + m.d_expert) * 2
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    p = os.path.join(ROOT, "discrete_diffusion_decoding_amd", "csrc", "k_gemm.hip")
+    h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kh):
+    """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", "expert_gateup_full_step_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha256_16") != kh:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(m_full, seed):
+    """Time the oracle on a bounded sample of the same step: one full-width
+    layer over a 2048-token prefix KV (synthetic K/V) for 256 canvas rows, and
+    the LM head + sampler + soft embedding over 1/16 of the vocabulary; scaled
+    to a whole 30-layer step and to the block's output tokens/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from discrete_diffusion_decoding_amd import synth
+    from discrete_diffusion_decoding_amd.configs import FULL_LAYER
+    from oracle import model as om
+    from oracle import sampler as osmp
+
+    T, P = 256, 2048
+    lm = om.Model(FULL_LAYER, synth.SynthWeights(FULL_LAYER, seed, cache_layers=True))
+    hc = synth.hidden(seed, "cpu_canvas", (T, FULL_LAYER.d_model))
+    Kp = synth.hidden(seed, "cpu_k", (P, FULL_LAYER.n_kv_heads, FULL_LAYER.head_dim))
+    Vp = synth.hidden(seed, "cpu_v", (P, FULL_LAYER.n_kv_heads, FULL_LAYER.head_dim))
+    lm.layer_dense(0)  # generate the weights outside the timed region
+    t0 = time.perf_counter()
+    lm.canvas_hidden(hc, [(Kp.astype(np.float64), Vp.astype(np.float64))], P)
+    t_layer = time.perf_counter() - t0
+    frac = 16
+    Vs = m_full.vocab // frac
+    E = synth.normal_bf16(seed, "embed", (m_full.vocab, m_full.d_model))[:Vs]
+    g = {"embed": E, "final_norm": np.full(m_full.d_model, synth.BF16_ONE, np.uint16)}
+
+    class _W:
+        def glob(self):
+            return g
+
+    hm = om.Model(m_full, _W())
+    hm.glob()
+    t0 = time.perf_counter()
+    logits = hm.head(hc)
+    osmp.entropy(logits)
+    osmp.gumbel_argmax(logits.astype(np.float32), np.float32(1.25), 1, 1)
+    hm.soft_embedding(logits)
+    t_head = time.perf_counter() - t0
+    step_s = m_full.n_layers * t_layer + frac * t_head
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": round(T / (48 * step_s), 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"float64 numpy oracle: one full-width layer step (256 canvas rows, 2048-key prefix) "
+                   f"{t_layer:.2f}s x {m_full.n_layers} layers + LM head/entropy/Gumbel/soft-embedding on 1/{frac} "
+                   f"of the vocabulary {t_head:.2f}s x {frac} = {step_s:.1f}s per step, 48 steps per block"),
+        "ms_per_step": round(step_s * 1e3, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="full_step")
+    ap.add_argument("--seed", type=int, default=2024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from discrete_diffusion_decoding_amd import dg, synth
+    from discrete_diffusion_decoding_amd.configs import WORKLOADS, SamplerParams
+    from discrete_diffusion_decoding_amd.device import DeviceModel
+
+    wl = WORKLOADS[args.workload]
+    m = wl.model
+    if wl.hidden_input:
+        raise SystemExit("bench.py times token workloads (full_step, full_block, long_block, tiny_step)")
+    B, T, P, Bp = wl.batch, wl.canvas_len, wl.prefix_len, wl.prefix_batch
+    torch.cuda.set_device(0)
+    dg.lib()
+    t0 = time.perf_counter()
+    log(f"generating and uploading the {m.param_counts()['total'] / 1e9:.2f}B-parameter model")
+    dm = DeviceModel(m, args.seed)
+    setup_s = time.perf_counter() - t0
+    log(f"model resident after {setup_s:.1f}s")
+    prefix = torch.as_tensor(synth.tokens(args.seed, "prefix", (Bp, P), m.vocab)).cuda()
+    seeds = synth.row_seeds(args.seed, B)
+    kv = dm.kv_cache(Bp, P)
+    ws = dm.workspace(B * T, P + T)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dg.dg_prefill_prefix(dm.handle, prefix, Bp, P, P, kv, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    log(f"prefill {P} tokens x {Bp}: {prefill_ms:.1f} ms")
+
+    sp = SamplerParams()
+    sampler, keep = dg.make_sampler(sp, seeds)
+    st = dm.canvas_state(B, T)
+    canvas = dg.make_canvas(st)
+    dg.dg_init_canvas(dm.handle, canvas, B, T, seeds)
+
+    # one dumped step: touched experts per layer
+    ed = torch.zeros(m.n_layers, B * T, m.top_k, dtype=torch.int32, device="cuda")
+    st_d = dict(st)
+    st_d["expert_dump"] = ed
+    dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, dg.make_canvas(st_d), 0, sampler, ws)
+    edh = ed.cpu().numpy()
+    touched = [len(np.unique(edh[l])) for l in range(m.n_layers)]
+
+    step_idx = 1
+    for _ in range(args.warmup):
+        dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws)
+        step_idx = step_idx % (sp.max_steps - 2) + 1
+    torch.cuda.synchronize()
+    st["stopped"].zero_()
+    e0.record()
+    h0 = time.perf_counter()
+    for _ in range(args.steps):
+        dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws)
+        step_idx = step_idx % (sp.max_steps - 2) + 1
+    e1.record()
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (host clock {host_s * 1e3 / args.steps:.3f})")
+
+    kernel_ms = {}
+    if not args.no_profile:
+        dg.dg_profile_enable(dm.handle, True)
+        kp = max(1, min(args.steps, 5))
+        for _ in range(kp):
+            dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws)
+            step_idx = step_idx % (sp.max_steps - 2) + 1
+        torch.cuda.synchronize()
+        prof = dg.dg_profile_read(dm.handle)
+        dg.dg_profile_enable(dm.handle, False)
+        kernel_ms = {k: {"ms_per_step": round(v[0] / kp, 4), "launches_per_step": v[1] // kp}
+                     for k, v in prof.items()}
+
+    steps_taken, block_ms = None, None
+    if not args.no_block:
+        dg.dg_init_canvas(dm.handle, canvas, B, T, seeds)
+        e0.record()
+        dg.dg_generate_block(dm.handle, kv, Bp, P, P, B, T, canvas, sampler, ws, poll_every=8)
+        e1.record()
+        torch.cuda.synchronize()
+        block_ms = e0.elapsed_time(e1)
+        steps_taken = st["steps"].cpu().numpy().tolist()
+        log(f"block: steps taken {steps_taken}, {block_ms:.1f} ms")
+    spb = max(steps_taken) if steps_taken else sp.max_steps
+    tok_s = B * T / (spb * ms_per_step / 1e3)
+
+    alg_b = algorithmic_bytes(m, B, T, P, touched)
+    alg_f = algorithmic_flops(m, B, T, P)
+    floor_ms = max(alg_b / (HBM_PEAK_GBS * 1e9), alg_f / (BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    roof = None
+    if kernel_ms:
+        gu = kernel_ms["expert_gateup"]
+        per_launch_ms = gu["ms_per_step"] / max(1, gu["launches_per_step"])
+        bytes_l = gateup_bytes(m, B * T, float(np.mean(touched)))
+        ach = bytes_l / (per_launch_ms * 1e-3) / 1e9
+        kh = kernel_hash()
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(kh),
+                "kernel": "grouped expert gate/up GEMM (gemm_kernel<GEGLU>)",
+                "bytes_per_launch": int(bytes_l), "avg_launch_ms": round(per_launch_ms, 4),
+                "kernel_source_sha256_16": kh}
+
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "layers": m.n_layers, "d_model": m.d_model,
+                   "heads": f"{m.n_heads}q/{m.n_kv_heads}kv x {m.head_dim}",
+                   "experts": f"{m.n_experts} top-{m.top_k} x {m.d_expert} + shared {m.d_shared}",
+                   "vocab": m.vocab, "batch": B, "prefix": P, "canvas": T,
+                   "params_B": round(m.param_counts()["total"] / 1e9, 2)},
+        "roofline": roof,
+        "steps_per_block": spb, "steps_taken": steps_taken, "block_ms": block_ms,
+        "tokens_per_forward": round(T / spb, 3),
+        "step_roofline": {"bound": "hbm" if alg_b / (HBM_PEAK_GBS * 1e9) >= alg_f / (BF16_PEAK_TFLOPS * 1e12)
+                          else "mfma", "alg_bytes": int(alg_b), "alg_flops": int(alg_f),
+                          "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms_per_step, 4)},
+        "touched_experts_per_layer": float(np.mean(touched)),
+        "kernel_ms": kernel_ms, "prefill_ms": round(prefill_ms, 2), "setup_s": round(setup_s, 1),
+    }
+    dm.close()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(m, args.seed)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

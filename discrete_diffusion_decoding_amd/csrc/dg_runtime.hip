@@ -23,11 +23,44 @@
 
 using namespace dg;
 
+// Optional per-kernel-class timing with HIP events (off by default).
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;   // event pairs, reused across calls
+  std::vector<int> cls;           // class of each recorded pair
+  size_t used = 0;
+};
+
 struct dg_model {
   dg_model_desc d;
   dg_weights w;
   std::vector<const bf16_t*> layers;
   dg_layer_layout lay;
+  mutable Prof prof;
+};
+
+// timing scope: records an event pair around the enclosed launches when on
+struct ProfScope {
+  Prof& p;
+  hipStream_t st;
+  size_t idx;
+  bool rec;
+  ProfScope(const dg_model* m, int c, hipStream_t s) : p(m->prof), st(s), idx(0), rec(false) {
+    if (!p.on) return;
+    if (p.used * 2 + 2 > p.pool.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+      p.pool.push_back(a);
+      p.pool.push_back(b);
+      p.cls.push_back(c);
+    }
+    idx = p.used++;
+    p.cls[idx] = c;
+    rec = hipEventRecord(p.pool[2 * idx], st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (rec) (void)hipEventRecord(p.pool[2 * idx + 1], st);
+  }
 };
 
 #define DG_CK(x)                                                        \
@@ -117,7 +150,11 @@ extern "C" dg_status dg_model_create(const dg_model_desc* d, const dg_weights* w
   return DG_OK;
 }
 
-extern "C" void dg_model_destroy(dg_model* m) { delete m; }
+extern "C" void dg_model_destroy(dg_model* m) {
+  if (!m) return;
+  for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
+  delete m;
+}
 
 extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
   if (!m || Bp < 1 || P_max < 0) return 0;
@@ -279,6 +316,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g = gargs();
       g.A = xn; g.lda = D; g.W = lw(m, l, m->lay.w_qkv); g.ldw = D; g.K = D; g.N = qkvd; g.k_chunk = D;
       g.M = R; g.m_split = msplit; g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
+      ProfScope ps_(m, DG_PROF_DENSE, st);
       DG_CK(gemm(EPI_STORE_BF16, 4, g, st));
     }
     // QK norm + RoPE; K / V^T scatter
@@ -298,6 +336,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
         a.vtdst = at<bf16_t>(ws, p.vc); a.v_bstride = (long)Hkv * hd * T; a.v_hstride = (long)hd * T; a.v_pitch = T;
         a.t_offset = 0;
       }
+      ProfScope ps_(m, DG_PROF_OTHER, st);
       DG_CK(qk_norm_rope(a, st));
     }
     // attention
@@ -326,6 +365,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
         a.v2_bstride = (long)Hkv * hd * T; a.v2_hstride = (long)hd * T; a.v2_pitch = T; a.n2 = T;
         a.causal = 0; a.qpos0 = ps.P;
       }
+      ProfScope ps_(m, DG_PROF_ATTN, st);
       DG_CK(attention(a, st));
       DG_CK(attention_merge(at<float>(ws, p.opart), at<float>(ws, p.ml), splits, R, H, hd, o, ps.flag, st));
     }
@@ -334,34 +374,45 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g = gargs();
       g.A = o; g.lda = H * hd; g.W = lw(m, l, m->lay.w_o); g.ldw = H * hd; g.K = H * hd; g.N = D;
       g.k_chunk = H * hd; g.M = R; g.m_split = msplit; g.C = h; g.ldc = D; g.flag = ps.flag;
+      ProfScope ps_(m, DG_PROF_DENSE, st);
       DG_CK(gemm(EPI_ADD_F32, 4, g, st));
     }
-    DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, ps.flag, st));
+    {
+      ProfScope ps_(m, DG_PROF_OTHER, st);
+      DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, ps.flag, st));
+    }
     // router logits (hi and lo rows) and top-k
     {
       GemmArgs g = gargs();
       g.A = xr; g.lda = D; g.W = lw(m, l, m->lay.w_router); g.ldw = D; g.K = D; g.N = E; g.k_chunk = D;
       g.M = 2 * R; g.m_split = cdiv(2 * R, 64); g.C = rlog; g.ldc = E; g.flag = ps.flag;
+      ProfScope ps_(m, DG_PROF_ROUTER, st);
       DG_CK(gemm(EPI_STORE_F32, 4, g, st));
     }
+    {
+    ProfScope psr_(m, DG_PROF_ROUTER, st);
     DG_CK(router_topk(rlog, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
                       ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
     DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, ps.flag, st));
+    }
     // experts: gate/up (GEGLU) then down, grouped by expert over the permuted slots
     {
       GemmArgs g = gargs();
       g.A = xn2; g.lda = D; g.a_rows = slot_row; g.W = lw(m, l, m->lay.w_gate); g.W2 = lw(m, l, m->lay.w_up);
       g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D; g.group_off = off; g.G = E;
       g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
+      ProfScope ps_(m, DG_PROF_EXPERT_GATEUP, st);
       DG_CK(gemm(EPI_GEGLU_BF16, 4, g, st));
     }
     {
       GemmArgs g = gargs();
       g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
       g.N = D; g.k_chunk = fe; g.group_off = off; g.G = E; g.C = ybuf; g.ldc = D; g.flag = ps.flag;
+      ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_F32, 4, g, st));
     }
     if (fs) {
+      ProfScope ps_(m, DG_PROF_SHARED, st);
       GemmArgs g = gargs();
       g.A = xn2; g.lda = D; g.W = lw(m, l, m->lay.w_gate_sh); g.W2 = lw(m, l, m->lay.w_up_sh); g.ldw = D;
       g.K = D; g.N = fs; g.k_chunk = D; g.M = R; g.m_split = msplit; g.C = hs; g.ldc = fs; g.flag = ps.flag;
@@ -374,8 +425,11 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     const bf16_t* nw = nullptr;
     if (l + 1 < d.n_layers) nw = lw(m, l + 1, m->lay.attn_norm);
     else if (ps.final_norm) nw = (const bf16_t*)m->w.final_norm;
-    DG_CK(moe_combine(h, ys, ybuf, slot_of, egate, R, D, k, nw, d.rms_eps, xn,
-                      ps.hidden_dump ? ps.hidden_dump + (size_t)(l + 1) * R * D : nullptr, ps.flag, st));
+    {
+      ProfScope psc_(m, DG_PROF_OTHER, st);
+      DG_CK(moe_combine(h, ys, ybuf, slot_of, egate, R, D, k, nw, d.rms_eps, xn,
+                        ps.hidden_dump ? ps.hidden_dump + (size_t)(l + 1) * R * D : nullptr, ps.flag, st));
+    }
   }
   return DG_OK;
 }
@@ -510,6 +564,7 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     g.A = (const bf16_t*)c->self_cond; g.lda = D; g.W = (const bf16_t*)m->w.self_cond_w; g.ldw = D; g.K = D;
     g.N = D; g.k_chunk = D; g.M = R; g.m_split = cdiv(R, 64); g.C = h; g.ldc = D;
     g.col_gate = (const bf16_t*)m->w.self_cond_gate; g.flag = flag;
+    ProfScope ps_(m, DG_PROF_DENSE, st);
     DG_CK(gemm(EPI_ADD_GATED_F32, 4, g, st));
   }
   DG_CK(rmsnorm_rows(h, m->layers[0] + m->lay.attn_norm, R, D, d.rms_eps, xn, nullptr, c->hidden_dump, flag, st));
@@ -526,14 +581,19 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     GemmArgs g = gargs();
     g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D; g.M = R;
     g.m_split = cdiv(R, 64); g.C = logits; g.ldc = V; g.flag = flag;
+    ProfScope ps_(m, DG_PROF_LMHEAD, st);
     DG_CK(gemm(EPI_STORE_F32, 4, g, st));
   }
   float* rowstat = at<float>(ws, p.rowstat);
   SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, rowstat,
                               nullptr, flag);
-  DG_CK(sample_partial(sa, st));
-  DG_CK(sample_finish(sa, st));
+  {
+    ProfScope ps_(m, DG_PROF_SAMPLER, st);
+    DG_CK(sample_partial(sa, st));
+    DG_CK(sample_finish(sa, st));
+  }
   if (d.self_cond) {
+    ProfScope ps_(m, DG_PROF_SOFTEMB, st);
     bf16_t* P_ = at<bf16_t>(ws, p.P);
     DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, flag, st));
     GemmArgs g = gargs();
@@ -676,4 +736,28 @@ extern "C" void dg_host_ln_batch(const float* x, float* out, int64_t n) {
 }
 extern "C" void dg_host_gumbel_batch(const uint32_t* w, float* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = dg_gumbel(dg_uniform_open01(w[i]));
+}
+
+extern "C" dg_status dg_profile_enable(dg_model* m, int32_t on) {
+  if (!m) return DG_ERR_ARG;
+  m->prof.on = on != 0;
+  m->prof.used = 0;
+  return DG_OK;
+}
+
+extern "C" dg_status dg_profile_read(dg_model* m, int32_t cls, double* total_ms, int32_t* count) {
+  if (!m || !total_ms || !count || cls < 0 || cls >= DG_PROF_NCLASS) return DG_ERR_ARG;
+  double t = 0.0;
+  int n = 0;
+  for (size_t i = 0; i < m->prof.used; ++i) {
+    if (m->prof.cls[i] != cls) continue;
+    DG_CK(hipEventSynchronize(m->prof.pool[2 * i + 1]));
+    float ms = 0.f;
+    DG_CK(hipEventElapsedTime(&ms, m->prof.pool[2 * i], m->prof.pool[2 * i + 1]));
+    t += ms;
+    ++n;
+  }
+  *total_ms = t;
+  *count = n;
+  return DG_OK;
 }

@@ -86,6 +86,8 @@ def lib():
             "dg_init_canvas": (st, [vp, C.POINTER(Canvas), i32, i32, C.POINTER(C.c_uint64), vp]),
             "dg_transpose_bf16": (st, [vp, vp, C.c_int64, C.c_int64, vp]),
             "dg_gemm_bf16": (st, [vp, C.c_int64, vp, C.c_int64, i32, i32, i32, vp, C.c_int64, vp]),
+            "dg_profile_enable": (st, [vp, i32]),
+            "dg_profile_read": (st, [vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]),
             "dg_host_philox": (None, [C.POINTER(C.c_uint32), C.POINTER(C.c_uint32), C.POINTER(C.c_uint32)]),
             "dg_host_ln": (C.c_float, [C.c_float]),
             "dg_host_gumbel_of_word": (C.c_float, [C.c_uint32]),
@@ -212,6 +214,23 @@ def dg_transpose_bf16(src, dst, rows, cols, stream=None):
 def dg_gemm_bf16(A, W, Cout, M, N, K, lda=None, ldw=None, ldc=None, stream=None):
     _ck(lib().dg_gemm_bf16(_ptr(A), lda or K, _ptr(W), ldw or K, M, N, K, _ptr(Cout), ldc or N, _stream(stream)),
         "dg_gemm_bf16")
+
+
+PROF_CLASSES = ("dense", "attn", "router", "expert_gateup", "expert_down", "shared", "lmhead", "sampler",
+                "softemb", "other")
+
+
+def dg_profile_enable(h, on: bool):
+    _ck(lib().dg_profile_enable(h, 1 if on else 0), "dg_profile_enable")
+
+
+def dg_profile_read(h) -> dict:
+    out = {}
+    for i, name in enumerate(PROF_CLASSES):
+        t, n = C.c_double(), C.c_int32()
+        _ck(lib().dg_profile_read(h, i, C.byref(t), C.byref(n)), "dg_profile_read")
+        out[name] = (float(t.value), int(n.value))
+    return out
 
 
 # host reference of the sampler arithmetic (no GPU)

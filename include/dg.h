@@ -217,6 +217,27 @@ dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, i
 /* out [cols][rows] = in [rows][cols]^T (bf16), e.g. embed -> embed_t. */
 dg_status dg_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, dg_stream_t stream);
 
+/* Timing of kernel classes with HIP events recorded around their launches
+ * (for measurement; adds event records to the stream while enabled).
+ * dg_profile_enable(m, 1) clears the records and starts recording;
+ * dg_profile_read waits for the recorded events and returns the summed
+ * elapsed milliseconds and the number of launch groups of class `cls`. */
+enum {
+  DG_PROF_DENSE = 0,          /* QKV and O projections, self-conditioning projection */
+  DG_PROF_ATTN = 1,           /* attention partials + merge                          */
+  DG_PROF_ROUTER = 2,         /* router logits, top-k, expert permutation            */
+  DG_PROF_EXPERT_GATEUP = 3,  /* grouped expert gate/up GEMM with GELU-gating         */
+  DG_PROF_EXPERT_DOWN = 4,    /* grouped expert down GEMM                            */
+  DG_PROF_SHARED = 5,         /* shared FFN                                          */
+  DG_PROF_LMHEAD = 6,         /* LM-head logits GEMM                                 */
+  DG_PROF_SAMPLER = 7,        /* entropy / Gumbel / lock / stop                       */
+  DG_PROF_SOFTEMB = 8,        /* soft-prediction embedding                           */
+  DG_PROF_OTHER = 9,          /* norms, RoPE, combine                                */
+  DG_PROF_NCLASS = 10
+};
+dg_status dg_profile_enable(dg_model* m, int32_t on);
+dg_status dg_profile_read(dg_model* m, int32_t cls, double* total_ms, int32_t* count);
+
 /* Host-side reference entry points of the library's own sampler arithmetic
  * (same source as the device code; no GPU needed): Philox4x32-10 block,
  * fp32 log, Gumbel variate of a 32-bit word, 1/tau of a step. */
