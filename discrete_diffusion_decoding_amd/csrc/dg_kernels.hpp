@@ -9,12 +9,14 @@ namespace dg {
 
 enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_ADD_F32 = 2, EPI_ADD_GATED_F32 = 3, EPI_GEGLU_BF16 = 4 };
 
-// C[r, n] (op)= sum_k A[row(r), k] * W_g[n, k] for r in the rows of group g.
+// C[r, n] (op)= sum_k A[row(r), k] * W_g[n, k] over row chunks ("items").
 // A: bf16 rows of pitch lda; row(r) = a_rows ? a_rows[r] : r.
 // W: bf16 [N, ldw] per group, groups w_gstride elements apart (W2 likewise for GEGLU).
-// Groups: rows [group_off[g], group_off[g+1]) (or [0, M) with one group).
-// Rows are processed in chunks of 16*MF; `m_split` lanes of work share a group's
-// chunks.  Split-K: `k_split` ranges of `k_chunk`, partial outputs c_kstride apart.
+// Items: with `items` (device int4 {group, first row, row count, 0}, count in
+// *n_items), each item is one chunk of <= 64 rows of one group; without, the
+// rows [0, M) of group 0 are cut into chunks of 64.  items_max bounds the item
+// count (the grid is items_max x column tiles x k_split; spare workgroups exit).
+// Split-K: `k_split` ranges of `k_chunk`, partial outputs c_kstride apart.
 struct GemmArgs {
   const bf16_t* A;
   long lda;
@@ -25,10 +27,10 @@ struct GemmArgs {
   long w_gstride;
   int K, N;
   int k_chunk;
-  const int32_t* group_off;
+  const int4* items;
+  const int32_t* n_items;
+  int items_max;
   int M;
-  int G;
-  int m_split;
   int k_split;
   void* C;
   long ldc;
@@ -37,7 +39,8 @@ struct GemmArgs {
   const int32_t* flag;
 };
 
-hipError_t gemm(int epi, int mf, const GemmArgs& a, hipStream_t s);
+hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
+constexpr int kGemmRowChunk = 64;
 
 // ---- elementwise / reduction kernels (k_elem.hip) ----
 struct RowsCtx {
@@ -81,8 +84,11 @@ hipError_t attention_merge(const float* opart, const float* mlpart, int splits, 
 
 hipError_t router_topk(const float* rlog, int rows, int E, int k, int32_t* idx, float* gate,
                        int32_t* idx_dump, float* gate_dump, const int32_t* flag, hipStream_t s);
+// also emits the GEMM work list: int4 {expert, first slot, rows, 0} per chunk of
+// <= chunk rows of every touched expert, and its length in *n_items
 hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* counts, int32_t* offsets,
-                       int32_t* slot_of, int32_t* slot_row, const int32_t* flag, hipStream_t s);
+                       int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
+                       const int32_t* flag, hipStream_t s);
 // h[r] += ys[r] + sum_j gate[r,j] * Y[slot_of[r,j]]; then optional next RMSNorm -> xn, dump of h
 hipError_t moe_combine(float* h, const float* ys, const float* Y, const int32_t* slot_of, const float* gate,
                        int rows, int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump,

@@ -165,8 +165,8 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // ---------------------------------------------------------------------------
 // workspace plan
 struct Plan {
-  size_t h, xn, qkv, q, kc, vc, opart, ml, o, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, hbuf, ybuf,
-      hs, ys, logits, spart, rowstat, P, separt, flag, total;
+  size_t h, xn, qkv, q, kc, vc, opart, ml, o, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
+      nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, P, separt, flag, total;
   int splits_max, vsplit, ksplit, kchunk;
 };
 
@@ -214,6 +214,8 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.off = take((E + 1) * 4);
   p.slot_of = take(R * k * 4);
   p.slot_row = take(R * k * 4);
+  p.items = take((E + (R * k + kGemmRowChunk - 1) / kGemmRowChunk) * 16);
+  p.nitems = take(16);
   p.hbuf = take(R * k * d.d_expert * 2);
   p.ybuf = take(R * k * D * 4);
   p.hs = take(R * std::max(d.d_shared, 1) * 2);
@@ -264,10 +266,16 @@ static const bf16_t* lw(const dg_model* m, int l, size_t off) { return m->layers
 static GemmArgs gargs() {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
-  g.G = 1;
-  g.m_split = 1;
   g.k_split = 1;
   return g;
+}
+
+// dense rows [0, M) in chunks of kGemmRowChunk
+static void dense_rows(GemmArgs& g, int M) {
+  g.M = M;
+  g.items = nullptr;
+  g.n_items = nullptr;
+  g.items_max = cdiv(M, kGemmRowChunk);
 }
 
 static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pass& ps, hipStream_t st) {
@@ -292,16 +300,18 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   int32_t* off = at<int32_t>(ws, p.off);
   int32_t* slot_of = at<int32_t>(ws, p.slot_of);
   int32_t* slot_row = at<int32_t>(ws, p.slot_row);
+  int4* items = at<int4>(ws, p.items);
+  int32_t* nitems = at<int32_t>(ws, p.nitems);
+  const int items_max = E + cdiv((long)R * k, kGemmRowChunk);
   bf16_t* hbuf = at<bf16_t>(ws, p.hbuf);
   float* ybuf = at<float>(ws, p.ybuf);
   bf16_t* hs = at<bf16_t>(ws, p.hs);
   float* ys = fs ? at<float>(ws, p.ys) : nullptr;
-  const int msplit = cdiv(R, 64);
 
   // attention split choice: about one workgroup per CU
   const int GQ = H / Hkv;
   const int nkeys = ps.prefill ? ps.q0 + R : ps.P + ps.per_batch;
-  const int base_wg = cdiv(ps.per_batch, 16 * (4 / GQ)) * Hkv * ps.B;
+  const int base_wg = cdiv(ps.per_batch, 128 / GQ) * Hkv * ps.B;   // attention workgroups per key split
   int splits = std::max(1, std::min(p.splits_max, cdiv(256, base_wg)));
   const int split_len = cdiv(cdiv(nkeys, splits), 32) * 32;
   splits = cdiv(nkeys, split_len);
@@ -315,9 +325,9 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     {
       GemmArgs g = gargs();
       g.A = xn; g.lda = D; g.W = lw(m, l, m->lay.w_qkv); g.ldw = D; g.K = D; g.N = qkvd; g.k_chunk = D;
-      g.M = R; g.m_split = msplit; g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
+      dense_rows(g, R); g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_DENSE, st);
-      DG_CK(gemm(EPI_STORE_BF16, 4, g, st));
+      DG_CK(gemm(EPI_STORE_BF16, g, st));
     }
     // QK norm + RoPE; K / V^T scatter
     {
@@ -373,9 +383,9 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     {
       GemmArgs g = gargs();
       g.A = o; g.lda = H * hd; g.W = lw(m, l, m->lay.w_o); g.ldw = H * hd; g.K = H * hd; g.N = D;
-      g.k_chunk = H * hd; g.M = R; g.m_split = msplit; g.C = h; g.ldc = D; g.flag = ps.flag;
+      g.k_chunk = H * hd; dense_rows(g, R); g.C = h; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_DENSE, st);
-      DG_CK(gemm(EPI_ADD_F32, 4, g, st));
+      DG_CK(gemm(EPI_ADD_F32, g, st));
     }
     {
       ProfScope ps_(m, DG_PROF_OTHER, st);
@@ -385,42 +395,44 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     {
       GemmArgs g = gargs();
       g.A = xr; g.lda = D; g.W = lw(m, l, m->lay.w_router); g.ldw = D; g.K = D; g.N = E; g.k_chunk = D;
-      g.M = 2 * R; g.m_split = cdiv(2 * R, 64); g.C = rlog; g.ldc = E; g.flag = ps.flag;
+      dense_rows(g, 2 * R); g.C = rlog; g.ldc = E; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_ROUTER, st);
-      DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+      DG_CK(gemm(EPI_STORE_F32, g, st));
     }
     {
     ProfScope psr_(m, DG_PROF_ROUTER, st);
     DG_CK(router_topk(rlog, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
                       ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
-    DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, ps.flag, st));
+    DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, kGemmRowChunk, ps.flag, st));
     }
     // experts: gate/up (GEGLU) then down, grouped by expert over the permuted slots
     {
       GemmArgs g = gargs();
       g.A = xn2; g.lda = D; g.a_rows = slot_row; g.W = lw(m, l, m->lay.w_gate); g.W2 = lw(m, l, m->lay.w_up);
-      g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D; g.group_off = off; g.G = E;
+      g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D;
+      g.items = items; g.n_items = nitems; g.items_max = items_max;
       g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_GATEUP, st);
-      DG_CK(gemm(EPI_GEGLU_BF16, 4, g, st));
+      DG_CK(gemm(EPI_GEGLU_BF16, g, st));
     }
     {
       GemmArgs g = gargs();
       g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
-      g.N = D; g.k_chunk = fe; g.group_off = off; g.G = E; g.C = ybuf; g.ldc = D; g.flag = ps.flag;
+      g.N = D; g.k_chunk = fe; g.items = items; g.n_items = nitems; g.items_max = items_max;
+      g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
-      DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+      DG_CK(gemm(EPI_STORE_F32, g, st));
     }
     if (fs) {
       ProfScope ps_(m, DG_PROF_SHARED, st);
       GemmArgs g = gargs();
       g.A = xn2; g.lda = D; g.W = lw(m, l, m->lay.w_gate_sh); g.W2 = lw(m, l, m->lay.w_up_sh); g.ldw = D;
-      g.K = D; g.N = fs; g.k_chunk = D; g.M = R; g.m_split = msplit; g.C = hs; g.ldc = fs; g.flag = ps.flag;
-      DG_CK(gemm(EPI_GEGLU_BF16, 4, g, st));
+      g.K = D; g.N = fs; g.k_chunk = D; dense_rows(g, R); g.C = hs; g.ldc = fs; g.flag = ps.flag;
+      DG_CK(gemm(EPI_GEGLU_BF16, g, st));
       GemmArgs g2 = gargs();
       g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D; g2.k_chunk = fs;
-      g2.M = R; g2.m_split = msplit; g2.C = ys; g2.ldc = D; g2.flag = ps.flag;
-      DG_CK(gemm(EPI_STORE_F32, 4, g2, st));
+      dense_rows(g2, R); g2.C = ys; g2.ldc = D; g2.flag = ps.flag;
+      DG_CK(gemm(EPI_STORE_F32, g2, st));
     }
     const bf16_t* nw = nullptr;
     if (l + 1 < d.n_layers) nw = lw(m, l + 1, m->lay.attn_norm);
@@ -562,10 +574,10 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   if (d.self_cond) {
     GemmArgs g = gargs();
     g.A = (const bf16_t*)c->self_cond; g.lda = D; g.W = (const bf16_t*)m->w.self_cond_w; g.ldw = D; g.K = D;
-    g.N = D; g.k_chunk = D; g.M = R; g.m_split = cdiv(R, 64); g.C = h; g.ldc = D;
+    g.N = D; g.k_chunk = D; dense_rows(g, R); g.C = h; g.ldc = D;
     g.col_gate = (const bf16_t*)m->w.self_cond_gate; g.flag = flag;
     ProfScope ps_(m, DG_PROF_DENSE, st);
-    DG_CK(gemm(EPI_ADD_GATED_F32, 4, g, st));
+    DG_CK(gemm(EPI_ADD_GATED_F32, g, st));
   }
   DG_CK(rmsnorm_rows(h, m->layers[0] + m->lay.attn_norm, R, D, d.rms_eps, xn, nullptr, c->hidden_dump, flag, st));
   Pass ps{};
@@ -579,10 +591,9 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   float* logits = c->logits_dump ? c->logits_dump : at<float>(ws, p.logits);
   {
     GemmArgs g = gargs();
-    g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D; g.M = R;
-    g.m_split = cdiv(R, 64); g.C = logits; g.ldc = V; g.flag = flag;
+    g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D; dense_rows(g, R); g.C = logits; g.ldc = V; g.flag = flag;
     ProfScope ps_(m, DG_PROF_LMHEAD, st);
-    DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+    DG_CK(gemm(EPI_STORE_F32, g, st));
   }
   float* rowstat = at<float>(ws, p.rowstat);
   SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, rowstat,
@@ -598,9 +609,9 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, flag, st));
     GemmArgs g = gargs();
     g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
-    g.k_split = p.ksplit; g.M = R; g.m_split = cdiv(R, 64); g.C = at<float>(ws, p.separt); g.ldc = D;
+    g.k_split = p.ksplit; dense_rows(g, R); g.C = at<float>(ws, p.separt); g.ldc = D;
     g.c_kstride = (long)R * D; g.flag = flag;
-    DG_CK(gemm(EPI_STORE_F32, 4, g, st));
+    DG_CK(gemm(EPI_STORE_F32, g, st));
     DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, c->stopped, T, flag,
                             st));
   }
@@ -712,8 +723,8 @@ extern "C" dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int
   if (K % 64) return DG_ERR_SHAPE;
   GemmArgs g = gargs();
   g.A = (const bf16_t*)A; g.lda = lda; g.W = (const bf16_t*)W; g.ldw = ldw; g.K = K; g.N = N; g.k_chunk = K;
-  g.M = M; g.m_split = cdiv(M, 64); g.C = Cm; g.ldc = ldc;
-  DG_CK(gemm(EPI_STORE_F32, 4, g, (hipStream_t)stream));
+  dense_rows(g, M); g.C = Cm; g.ldc = ldc;
+  DG_CK(gemm(EPI_STORE_F32, g, (hipStream_t)stream));
   return DG_OK;
 }
 

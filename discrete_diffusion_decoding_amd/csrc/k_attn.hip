@@ -5,14 +5,19 @@
 // every canvas key of their own canvas; prefix queries (prefill) see keys at
 // positions <= their own.  Query head h reads key/value head h / (H / Hkv).
 //
-// One wave owns 16 query rows of one head.  Per tile of 32 keys it computes
-// S^T = K Q^T with keys as the MFMA M dimension, so each lane ends up holding
-// 8 probabilities of ONE query row (keys 4*(l/16)+i and 16+4*(l/16)+i).  Those
-// 8 values are exactly an A operand of the P V product if the same 32-key
-// order is used for the B operand, which is read from V^T (values are cached
-// transposed, [head][dim][position]) with two 8-byte loads.  No LDS is used.
-// Scores are kept in log2 units (scale * log2 e folded in).  Each key split
-// writes unnormalised O with its running max / sum; a merge kernel combines.
+// A workgroup (8 waves) owns 8 row fragments of 16 (query, head) rows that share
+// one key/value head: 16 * 8 / GQ queries times the GQ query heads of that kv
+// head.  Key/value tiles of 32 keys are loaded cooperatively (16-byte loads,
+// clamped and branch-free) into double-buffered LDS; the next tile's loads are
+// in flight while the current one is multiplied.  K rows are padded by 16 bytes
+// and V^T rows (values are cached transposed, [head][dim][position]) by 16 bytes
+// so the MFMA operand reads hit distinct banks.
+//
+// Each wave computes S^T = K Q^T with keys as the MFMA M dimension, so every
+// lane holds 8 probabilities of ONE query row (keys 4*(l/16)+i and 16+4*(l/16)+i);
+// those 8 values are the A operand of P V when the B operand (from V^T) uses
+// the same 32-key order.  Scores are kept in log2 units.  Each key split writes
+// unnormalised O with its running max / sum; attention_merge combines them.
 #include <math.h>
 
 #include "dg_kernels.hpp"
@@ -20,38 +25,102 @@
 namespace dg {
 
 template <int HD>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
+  constexpr int KP = HD + 8;   // K tile pitch (elements)
+  constexpr int VP = 40;       // V^T tile pitch (elements): 32 keys + pad
+  constexpr int KCH = 32 * HD / 8;   // 16-byte chunks of a K tile
+  constexpr int VCH = HD * 4;        // 16-byte chunks of a V^T tile
+  constexpr int KPT = (KCH + 511) / 512, VPT = (VCH + 511) / 512;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][32 * KP];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][HD * VP];
   if (a.flag && *a.flag) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int GQ = a.H / a.Hkv;
-  const int qb_per_wg = 4 / GQ;
-  const int hq = wave % GQ, qb = wave / GQ;
+  const int qpw = 128 / GQ;                      // queries per workgroup
   const int g = blockIdx.y % a.Hkv, split = blockIdx.y / a.Hkv;
   const int b = blockIdx.z;
-  const int h = g * GQ + hq;
   const int R = a.rows_per_batch;
-  const int qrow0 = (blockIdx.x * qb_per_wg + qb) * 16;
-  if (qrow0 >= R) return;
+  const int q0wg = blockIdx.x * qpw;
+  const int hq = wave % GQ, qf = wave / GQ;      // this wave's head and query fragment
+  const int h = g * GQ + hq;
+  const int qrow0 = q0wg + qf * 16;
   const int lr = lane & 15, lg = lane >> 4;
-
-  const int myq = min(qrow0 + lr, R - 1);
-  const bf16_t* qp = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
-  constexpr int KS = HD / 32;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = load_bf16x8(qp + 32 * ks);
 
   const int nk = a.n1 + a.n2;
   const int kbeg = split * a.split_len;
   int kend = min(nk, kbeg + a.split_len);
-  if (a.causal) kend = min(kend, a.qpos0 + min(qrow0 + 15, R - 1) + 1);
-  const int qpos = a.qpos0 + myq;
+  if (a.causal) kend = min(kend, a.qpos0 + min(q0wg + qpw, R));
+  const int ntile = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
 
   const int b1 = (a.nb1 == 1) ? 0 : b;
   const bf16_t* K1 = a.k1 + b1 * a.k1_bstride + g * a.k1_hstride;
   const bf16_t* V1 = a.vt1 + b1 * a.v1_bstride + g * a.v1_hstride;
-  const bf16_t* K2 = a.k2 ? a.k2 + b * a.k2_bstride + g * a.k2_hstride : nullptr;
-  const bf16_t* V2 = a.vt2 ? a.vt2 + b * a.v2_bstride + g * a.v2_hstride : nullptr;
+  const bf16_t* K2 = a.k2 ? a.k2 + b * a.k2_bstride + g * a.k2_hstride : K1;
+  const bf16_t* V2 = a.vt2 ? a.vt2 + b * a.v2_bstride + g * a.v2_hstride : V1;
+
+  // Q fragments: B operand of S^T (row = lr, hd slots 32 ks + 8 lg)
+  const int myq = min(qrow0 + lr, R - 1);
+  const bf16_t* qp = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
+  constexpr int KS = HD / 32;
+  bf16x8 qfr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qfr[ks] = load_bf16x8(qp + 32 * ks);
+  const int qpos = a.qpos0 + myq;
+  const bool wave_live = qrow0 < R;
+
+  // cooperative tile loads (registers -> LDS); at most two 16-byte chunks of
+  // K and two of V^T per thread (hd <= 256), written out slot by slot so the
+  // staging values stay in registers
+  static_assert(KPT <= 2 && VPT <= 2, "tile staging assumes hd <= 256");
+  uint4 ks0v, ks1v, vs0v, vs1v;
+#define DG_K_SRC(C)                                                                                \
+  ({                                                                                               \
+    const int kc_ = min(kt_ + min((C) / (HD / 8), 31), nk - 1);                                    \
+    (kc_ < a.n1 ? K1 + (long)kc_ * HD : K2 + (long)(kc_ - a.n1) * HD) + ((C) % (HD / 8)) * 8;      \
+  })
+#define DG_V_SRC(C)                                                                                \
+  ({                                                                                               \
+    const int c_ = min((C), VCH - 1);                                                              \
+    (kt_ < a.n1 ? V1 + (long)(c_ >> 2) * a.v1_pitch + kt_ : V2 + (long)(c_ >> 2) * a.v2_pitch + (kt_ - a.n1)) \
+        + (c_ & 3) * 8;                                                                            \
+  })
+#define DG_ATTN_ISSUE(KT)                                                                          \
+  do {                                                                                             \
+    const int kt_ = (KT);                                                                          \
+    ks0v = *reinterpret_cast<const uint4*>(DG_K_SRC(tid));                                         \
+    if (KPT > 1) ks1v = *reinterpret_cast<const uint4*>(DG_K_SRC(tid + 512));                      \
+    vs0v = *reinterpret_cast<const uint4*>(DG_V_SRC(tid));                                         \
+    if (VPT > 1) vs1v = *reinterpret_cast<const uint4*>(DG_V_SRC(tid + 512));                      \
+  } while (0)
+#define DG_K_PUT(BUF, C, V)                                                                        \
+  do {                                                                                             \
+    if (KCH % 512 == 0 || (C) < KCH)                                                               \
+      *reinterpret_cast<uint4*>(&Ks[BUF][((C) / (HD / 8)) * KP + ((C) % (HD / 8)) * 8]) = (V);     \
+  } while (0)
+#define DG_V_PUT(BUF, KT, C, VV)                                                                   \
+  do {                                                                                             \
+    if (VCH % 512 == 0 || (C) < VCH) {                                                             \
+      uint4 v = (VV);                                                                              \
+      const int k0 = (KT) + ((C) & 3) * 8; /* zero the values of keys beyond the valid range */    \
+      if (k0 + 8 > nk) {                                                                           \
+        const int nv = max(0, nk - k0);                                                            \
+        v.x = nv >= 2 ? v.x : (nv == 1 ? (v.x & 0x0000FFFFu) : 0u);                                 \
+        v.y = nv >= 4 ? v.y : (nv == 3 ? (v.y & 0x0000FFFFu) : 0u);                                 \
+        v.z = nv >= 6 ? v.z : (nv == 5 ? (v.z & 0x0000FFFFu) : 0u);                                 \
+        v.w = nv >= 8 ? v.w : (nv == 7 ? (v.w & 0x0000FFFFu) : 0u);                                 \
+      }                                                                                            \
+      *reinterpret_cast<uint4*>(&Vs[BUF][((C) >> 2) * VP + ((C) & 3) * 8]) = v;                    \
+    }                                                                                              \
+  } while (0)
+#define DG_ATTN_STORE(BUF, KT)                                                                     \
+  do {                                                                                             \
+    DG_K_PUT(BUF, tid, ks0v);                                                                      \
+    if (KPT > 1) DG_K_PUT(BUF, tid + 512, ks1v);                                                   \
+    DG_V_PUT(BUF, KT, tid, vs0v);                                                                  \
+    if (VPT > 1) DG_V_PUT(BUF, KT, tid + 512, vs1v);                                               \
+  } while (0)
 
   floatx4 O[HD / 16];
 #pragma unroll
@@ -59,79 +128,89 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
 
-  for (int kt = kbeg; kt < kend; kt += 32) {
-    floatx4 s[2];
+  if (ntile > 0) {
+    DG_ATTN_ISSUE(kbeg);
+    DG_ATTN_STORE(0, kbeg);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int buf = t & 1;
+    const int kt = kbeg + 32 * t;
+    if (t + 1 < ntile) DG_ATTN_ISSUE(kt + 32);
+    if (wave_live) {
+      floatx4 s[2];
 #pragma unroll
-    for (int kf = 0; kf < 2; ++kf) {
-      const int key = min(kt + kf * 16 + lr, nk - 1);
-      const bf16_t* kp = (key < a.n1 ? K1 + (long)key * HD : K2 + (long)(key - a.n1) * HD) + lg * 8;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kf = 0; kf < 2; ++kf) {
+        const bf16_t* kp = &Ks[buf][(kf * 16 + lr) * KP + lg * 8];
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(load_bf16x8(kp + 32 * ks), qf[ks], acc);
-      s[kf] = acc;
-    }
-    float p[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kf = 0; kf < 2; ++kf)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt + kf * 16 + lg * 4 + i;
-        const bool ok = key < kend && (!a.causal || key <= qpos);
-        const float v = ok ? s[kf][i] * sl2 : -INFINITY;
-        p[kf * 4 + i] = v;
-        mx = fmaxf(mx, v);
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(load_bf16x8(kp + 32 * ks), qfr[ks], acc);
+        s[kf] = acc;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const bool live = m_new != -INFINITY;
-    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
-    float ps = 0.f;
+      float p[8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = live ? exp2f(p[e] - m_new) : 0.f;
-      ps += p[e];
-    }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // O rows are 4*lg + i; their alpha lives in lane (4*lg + i)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float ai = __shfl(alpha, lg * 4 + i, 64);
-#pragma unroll
-      for (int nf = 0; nf < HD / 16; ++nf) O[nf][i] *= ai;
-    }
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];
-#pragma unroll
-    for (int nf = 0; nf < HD / 16; ++nf) {
-      const int dim = nf * 16 + lr;
-      bf16x8 vb;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int key0 = kt + hh * 16 + lg * 4;
-        uint2 raw = {0u, 0u};
-        if (key0 < nk) {
-          const bf16_t* vp = key0 < a.n1 ? V1 + (long)dim * a.v1_pitch + key0
-                                          : V2 + (long)dim * a.v2_pitch + (key0 - a.n1);
-          raw = *reinterpret_cast<const uint2*>(vp);
-        }
-        uint16_t w[4] = {(uint16_t)(raw.x & 0xFFFF), (uint16_t)(raw.x >> 16), (uint16_t)(raw.y & 0xFFFF),
-                         (uint16_t)(raw.y >> 16)};
+      for (int kf = 0; kf < 2; ++kf)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool okk = (key0 + i) < nk;
-          vb[hh * 4 + i] = __builtin_bit_cast(__bf16, okk ? w[i] : (uint16_t)0);
+          const int key = kt + kf * 16 + lg * 4 + i;
+          const bool ok = key < kend && (!a.causal || key <= qpos);
+          const float v = ok ? s[kf][i] * sl2 : -INFINITY;
+          p[kf * 4 + i] = v;
+          mx = fmaxf(mx, v);
         }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const bool live = m_new != -INFINITY;
+      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+      float ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = live ? exp2f(p[e] - m_new) : 0.f;
+        ps += p[e];
       }
-      O[nf] = mfma16x16x32(pf, vb, O[nf]);
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, lg * 4 + i, 64);
+#pragma unroll
+        for (int nf = 0; nf < HD / 16; ++nf) O[nf][i] *= ai;
+      }
+      bf16x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];
+#pragma unroll
+      for (int nf = 0; nf < HD / 16; ++nf) {
+        const bf16_t* vp = &Vs[buf][(nf * 16 + lr) * VP + lg * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+        bf16x8 vb;
+        vb[0] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x & 0xFFFF));
+        vb[1] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x >> 16));
+        vb[2] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y & 0xFFFF));
+        vb[3] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y >> 16));
+        vb[4] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x & 0xFFFF));
+        vb[5] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x >> 16));
+        vb[6] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y & 0xFFFF));
+        vb[7] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y >> 16));
+        O[nf] = mfma16x16x32(pf, vb, O[nf]);
+      }
     }
+    if (t + 1 < ntile) DG_ATTN_STORE(buf ^ 1, kt + 32);
+    __syncthreads();
   }
 
+#undef DG_ATTN_ISSUE
+#undef DG_ATTN_STORE
+#undef DG_K_SRC
+#undef DG_V_SRC
+#undef DG_K_PUT
+#undef DG_V_PUT
+  if (!wave_live) return;
   const long BR = (long)a.B * R;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -151,13 +230,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 hipError_t attention(const AttnArgs& a, hipStream_t s) {
   const int GQ = a.H / a.Hkv;
   if (a.H % a.Hkv != 0 || (GQ != 1 && GQ != 2 && GQ != 4)) return hipErrorInvalidValue;
-  if (a.split_len % 32 != 0 || a.rows_per_batch <= 0) return hipErrorInvalidValue;
-  const int qb_per_wg = 4 / GQ;
-  dim3 grid((a.rows_per_batch + 16 * qb_per_wg - 1) / (16 * qb_per_wg), a.Hkv * a.splits, a.B);
+  if (a.split_len % 32 != 0 || a.rows_per_batch <= 0 || (a.n2 > 0 && a.n1 % 32 != 0)) return hipErrorInvalidValue;
+  const int qpw = 128 / GQ;
+  dim3 grid((a.rows_per_batch + qpw - 1) / qpw, a.Hkv * a.splits, a.B);
   switch (a.hd) {
-    case 64: hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(attn_kernel<256>, grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(512), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(512), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(attn_kernel<256>, grid, dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

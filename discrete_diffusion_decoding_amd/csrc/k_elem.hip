@@ -168,34 +168,44 @@ hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of key-split attention partials (scores kept in log2 units).
+// Merge of key-split attention partials (scores kept in log2 units): per row,
+// the split weights 2^(m_s - M) / L of every head are formed once in LDS, then
+// the outputs are summed with coalesced reads of the partials.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const float* ml, int splits, int rows,
                                                          int H, int hd, bf16_t* out, const int32_t* flag) {
   if (flag && *flag) return;
+  __shared__ float wts[1024];
   const int r = blockIdx.x;
   const long srow = (long)rows * H;
-  for (int idx = threadIdx.x; idx < H * hd; idx += blockDim.x) {
-    const int h = idx / hd;
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
     const long base = (long)r * H + h;
     float M = -INFINITY;
     for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(s * srow + base) * 2]);
-    float L = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < splits; ++s) {
-        const float m = ml[(s * srow + base) * 2];
-        if (m == -INFINITY) continue;
-        const float w = exp2f(m - M);
-        L += w * ml[(s * srow + base) * 2 + 1];
-        acc += w * op[(s * srow + base) * hd + (idx - h * hd)];
-      }
+    float L = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float m = ml[(s * srow + base) * 2];
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      wts[h * splits + s] = w;
+      L += w * ml[(s * srow + base) * 2 + 1];
     }
-    out[(long)r * H * hd + idx] = f2bf(L > 0.f ? acc / L : 0.f);
+    const float il = L > 0.f ? 1.0f / L : 0.f;
+    for (int s = 0; s < splits; ++s) wts[h * splits + s] *= il;
+  }
+  __syncthreads();
+  const long rowoff = (long)r * H * hd;
+  const long sstride = srow * hd;
+  for (int idx = threadIdx.x; idx < H * hd; idx += blockDim.x) {
+    const int h = idx / hd;
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) acc += wts[h * splits + s] * op[s * sstride + rowoff + idx];
+    out[rowoff + idx] = f2bf(acc);
   }
 }
 
 hipError_t attention_merge(const float* opart, const float* mlpart, int splits, int rows, int H, int hd,
                            bf16_t* out, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (H * splits > 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(attn_merge_kernel, dim3(rows), dim3(256), 0, s, opart, mlpart, splits, rows, H, hd, out, flag);
   return hipGetLastError();
 }
@@ -279,11 +289,13 @@ hipError_t router_topk(const float* rlog, int rows, int E, int k, int32_t* idx, 
 // 16 waves of a tile and across tiles.
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int na, int k, int E, int32_t* counts,
                                                        int32_t* offsets, int32_t* slot_of, int32_t* slot_row,
+                                                       int4* items, int32_t* n_items, int chunk,
                                                        const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ int wcnt[16][256];
   __shared__ int cnt[256];
   __shared__ int off[257];
+  __shared__ int ibase[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < 256; e += 1024) cnt[e] = 0;
   for (int base = 0; base < na; base += 1024) {
@@ -317,17 +329,25 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
     __syncthreads();
   }
   if (tid == 0) {
-    int run = 0;
+    int run = 0, ni = 0;
     for (int e = 0; e < E; ++e) {
       off[e] = run;
+      ibase[e] = ni;
       run += cnt[e];
+      ni += (cnt[e] + chunk - 1) / chunk;
     }
     off[E] = run;
+    ibase[E] = ni;
+    *n_items = ni;
   }
   __syncthreads();
   for (int e = tid; e <= E; e += 1024) {
     offsets[e] = off[e];
-    if (e < E) counts[e] = cnt[e];
+    if (e < E) {
+      counts[e] = cnt[e];
+      int i = ibase[e];
+      for (int r = 0; r < cnt[e]; r += chunk, ++i) items[i] = make_int4(e, off[e] + r, min(chunk, cnt[e] - r), 0);
+    }
   }
   for (int a = tid; a < na; a += 1024) {
     const int e = idx[a];
@@ -338,11 +358,12 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
 }
 
 hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* counts, int32_t* offsets,
-                       int32_t* slot_of, int32_t* slot_row, const int32_t* flag, hipStream_t s) {
+                       int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
+                       const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (E > 255) return hipErrorInvalidValue;
+  if (E > 255 || chunk < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(1024), 0, s, idx, rows * k, k, E, counts, offsets, slot_of,
-                     slot_row, flag);
+                     slot_row, items, n_items, chunk, flag);
   return hipGetLastError();
 }
 
