@@ -170,12 +170,16 @@ def main():
     setup_s = time.perf_counter() - t0
     log(f"model resident after {setup_s:.1f}s")
     prefix = torch.as_tensor(synth.tokens(args.seed, "prefix", (Bp, P), m.vocab)).cuda()
+    torch.cuda.synchronize()
+    # a non-default stream: libdg replays each step as a captured hipGraph there
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     seeds = synth.row_seeds(args.seed, B)
     kv = dm.kv_cache(Bp, P)
     ws = dm.workspace(B * T, P + T)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    dg.dg_prefill_prefix(dm.handle, prefix, Bp, P, P, kv, ws)
+    dg.dg_prefill_prefix(dm.handle, prefix, Bp, P, P, kv, ws, stream=stream)
     e1.record()
     torch.cuda.synchronize()
     prefill_ms = e0.elapsed_time(e1)
@@ -185,26 +189,28 @@ def main():
     sampler, keep = dg.make_sampler(sp, seeds)
     st = dm.canvas_state(B, T)
     canvas = dg.make_canvas(st)
-    dg.dg_init_canvas(dm.handle, canvas, B, T, seeds)
+    dg.dg_init_canvas(dm.handle, canvas, B, T, seeds, stream=stream)
 
     # one dumped step: touched experts per layer
     ed = torch.zeros(m.n_layers, B * T, m.top_k, dtype=torch.int32, device="cuda")
     st_d = dict(st)
     st_d["expert_dump"] = ed
-    dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, dg.make_canvas(st_d), 0, sampler, ws)
+    dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, dg.make_canvas(st_d), 0, sampler, ws, stream=stream)
+    torch.cuda.synchronize()
     edh = ed.cpu().numpy()
     touched = [len(np.unique(edh[l])) for l in range(m.n_layers)]
 
     step_idx = 1
     for _ in range(args.warmup):
-        dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws)
+        dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws, stream=stream)
         step_idx = step_idx % (sp.max_steps - 2) + 1
     torch.cuda.synchronize()
     st["stopped"].zero_()
+    torch.cuda.synchronize()
     e0.record()
     h0 = time.perf_counter()
     for _ in range(args.steps):
-        dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws)
+        dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws, stream=stream)
         step_idx = step_idx % (sp.max_steps - 2) + 1
     e1.record()
     torch.cuda.synchronize()
@@ -217,7 +223,7 @@ def main():
         dg.dg_profile_enable(dm.handle, True)
         kp = max(1, min(args.steps, 5))
         for _ in range(kp):
-            dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws)
+            dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, canvas, step_idx, sampler, ws, stream=stream)
             step_idx = step_idx % (sp.max_steps - 2) + 1
         torch.cuda.synchronize()
         prof = dg.dg_profile_read(dm.handle)
@@ -227,9 +233,9 @@ def main():
 
     steps_taken, block_ms = None, None
     if not args.no_block:
-        dg.dg_init_canvas(dm.handle, canvas, B, T, seeds)
+        dg.dg_init_canvas(dm.handle, canvas, B, T, seeds, stream=stream)
         e0.record()
-        dg.dg_generate_block(dm.handle, kv, Bp, P, P, B, T, canvas, sampler, ws, poll_every=8)
+        dg.dg_generate_block(dm.handle, kv, Bp, P, P, B, T, canvas, sampler, ws, poll_every=8, stream=stream)
         e1.record()
         torch.cuda.synchronize()
         block_ms = e0.elapsed_time(e1)

@@ -43,17 +43,20 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
 constexpr int kGemmRowChunk = 64;
 
 // ---- elementwise / reduction kernels (k_elem.hip) ----
-struct RowsCtx {
-  int rows;        // token rows in this pass
-  int per_batch;   // rows per batch element (T for the canvas, chunk for prefill)
-  int pos0;        // absolute position of the first row of each batch element
-};
 
 hipError_t embed_rows(const int32_t* tokens, const bf16_t* E, int rows, int d, float* h,
                       const int32_t* flag, hipStream_t s);
-// out = bf16(rms(h) * w); optional hi/lo split rows for the router, optional dump of h
-hipError_t rmsnorm_rows(const float* h, const bf16_t* w, int rows, int d, float eps, bf16_t* out,
-                        bf16_t* split_hi_lo, float* dump, const int32_t* flag, hipStream_t s);
+// Split-K partial sums: nsplit slices `stride` floats apart, each [rows][d] (or [rows][E]).
+struct Partials {
+  const float* p;
+  int n;
+  long stride;
+};
+
+// h += (gate ? sigmoid(gate) : 1) * sum_s part_s (optional); out = bf16(rms(h) * w);
+// optional hi/lo split rows for the router, optional dump of h
+hipError_t rmsnorm_rows(float* h, const bf16_t* w, int rows, int d, float eps, bf16_t* out, bf16_t* split_hi_lo,
+                        float* dump, Partials part, const bf16_t* part_gate, const int32_t* flag, hipStream_t s);
 // per-head RMSNorm + RoPE of q and k, scatter of k / v into the attention caches
 struct QkRopeArgs {
   const bf16_t* qkv; int rows; int H, Hkv, hd; float eps; float theta;
@@ -82,15 +85,16 @@ hipError_t attention(const AttnArgs& a, hipStream_t s);
 hipError_t attention_merge(const float* opart, const float* mlpart, int splits, int rows, int H, int hd,
                            bf16_t* out, const int32_t* flag, hipStream_t s);
 
-hipError_t router_topk(const float* rlog, int rows, int E, int k, int32_t* idx, float* gate,
-                       int32_t* idx_dump, float* gate_dump, const int32_t* flag, hipStream_t s);
+// router logits = sum over split-K partials of the hi rows [0, rows) and lo rows [rows, 2 rows)
+hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
+                       float* gate_dump, const int32_t* flag, hipStream_t s);
 // also emits the GEMM work list: int4 {expert, first slot, rows, 0} per chunk of
 // <= chunk rows of every touched expert, and its length in *n_items
 hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* counts, int32_t* offsets,
                        int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
                        const int32_t* flag, hipStream_t s);
-// h[r] += ys[r] + sum_j gate[r,j] * Y[slot_of[r,j]]; then optional next RMSNorm -> xn, dump of h
-hipError_t moe_combine(float* h, const float* ys, const float* Y, const int32_t* slot_of, const float* gate,
+// h[r] += sum_s ys_s[r] + sum_j gate[r,j] * Y[slot_of[r,j]]; then optional next RMSNorm -> xn, dump of h
+hipError_t moe_combine(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate,
                        int rows, int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump,
                        const int32_t* flag, hipStream_t s);
 
@@ -117,7 +121,7 @@ hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf1
 hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* seeds, hipStream_t s);
 hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
 hipError_t fill_u16(uint16_t* p, uint16_t v, long n, hipStream_t s);
-hipError_t set_step(int32_t* steps, int B, int step, hipStream_t s);
+hipError_t set_step(int32_t* steps, const int32_t* stopped, int B, int step, hipStream_t s);
 hipError_t transpose_bf16(const bf16_t* in, bf16_t* out, long rows, long cols, hipStream_t s);
 
 }  // namespace dg

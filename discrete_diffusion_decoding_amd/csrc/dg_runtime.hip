@@ -31,12 +31,34 @@ struct Prof {
   size_t used = 0;
 };
 
+// A captured step (one hipGraph per distinct set of step arguments).
+struct GraphKey {
+  int kind;  // 0: dg_denoise_step, 1: a step of dg_generate_block (stop-flag early exits)
+  const void* kv;
+  int Bp, P, P_max, B, T;
+  dg_canvas c;
+  float tau_start, tau_end, lock_thresh, stop_thresh;
+  int max_steps, lock_rule, stop_rule;
+  uint64_t seeds[16];
+  void* ws;
+  size_t ws_bytes;
+};
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraphExec_t exec;
+  unsigned long long last_use;
+};
+
 struct dg_model {
   dg_model_desc d;
   dg_weights w;
   std::vector<const bf16_t*> layers;
   dg_layer_layout lay;
   mutable Prof prof;
+  bool use_graphs = true;
+  std::vector<GraphEntry> graphs;
+  unsigned long long use_clock = 0;
 };
 
 // timing scope: records an event pair around the enclosed launches when on
@@ -153,7 +175,14 @@ extern "C" dg_status dg_model_create(const dg_model_desc* d, const dg_weights* w
 extern "C" void dg_model_destroy(dg_model* m) {
   if (!m) return;
   for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
+  for (GraphEntry& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
   delete m;
+}
+
+extern "C" dg_status dg_set_graphs(dg_model* m, int32_t enable) {
+  if (!m) return DG_ERR_ARG;
+  m->use_graphs = enable != 0;
+  return DG_OK;
 }
 
 extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
@@ -165,12 +194,25 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // ---------------------------------------------------------------------------
 // workspace plan
 struct Plan {
-  size_t h, xn, qkv, q, kc, vc, opart, ml, o, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
+  size_t h, xn, qkv, q, kc, vc, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
       nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, P, separt, flag, total;
   int splits_max, vsplit, ksplit, kchunk;
 };
 
 static const int kMaxSplits = 16;
+static const int kMaxDenseSplit = 8;    // split-K slices of a dense projection
+static const int kMaxRouterSplit = 16;  // split-K slices of the router logits
+
+// Split the contraction of a dense product when its output tiles alone would
+// leave the GPU short of ~512 workgroups (2 per CU): returns the slice count and
+// sets the 64-aligned slice length.
+static int choose_ksplit(long tiles_times_items, int K, int max_split, int* k_chunk) {
+  int ks = (int)std::max(1L, std::min((long)max_split, (512 + tiles_times_items - 1) / tiles_times_items));
+  ks = std::min(ks, std::max(1, K / 128));
+  int kc = cdiv(cdiv(K, ks), 64) * 64;
+  *k_chunk = kc;
+  return cdiv(K, kc);
+}
 
 static void soft_split(const dg_model_desc& d, int rows, int* ksplit, int* kchunk) {
   const int items = cdiv(d.d_model, 128) * cdiv(rows, 64);
@@ -205,9 +247,10 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.opart = take((size_t)kMaxSplits * R * H * hd * 4);
   p.ml = take((size_t)kMaxSplits * R * H * 2 * 4);
   p.o = take(R * H * hd * 2);
+  p.dpart = take((size_t)kMaxDenseSplit * R * D * 4);
   p.xn2 = take(R * D * 2);
   p.xr = take(2 * R * D * 2);
-  p.rlog = take(2 * R * E * 4);
+  p.rlog = take((size_t)kMaxRouterSplit * 2 * R * E * 4);
   p.eidx = take(R * k * 4);
   p.egate = take(R * k * 4);
   p.cnt = take((E + 1) * 4);
@@ -219,7 +262,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.hbuf = take(R * k * d.d_expert * 2);
   p.ybuf = take(R * k * D * 4);
   p.hs = take(R * std::max(d.d_shared, 1) * 2);
-  p.ys = take(d.d_shared ? R * D * 4 : 0);
+  p.ys = take(d.d_shared ? (size_t)kMaxDenseSplit * R * D * 4 : 0);
   if (V) {
     p.vsplit = vsplit_of(rows, (int)V);
     p.logits = take(R * V * 4);
@@ -379,31 +422,40 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       DG_CK(attention(a, st));
       DG_CK(attention_merge(at<float>(ws, p.opart), at<float>(ws, p.ml), splits, R, H, hd, o, ps.flag, st));
     }
-    // O projection + residual
+    // O projection: split-K partials, summed into the residual by the next norm
+    Partials opp{at<float>(ws, p.dpart), 1, (long)R * D};
     {
       GemmArgs g = gargs();
       g.A = o; g.lda = H * hd; g.W = lw(m, l, m->lay.w_o); g.ldw = H * hd; g.K = H * hd; g.N = D;
-      g.k_chunk = H * hd; dense_rows(g, R); g.C = h; g.ldc = D; g.flag = ps.flag;
+      dense_rows(g, R);
+      g.k_split = choose_ksplit((long)g.items_max * cdiv(D, 64), H * hd, kMaxDenseSplit, &g.k_chunk);
+      opp.n = g.k_split;
+      g.C = at<float>(ws, p.dpart); g.ldc = D; g.c_kstride = (long)R * D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_DENSE, st);
-      DG_CK(gemm(EPI_ADD_F32, g, st));
+      DG_CK(gemm(EPI_STORE_F32, g, st));
     }
     {
       ProfScope ps_(m, DG_PROF_OTHER, st);
-      DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, ps.flag, st));
+      DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, opp, nullptr, ps.flag,
+                         st));
     }
-    // router logits (hi and lo rows) and top-k
+    // router logits (hi and lo rows, split-K partials) and top-k
+    Partials rlp{rlog, 1, (long)2 * R * E};
     {
       GemmArgs g = gargs();
-      g.A = xr; g.lda = D; g.W = lw(m, l, m->lay.w_router); g.ldw = D; g.K = D; g.N = E; g.k_chunk = D;
-      dense_rows(g, 2 * R); g.C = rlog; g.ldc = E; g.flag = ps.flag;
+      g.A = xr; g.lda = D; g.W = lw(m, l, m->lay.w_router); g.ldw = D; g.K = D; g.N = E;
+      dense_rows(g, 2 * R);
+      g.k_split = choose_ksplit((long)g.items_max * cdiv(E, 64), D, kMaxRouterSplit, &g.k_chunk);
+      rlp.n = g.k_split;
+      g.C = rlog; g.ldc = E; g.c_kstride = (long)2 * R * E; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_ROUTER, st);
       DG_CK(gemm(EPI_STORE_F32, g, st));
     }
     {
-    ProfScope psr_(m, DG_PROF_ROUTER, st);
-    DG_CK(router_topk(rlog, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
-                      ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
-    DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, kGemmRowChunk, ps.flag, st));
+      ProfScope psr_(m, DG_PROF_ROUTER, st);
+      DG_CK(router_topk(rlp, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
+                        ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
+      DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, kGemmRowChunk, ps.flag, st));
     }
     // experts: gate/up (GEGLU) then down, grouped by expert over the permuted slots
     {
@@ -423,6 +475,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_F32, g, st));
     }
+    Partials ysp{ys, 0, (long)R * D};
     if (fs) {
       ProfScope ps_(m, DG_PROF_SHARED, st);
       GemmArgs g = gargs();
@@ -430,8 +483,11 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.K = D; g.N = fs; g.k_chunk = D; dense_rows(g, R); g.C = hs; g.ldc = fs; g.flag = ps.flag;
       DG_CK(gemm(EPI_GEGLU_BF16, g, st));
       GemmArgs g2 = gargs();
-      g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D; g2.k_chunk = fs;
-      dense_rows(g2, R); g2.C = ys; g2.ldc = D; g2.flag = ps.flag;
+      g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
+      dense_rows(g2, R);
+      g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, 64), fs, kMaxDenseSplit, &g2.k_chunk);
+      ysp.n = g2.k_split;
+      g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
       DG_CK(gemm(EPI_STORE_F32, g2, st));
     }
     const bf16_t* nw = nullptr;
@@ -439,7 +495,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     else if (ps.final_norm) nw = (const bf16_t*)m->w.final_norm;
     {
       ProfScope psc_(m, DG_PROF_OTHER, st);
-      DG_CK(moe_combine(h, ys, ybuf, slot_of, egate, R, D, k, nw, d.rms_eps, xn,
+      DG_CK(moe_combine(h, ysp, ybuf, slot_of, egate, R, D, k, nw, d.rms_eps, xn,
                         ps.hidden_dump ? ps.hidden_dump + (size_t)(l + 1) * R * D : nullptr, ps.flag, st));
     }
   }
@@ -469,7 +525,7 @@ extern "C" dg_status dg_forward_hidden(dg_model* m, const void* kv, int32_t Bp, 
   // the caller's hidden buffer is the residual stream
   DG_CK(hipMemcpyAsync(at<float>(ws, p.h), hidden, (size_t)R * m->d.d_model * 4, hipMemcpyDeviceToDevice, st));
   DG_CK(rmsnorm_rows(at<float>(ws, p.h), m->layers[0] + m->lay.attn_norm, R, m->d.d_model, m->d.rms_eps,
-                     at<bf16_t>(ws, p.xn), nullptr, hidden_dump, nullptr, st));
+                     at<bf16_t>(ws, p.xn), nullptr, hidden_dump, Partials{nullptr, 0, 0}, nullptr, nullptr, st));
   Pass ps{};
   ps.rows = R; ps.B = B; ps.per_batch = T; ps.pos0 = P; ps.prefill = false;
   ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = Bp; ps.P = P; ps.P_max = P_max;
@@ -505,7 +561,7 @@ static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* h
                              (size_t)R * d.d_model * 4, hipMemcpyDeviceToDevice, st));
       }
       DG_CK(rmsnorm_rows(at<float>(ws, p.h), m->layers[0] + m->lay.attn_norm, R, d.d_model, d.rms_eps,
-                         at<bf16_t>(ws, p.xn), nullptr, nullptr, nullptr, st));
+                         at<bf16_t>(ws, p.xn), nullptr, nullptr, Partials{nullptr, 0, 0}, nullptr, nullptr, st));
       Pass ps{};
       ps.rows = R; ps.B = 1; ps.per_batch = R; ps.pos0 = q0; ps.prefill = true; ps.bp = bp; ps.q0 = q0;
       ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = 1; ps.P = 0; ps.P_max = P_max;
@@ -571,15 +627,20 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   float* h = at<float>(ws, p.h);
   bf16_t* xn = at<bf16_t>(ws, p.xn);
   DG_CK(embed_rows(c->tokens, (const bf16_t*)m->w.embed, R, D, h, flag, st));
+  // self-conditioning: split-K partials of s_prev W_sc^T, gated and added by the first norm
+  Partials scp{at<float>(ws, p.dpart), 0, (long)R * D};
   if (d.self_cond) {
     GemmArgs g = gargs();
     g.A = (const bf16_t*)c->self_cond; g.lda = D; g.W = (const bf16_t*)m->w.self_cond_w; g.ldw = D; g.K = D;
-    g.N = D; g.k_chunk = D; dense_rows(g, R); g.C = h; g.ldc = D;
-    g.col_gate = (const bf16_t*)m->w.self_cond_gate; g.flag = flag;
+    g.N = D; dense_rows(g, R);
+    g.k_split = choose_ksplit((long)g.items_max * cdiv(D, 64), D, kMaxDenseSplit, &g.k_chunk);
+    scp.n = g.k_split;
+    g.C = at<float>(ws, p.dpart); g.ldc = D; g.c_kstride = (long)R * D; g.flag = flag;
     ProfScope ps_(m, DG_PROF_DENSE, st);
-    DG_CK(gemm(EPI_ADD_GATED_F32, g, st));
+    DG_CK(gemm(EPI_STORE_F32, g, st));
   }
-  DG_CK(rmsnorm_rows(h, m->layers[0] + m->lay.attn_norm, R, D, d.rms_eps, xn, nullptr, c->hidden_dump, flag, st));
+  DG_CK(rmsnorm_rows(h, m->layers[0] + m->lay.attn_norm, R, D, d.rms_eps, xn, nullptr, c->hidden_dump, scp,
+                     (const bf16_t*)m->w.self_cond_gate, flag, st));
   Pass ps{};
   ps.rows = R; ps.B = B; ps.per_batch = T; ps.pos0 = P; ps.prefill = false;
   ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = Bp; ps.P = P; ps.P_max = P_max;
@@ -619,6 +680,76 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   return DG_OK;
 }
 
+__global__ void dg_all_stopped_kernel(const int32_t* stopped, int B, int32_t* flag) {
+  if (threadIdx.x == 0) {
+    int all = 1;
+    for (int b = 0; b < B; ++b) all &= (stopped[b] != 0);
+    *flag = all;
+  }
+}
+
+// Enqueue one step whose step index is read from canvas->steps on the device,
+// as a replay of a captured hipGraph when possible (the default stream cannot
+// be captured, and profiling records events: those run the launches directly).
+static dg_status step_device_indexed(dg_model* m, const void* kv, int Bp, int P, int P_max, int B, int T,
+                                     dg_canvas* c, const dg_sampler* sp, void* ws, size_t ws_bytes, const Plan& p,
+                                     int32_t* flag, hipStream_t st) {
+  auto enqueue = [&]() -> dg_status {
+    dg_status r = step_impl(m, kv, Bp, P, P_max, B, T, c, -1, sp, ws, p, flag, nullptr, st);
+    if (r != DG_OK) return r;
+    if (flag) {
+      hipLaunchKernelGGL(dg_all_stopped_kernel, dim3(1), dim3(64), 0, st, c->stopped, B, flag);
+      DG_CK(hipGetLastError());
+    }
+    return DG_OK;
+  };
+  if (!m->use_graphs || m->prof.on || st == nullptr) return enqueue();
+  GraphKey key;
+  memset(&key, 0, sizeof(key));
+  key.kind = flag ? 1 : 0;
+  key.kv = kv; key.Bp = Bp; key.P = P; key.P_max = P_max; key.B = B; key.T = T;
+  key.c = *c;
+  key.tau_start = sp->tau_start; key.tau_end = sp->tau_end; key.lock_thresh = sp->lock_thresh;
+  key.stop_thresh = sp->stop_thresh; key.max_steps = sp->max_steps; key.lock_rule = sp->lock_rule;
+  key.stop_rule = sp->stop_rule;
+  for (int b = 0; b < B && b < 16; ++b) key.seeds[b] = sp->row_seeds[b];
+  key.ws = ws; key.ws_bytes = ws_bytes;
+  for (GraphEntry& g : m->graphs) {
+    if (memcmp(&g.key, &key, sizeof(key)) == 0) {
+      g.last_use = ++m->use_clock;
+      DG_CK(hipGraphLaunch(g.exec, st));
+      return DG_OK;
+    }
+  }
+  DG_CK(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+  dg_status r = enqueue();
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(st, &graph);
+  if (r != DG_OK || ec != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (r != DG_OK) return r;
+    fprintf(stderr, "libdg: stream capture failed: %s\n", hipGetErrorString(ec));
+    return DG_ERR_HIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) {
+    fprintf(stderr, "libdg: graph instantiation failed: %s\n", hipGetErrorString(ei));
+    return DG_ERR_HIP;
+  }
+  if (m->graphs.size() >= 8) {
+    size_t oldest = 0;
+    for (size_t i = 1; i < m->graphs.size(); ++i)
+      if (m->graphs[i].last_use < m->graphs[oldest].last_use) oldest = i;
+    (void)hipGraphExecDestroy(m->graphs[oldest].exec);
+    m->graphs.erase(m->graphs.begin() + oldest);
+  }
+  m->graphs.push_back(GraphEntry{key, exec, ++m->use_clock});
+  DG_CK(hipGraphLaunch(exec, st));
+  return DG_OK;
+}
+
 extern "C" dg_status dg_denoise_step(dg_model* m, const void* kv, int32_t Bp, int32_t P, int32_t P_max, int32_t B,
                                      int32_t T, dg_canvas* canvas, int32_t step, const dg_sampler* sp, void* ws,
                                      size_t ws_bytes, dg_stream_t stream) {
@@ -630,15 +761,11 @@ extern "C" dg_status dg_denoise_step(dg_model* m, const void* kv, int32_t Bp, in
   if (step < 0 || !ws || (P > 0 && !kv)) return DG_ERR_ARG;
   const Plan p = make_plan(m->d, B * T, P + T);
   if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
-  return step_impl(m, kv, Bp, P, P_max, B, T, canvas, step, sp, ws, p, nullptr, nullptr, (hipStream_t)stream);
-}
-
-__global__ void dg_all_stopped_kernel(const int32_t* stopped, int B, int32_t* flag) {
-  if (threadIdx.x == 0) {
-    int all = 1;
-    for (int b = 0; b < B; ++b) all &= (stopped[b] != 0);
-    *flag = all;
-  }
+  hipStream_t st = (hipStream_t)stream;
+  // the step index of every running row goes to the device; the step itself
+  // reads it there, so one captured graph serves every step index
+  DG_CK(set_step(canvas->steps, canvas->stopped, B, step, st));
+  return step_device_indexed(m, kv, Bp, P, P_max, B, T, canvas, sp, ws, ws_bytes, p, nullptr, st);
 }
 
 extern "C" dg_status dg_generate_block(dg_model* m, const void* kv, int32_t Bp, int32_t P, int32_t P_max,
@@ -660,10 +787,8 @@ extern "C" dg_status dg_generate_block(dg_model* m, const void* kv, int32_t Bp, 
   if (m->d.self_cond)
     DG_CK(fill_u16((uint16_t*)canvas->self_cond, 0, (long)B * T * m->d.d_model, st));
   for (int step = 0; step < sp->max_steps; ++step) {
-    s = step_impl(m, kv, Bp, P, P_max, B, T, canvas, -1, sp, ws, p, flag, nullptr, st);
+    s = step_device_indexed(m, kv, Bp, P, P_max, B, T, canvas, sp, ws, ws_bytes, p, flag, st);
     if (s != DG_OK) return s;
-    hipLaunchKernelGGL(dg_all_stopped_kernel, dim3(1), dim3(64), 0, st, canvas->stopped, B, flag);
-    DG_CK(hipGetLastError());
     if (poll_every > 0 && (step + 1) % poll_every == 0 && step + 1 < sp->max_steps) {
       int32_t hf = 0;
       DG_CK(hipMemcpyAsync(&hf, flag, sizeof(int32_t), hipMemcpyDeviceToHost, st));

@@ -30,19 +30,26 @@ hipError_t embed_rows(const int32_t* tokens, const bf16_t* E, int rows, int d, f
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const bf16_t* w, int rows, int d, float eps,
-                                                      bf16_t* out, bf16_t* split, float* dump,
-                                                      const int32_t* flag) {
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w, int rows, int d, float eps,
+                                                      bf16_t* out, bf16_t* split, float* dump, Partials part,
+                                                      const bf16_t* pgate, const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ float red[16];
   const int r = blockIdx.x;
-  const float* x = h + (long)r * d;
+  float* x = h + (long)r * d;
   float v[DG_MAXD_PER_THREAD];
   float ss = 0.f;
   int n = 0;
   for (int c = threadIdx.x; c < d; c += 256, ++n) {
-    v[n] = x[c];
-    ss += v[n] * v[n];
+    float xv = x[c];
+    if (part.n > 0) {
+      float acc = 0.f;
+      for (int s = 0; s < part.n; ++s) acc += part.p[s * part.stride + (long)r * d + c];
+      xv += pgate ? sigmoidf_(bf2f(pgate[c])) * acc : acc;
+      x[c] = xv;
+    }
+    v[n] = xv;
+    ss += xv * xv;
   }
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
@@ -59,12 +66,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const bf16
   }
 }
 
-hipError_t rmsnorm_rows(const float* h, const bf16_t* w, int rows, int d, float eps, bf16_t* out,
-                        bf16_t* split_hi_lo, float* dump, const int32_t* flag, hipStream_t s) {
+hipError_t rmsnorm_rows(float* h, const bf16_t* w, int rows, int d, float eps, bf16_t* out, bf16_t* split_hi_lo,
+                        float* dump, Partials part, const bf16_t* part_gate, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (d > 256 * DG_MAXD_PER_THREAD) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, h, w, rows, d, eps, out, split_hi_lo, dump,
-                     flag);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, h, w, rows, d, eps, out, split_hi_lo, dump, part,
+                     part_gate, flag);
   return hipGetLastError();
 }
 
@@ -214,7 +221,7 @@ hipError_t attention_merge(const float* opart, const float* mlpart, int splits, 
 // Router: logits = hi-part + lo-part products (an fp32-accurate product from two
 // bf16 MFMA passes), top-k by repeated wavefront argmax (ties -> lower expert),
 // gates = softmax over the k selected logits.  One wave per token row.
-__global__ __launch_bounds__(256) void topk_kernel(const float* rl, int rows, int E, int k, int32_t* idx,
+__global__ __launch_bounds__(256) void topk_kernel(Partials rl, int rows, int E, int k, int32_t* idx,
                                                    float* gate, int32_t* idx_dump, float* gate_dump,
                                                    const int32_t* flag) {
   if (flag && *flag) return;
@@ -225,7 +232,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* rl, int rows, in
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    v[j] = (e < E) ? rl[(long)r * E + e] + rl[(long)(rows + r) * E + e] : -INFINITY;
+    float hi = 0.f, lo = 0.f;
+    if (e < E) {
+      for (int s = 0; s < rl.n; ++s) {
+        hi += rl.p[s * rl.stride + (long)r * E + e];
+        lo += rl.p[s * rl.stride + (long)(rows + r) * E + e];
+      }
+    }
+    v[j] = (e < E) ? hi + lo : -INFINITY;
   }
   float selv[16];
   int seli[16];
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* rl, int rows, in
   }
 }
 
-hipError_t router_topk(const float* rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
+hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
                        float* gate_dump, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (E > 256 || k > 16 || k > E) return hipErrorInvalidValue;
@@ -368,7 +382,7 @@ hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* coun
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(float* h, const float* ys, const float* Y,
+__global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, const float* Y,
                                                       const int32_t* slot_of, const float* gate, int d, int k,
                                                       const bf16_t* nw, float eps, bf16_t* xn, float* dump,
                                                       const int32_t* flag) {
@@ -388,7 +402,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* h, const float* ys,
   for (int c = threadIdx.x; c < d; c += 256, ++n) {
     float acc = 0.f;
     for (int j = 0; j < k; ++j) acc += gts[j] * Y[(long)slots[j] * d + c];
-    if (ys) acc += ys[(long)r * d + c];
+    for (int s = 0; s < ys.n; ++s) acc += ys.p[s * ys.stride + (long)r * d + c];
     const float x = h[(long)r * d + c] + acc;
     h[(long)r * d + c] = x;
     v[n] = x;
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* h, const float* ys,
   }
 }
 
-hipError_t moe_combine(float* h, const float* ys, const float* Y, const int32_t* slot_of, const float* gate, int rows,
+hipError_t moe_combine(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate, int rows,
                        int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump, const int32_t* flag,
                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;

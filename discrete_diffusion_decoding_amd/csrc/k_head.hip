@@ -277,12 +277,13 @@ hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* see
   return hipGetLastError();
 }
 
-__global__ void set_step_kernel(int32_t* steps, int B, int step) {
-  if (threadIdx.x < B) steps[threadIdx.x] = step;
+__global__ void set_step_kernel(int32_t* steps, const int32_t* stopped, int B, int step) {
+  if (threadIdx.x < B && !stopped[threadIdx.x]) steps[threadIdx.x] = step;
 }
 
-hipError_t set_step(int32_t* steps, int B, int step, hipStream_t s) {
-  hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(64), 0, s, steps, B, step);
+hipError_t set_step(int32_t* steps, const int32_t* stopped, int B, int step, hipStream_t s) {
+  if (B > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(set_step_kernel, dim3(1), dim3(64), 0, s, steps, stopped, B, step);
   return hipGetLastError();
 }
 

@@ -87,6 +87,7 @@ def lib():
             "dg_transpose_bf16": (st, [vp, vp, C.c_int64, C.c_int64, vp]),
             "dg_gemm_bf16": (st, [vp, C.c_int64, vp, C.c_int64, i32, i32, i32, vp, C.c_int64, vp]),
             "dg_profile_enable": (st, [vp, i32]),
+            "dg_set_graphs": (st, [vp, i32]),
             "dg_profile_read": (st, [vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]),
             "dg_host_philox": (None, [C.POINTER(C.c_uint32), C.POINTER(C.c_uint32), C.POINTER(C.c_uint32)]),
             "dg_host_ln": (C.c_float, [C.c_float]),
@@ -218,6 +219,10 @@ def dg_gemm_bf16(A, W, Cout, M, N, K, lda=None, ldw=None, ldc=None, stream=None)
 
 PROF_CLASSES = ("dense", "attn", "router", "expert_gateup", "expert_down", "shared", "lmhead", "sampler",
                 "softemb", "other")
+
+
+def dg_set_graphs(h, on: bool):
+    _ck(lib().dg_set_graphs(h, 1 if on else 0), "dg_set_graphs")
 
 
 def dg_profile_enable(h, on: bool):

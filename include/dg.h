@@ -153,6 +153,12 @@ dg_status dg_layer_layout_get(const dg_model_desc* desc, dg_layer_layout* out);
 dg_status dg_model_create(const dg_model_desc* desc, const dg_weights* w, dg_model** out);
 void dg_model_destroy(dg_model* m);
 
+/* Replay each step as a captured hipGraph (default on).  Applies to
+ * dg_denoise_step and dg_generate_block on a non-default stream; the default
+ * stream cannot be captured and always runs the kernels directly.  Graphs are
+ * cached per distinct argument set (up to 8) and freed by dg_model_destroy. */
+dg_status dg_set_graphs(dg_model* m, int32_t enable);
+
 /* Bytes of the key/value cache for Bp prefixes of capacity P_max:
  * per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][hd][P_max], bf16. */
 size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max);

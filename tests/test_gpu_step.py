@@ -187,3 +187,36 @@ def test_tiny_block_equals_repeated_steps():
         assert np.array_equal(host(a[k]), host(b[k])), k
     assert host(a["steps"]).tolist() == [6, 6] and host(a["stopped"]).tolist() == [1, 1]
     dm.close()
+
+
+def test_graph_replay_equals_eager_launches():
+    """Steps replayed from a captured hipGraph (non-default stream) equal the
+    same steps launched kernel by kernel, bit for bit, over several steps."""
+    wl = WORKLOADS["tiny_step"]
+    m = wl.model
+    B, T, P = 1, wl.canvas_len, wl.prefix_len
+    dm = DeviceModel(m, SEED)
+    prefix = synth.tokens(SEED, "prefix", (1, P), m.vocab)
+    seeds = synth.row_seeds(SEED, B)
+    kv = dm.kv_cache(1, P)
+    ws = dm.workspace(B * T, P + T)
+    dg.dg_prefill_prefix(dm.handle, dev(prefix), 1, P, P, kv, ws)
+    sampler, keep = dg.make_sampler(SamplerParams(), seeds)
+    a = dm.canvas_state(B, T)
+    dg.dg_init_canvas(dm.handle, dg.make_canvas(a), B, T, seeds)
+    b = {k: v.clone() for k, v in a.items()}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    announce("graph replay: captured steps on a side stream")
+    ca = dg.make_canvas(a)
+    for step in range(5):
+        dg.dg_denoise_step(dm.handle, kv, 1, P, P, B, T, ca, step, sampler, ws, stream=s)
+    s.synchronize()
+    announce("graph replay: eager steps on the default stream")
+    dg.dg_set_graphs(dm.handle, False)
+    cb = dg.make_canvas(b)
+    for step in range(5):
+        dg.dg_denoise_step(dm.handle, kv, 1, P, P, B, T, cb, step, sampler, ws)
+    for k in ("tokens", "xhat", "argmax", "entropy", "locked", "stopped", "steps"):
+        assert np.array_equal(host(a[k]), host(b[k])), k
+    dm.close()
