@@ -40,6 +40,10 @@ struct GemmArgs {
 };
 
 hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
+// 256 activation rows x 128 weight rows per workgroup; dense rows only (items_max =
+// ceil(M / 256)); epilogues EPI_STORE_F32 (split-K partials) and EPI_STORE_BF16
+hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s);
+constexpr int kFatRowChunk = 256;
 constexpr int kGemmRowChunk = 64;
 
 // ---- elementwise / reduction kernels (k_elem.hip) ----
@@ -60,6 +64,7 @@ hipError_t rmsnorm_rows(float* h, const bf16_t* w, int rows, int d, float eps, b
 // per-head RMSNorm + RoPE of q and k, scatter of k / v into the attention caches
 struct QkRopeArgs {
   const bf16_t* qkv; int rows; int H, Hkv, hd; float eps; float theta;
+  const float2* rope;               // [per_batch][hd/2] (cos, sin) from rope_table
   const bf16_t* qnorm; const bf16_t* knorm;
   bf16_t* q;                        // [rows][H][hd]
   int per_batch, pos0;              // position of row r = pos0 + (r % per_batch)
@@ -69,6 +74,7 @@ struct QkRopeArgs {
   const int32_t* flag;
 };
 hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s);
+hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta, hipStream_t s);
 
 struct AttnArgs {
   const bf16_t* q; int H, Hkv, hd; float scale;

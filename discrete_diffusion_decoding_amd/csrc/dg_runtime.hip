@@ -12,6 +12,7 @@
 // Nothing here allocates device memory; every buffer is carved out of the
 // caller's workspace.
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -122,7 +123,8 @@ static dg_status check_desc(const dg_model_desc* d) {
   if (d->d_model % 64 || d->d_model > 4096 || d->d_expert % 64 || d->d_shared % 64 ||
       (d->n_heads * d->head_dim) % 64)
     return DG_ERR_SHAPE;
-  if (d->n_experts > 255 || d->top_k > 16 || d->top_k > d->n_experts) return DG_ERR_SHAPE;
+  if (d->n_experts > 255 || d->top_k > d->n_experts) return DG_ERR_SHAPE;
+  if (d->top_k != 1 && d->top_k != 2 && d->top_k != 4 && d->top_k != 8) return DG_ERR_SHAPE;
   if (d->vocab % 128) return DG_ERR_SHAPE;
   if (d->self_cond && d->vocab == 0) return DG_ERR_SHAPE;
   return DG_OK;
@@ -194,14 +196,14 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // ---------------------------------------------------------------------------
 // workspace plan
 struct Plan {
-  size_t h, xn, qkv, q, kc, vc, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
+  size_t h, xn, qkv, q, kc, vc, rope, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
       nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, P, separt, flag, total;
   int splits_max, vsplit, ksplit, kchunk;
 };
 
 static const int kMaxSplits = 16;
 static const int kMaxDenseSplit = 8;    // split-K slices of a dense projection
-static const int kMaxRouterSplit = 16;  // split-K slices of the router logits
+static const int kMaxRouterSplit = 8;   // split-K slices of the router logits
 
 // Split the contraction of a dense product when its output tiles alone would
 // leave the GPU short of ~512 workgroups (2 per CU): returns the slice count and
@@ -244,6 +246,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.q = take(R * H * hd * 2);
   p.kc = take(R * Hkv * hd * 2);
   p.vc = take(R * Hkv * hd * 2);
+  p.rope = take(R * (hd / 2) * 8);
   p.opart = take((size_t)kMaxSplits * R * H * hd * 4);
   p.ml = take((size_t)kMaxSplits * R * H * 2 * 4);
   p.o = take(R * H * hd * 2);
@@ -359,6 +362,10 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   const int split_len = cdiv(cdiv(nkeys, splits), 32) * 32;
   splits = cdiv(nkeys, split_len);
 
+  {
+    ProfScope ps_(m, DG_PROF_OTHER, st);
+    DG_CK(rope_table(at<float2>(ws, p.rope), ps.per_batch, ps.pos0, hd, d.rope_theta, st));
+  }
   for (int l = 0; l < d.n_layers; ++l) {
     const bf16_t* kvl = ps.kv ? ps.kv + (size_t)l * layer_kv : nullptr;
     const size_t bpo = ps.prefill ? (size_t)ps.bp * kv_one : 0;   // prefill: this prefix only
@@ -378,7 +385,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       memset(&a, 0, sizeof(a));
       a.qkv = qkv; a.rows = R; a.H = H; a.Hkv = Hkv; a.hd = hd; a.eps = d.rms_eps; a.theta = d.rope_theta;
       a.qnorm = lw(m, l, m->lay.q_norm); a.knorm = lw(m, l, m->lay.k_norm); a.q = q;
-      a.per_batch = ps.per_batch; a.pos0 = ps.pos0; a.flag = ps.flag;
+      a.per_batch = ps.per_batch; a.pos0 = ps.pos0; a.flag = ps.flag; a.rope = at<float2>(ws, p.rope);
       if (ps.prefill) {
         a.kdst = const_cast<bf16_t*>(Kc); a.k_bstride = 0; a.k_hstride = (long)ps.P_max * hd;
         a.vtdst = const_cast<bf16_t*>(Vc); a.v_bstride = 0; a.v_hstride = (long)hd * ps.P_max; a.v_pitch = ps.P_max;
@@ -848,7 +855,8 @@ extern "C" dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int
   if (K % 64) return DG_ERR_SHAPE;
   GemmArgs g = gargs();
   g.A = (const bf16_t*)A; g.lda = lda; g.W = (const bf16_t*)W; g.ldw = ldw; g.K = K; g.N = N; g.k_chunk = K;
-  dense_rows(g, M); g.C = Cm; g.ldc = ldc;
+  g.C = Cm; g.ldc = ldc;
+  dense_rows(g, M);
   DG_CK(gemm(EPI_STORE_F32, g, (hipStream_t)stream));
   return DG_OK;
 }

@@ -1,17 +1,39 @@
 // Row-wise kernels of one transformer layer of the denoising step (gfx950):
-// embedding gather, RMSNorm, per-head QK RMSNorm + rotary embedding with the
-// scatter of K and V^T into the attention caches, split-attention merge, MoE
-// router top-k, expert permutation (wavefront ballot scans) and the combine
-// that also produces the next RMSNorm.  All are bandwidth-trivial next to the
-// weight streams; they are written to keep the number of passes over the
-// activations low (one workgroup per token row, values kept in registers).
+// embedding gather, RMSNorm (optionally folding in split-K partial sums), the
+// per-step rotary table, per-head QK RMSNorm + rotary embedding writing K into
+// the attention caches, the tiled V -> V^T cache scatter, split-attention merge,
+// MoE router top-k, expert permutation (wavefront ballot scans) and the combine
+// that also produces the next RMSNorm.  They move little data next to the
+// weight streams, so they are written for latency: one workgroup per token row,
+// float4 accesses, every load of a row issued before it is reduced (split and
+// slot counts are template parameters, so the loops fully unroll).
 #include <math.h>
 
 #include "dg_kernels.hpp"
 
 namespace dg {
 
-#define DG_MAXD_PER_THREAD 16  // d_model <= 4096 with 256 threads
+#define DG_MAXC4 4  // float4 columns per thread: d_model <= 4096 with 256 threads
+
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 f4fma(float s, float4 a, float4 b) {
+  return make_float4(s * a.x + b.x, s * a.y + b.y, s * a.z + b.z, s * a.w + b.w);
+}
+__device__ __forceinline__ float f4dot(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float4 v) {
+  uint2 o;
+  o.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+  o.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+  *reinterpret_cast<uint2*>(p) = o;
+}
+__device__ __forceinline__ float4 load_bf16x4(const bf16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xFFFF0000u));
+}
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, const bf16_t* E, int d, float* h,
@@ -19,156 +41,218 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* tok, const bf
   if (flag && *flag) return;
   const int r = blockIdx.x;
   const bf16_t* e = E + (long)tok[r] * d;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) h[(long)r * d + c] = bf2f(e[c]);
+  for (int c = threadIdx.x * 4; c < d; c += blockDim.x * 4)
+    *reinterpret_cast<float4*>(h + (long)r * d + c) = load_bf16x4(e + c);
 }
 
 hipError_t embed_rows(const int32_t* tokens, const bf16_t* E, int rows, int d, float* h, const int32_t* flag,
                       hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (d % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(embed_kernel, dim3(rows), dim3(256), 0, s, tokens, E, d, h, flag);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
+// h += (gate ? sigmoid(gate) : 1) * sum_s part_s ; xn = bf16(rms(h) * w);
+// optional router hi/lo rows (xn2 and the bf16 residual of the fp32 value).
+template <int NS>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w, int rows, int d, float eps,
                                                       bf16_t* out, bf16_t* split, float* dump, Partials part,
                                                       const bf16_t* pgate, const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ float red[16];
   const int r = blockIdx.x;
-  float* x = h + (long)r * d;
-  float v[DG_MAXD_PER_THREAD];
-  float ss = 0.f;
-  int n = 0;
-  for (int c = threadIdx.x; c < d; c += 256, ++n) {
-    float xv = x[c];
-    if (part.n > 0) {
-      float acc = 0.f;
-      for (int s = 0; s < part.n; ++s) acc += part.p[s * part.stride + (long)r * d + c];
-      xv += pgate ? sigmoidf_(bf2f(pgate[c])) * acc : acc;
-      x[c] = xv;
+  const int d4 = d >> 2;
+  float4* x4 = reinterpret_cast<float4*>(h + (long)r * d);
+  float4 v[DG_MAXC4];
+  float4 ps[DG_MAXC4][NS > 0 ? NS : 1];
+#pragma unroll
+  for (int j = 0; j < DG_MAXC4; ++j) {
+    const int c4 = threadIdx.x + 256 * j;
+    if (c4 < d4) {
+      v[j] = x4[c4];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        ps[j][s] = reinterpret_cast<const float4*>(part.p + s * part.stride + (long)r * d)[c4];
     }
-    v[n] = xv;
-    ss += xv * xv;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < DG_MAXC4; ++j) {
+    const int c4 = threadIdx.x + 256 * j;
+    if (c4 < d4) {
+      if (NS > 0) {
+        float4 acc = ps[j][0];
+#pragma unroll
+        for (int s = 1; s < NS; ++s) acc = f4add(acc, ps[j][s]);
+        if (pgate) {
+          const float4 gt = load_bf16x4(pgate + 4 * c4);
+          acc = make_float4(sigmoidf_(gt.x) * acc.x, sigmoidf_(gt.y) * acc.y, sigmoidf_(gt.z) * acc.z,
+                            sigmoidf_(gt.w) * acc.w);
+        }
+        v[j] = f4add(v[j], acc);
+        x4[c4] = v[j];
+      }
+      ss += f4dot(v[j]);
+    }
   }
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  n = 0;
-  for (int c = threadIdx.x; c < d; c += 256, ++n) {
-    const float y = v[n] * inv * bf2f(w[c]);
-    const uint16_t hi = f2bf(y);
-    out[(long)r * d + c] = hi;
-    if (split) {
-      split[(long)r * d + c] = hi;
-      split[(long)(rows + r) * d + c] = f2bf(y - bf2f(hi));
+#pragma unroll
+  for (int j = 0; j < DG_MAXC4; ++j) {
+    const int c4 = threadIdx.x + 256 * j;
+    if (c4 < d4) {
+      const float4 wv = load_bf16x4(w + 4 * c4);
+      const float4 y = make_float4(v[j].x * inv * wv.x, v[j].y * inv * wv.y, v[j].z * inv * wv.z,
+                                   v[j].w * inv * wv.w);
+      store_bf16x4(out + (long)r * d + 4 * c4, y);
+      if (split) {
+        store_bf16x4(split + (long)r * d + 4 * c4, y);
+        const float4 hi = load_bf16x4(split + (long)r * d + 4 * c4);
+        store_bf16x4(split + (long)(rows + r) * d + 4 * c4,
+                     make_float4(y.x - hi.x, y.y - hi.y, y.z - hi.z, y.w - hi.w));
+      }
+      if (dump) reinterpret_cast<float4*>(dump + (long)r * d)[c4] = v[j];
     }
-    if (dump) dump[(long)r * d + c] = v[n];
   }
 }
 
 hipError_t rmsnorm_rows(float* h, const bf16_t* w, int rows, int d, float eps, bf16_t* out, bf16_t* split_hi_lo,
                         float* dump, Partials part, const bf16_t* part_gate, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d > 256 * DG_MAXD_PER_THREAD) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(rows), dim3(256), 0, s, h, w, rows, d, eps, out, split_hi_lo, dump, part,
-                     part_gate, flag);
+  if (d > 1024 * DG_MAXC4 || d % 4) return hipErrorInvalidValue;
+#define DG_NORM_CASE(N)                                                                               \
+  case N:                                                                                             \
+    hipLaunchKernelGGL(rmsnorm_kernel<N>, dim3(rows), dim3(256), 0, s, h, w, rows, d, eps, out, split_hi_lo, \
+                       dump, part, part_gate, flag);                                                  \
+    break;
+  switch (part.n) {
+    DG_NORM_CASE(0) DG_NORM_CASE(1) DG_NORM_CASE(2) DG_NORM_CASE(3) DG_NORM_CASE(4)
+    DG_NORM_CASE(5) DG_NORM_CASE(6) DG_NORM_CASE(7) DG_NORM_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef DG_NORM_CASE
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Rotary table of one pass: cos / sin of position pos0 + (r % per_batch) at
+// frequency theta^(-2j/hd), computed once in fp64 for all layers of the pass.
+__global__ void rope_table_kernel(float2* tab, int per_batch, int pos0, int half, float theta) {
+  const int t = blockIdx.x;
+  for (int j = threadIdx.x; j < half; j += blockDim.x) {
+    const double freq = exp(-(2.0 * (double)j / (double)(2 * half)) * log((double)theta));
+    double sv, cv;
+    sincos((double)(pos0 + t) * freq, &sv, &cv);
+    tab[(long)t * half + j] = make_float2((float)cv, (float)sv);
+  }
+}
+
+hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta, hipStream_t s) {
+  if (per_batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(per_batch), dim3(128), 0, s, tab, per_batch, pos0, hd / 2, theta);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // One workgroup per token row.  Waves take heads round-robin: q heads, then k
-// heads (both RMSNorm over head_dim + rotate-half RoPE), then v heads (copy).
-// Lane l holds elements l + 64 j of a head; the rotary partner of element e is
+// heads: RMSNorm over head_dim, then rotate-half RoPE from the table.  Lane l
+// holds elements l + 64 j of a head; the rotary partner of element e is
 // e +- hd/2, i.e. slot j +- hd/128 of the same lane when hd >= 128, or lane
 // l ^ (hd/2) when hd == 64.
 template <int HD>
 __global__ __launch_bounds__(256) void qk_rope_kernel(QkRopeArgs a) {
   if (a.flag && *a.flag) return;
   constexpr int HALF = HD / 2;
-  constexpr int NS = (HD + 63) / 64;
-  __shared__ float cs[HALF], sn[HALF];
+  constexpr int NS = HD / 64;
   const int r = blockIdx.x;
   const int tloc = r % a.per_batch, bidx = r / a.per_batch;
-  const double pos = (double)(a.pos0 + tloc);
-  for (int j = threadIdx.x; j < HALF; j += blockDim.x) {
-    const double freq = exp(-(2.0 * (double)j / (double)HD) * log((double)a.theta));
-    double sv, cv;
-    sincos(pos * freq, &sv, &cv);
-    cs[j] = (float)cv;
-    sn[j] = (float)sv;
-  }
-  __syncthreads();
+  const float2* tab = a.rope + (long)tloc * HALF;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int qkvd = (a.H + 2 * a.Hkv) * HD;
   const bf16_t* src = a.qkv + (long)r * qkvd;
-  const int nh = a.H + 2 * a.Hkv;
-  for (int hh = wave; hh < nh; hh += 4) {
+  for (int hh = wave; hh < a.H + a.Hkv; hh += 4) {
     const bf16_t* xs = src + hh * HD;
-    if (hh >= a.H + a.Hkv) {  // value head: scatter into V^T
-      const int g = hh - a.H - a.Hkv;
-      bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (a.t_offset + tloc);
-      for (int e = lane; e < HD; e += 64) vt[(long)e * a.v_pitch] = xs[e];
-      continue;
-    }
     const bool isq = hh < a.H;
     const bf16_t* nw = isq ? a.qnorm : a.knorm;
     float x[NS];
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const int e = lane + 64 * j;
-      x[j] = (e < HD) ? bf2f(xs[e]) : 0.f;
+      x[j] = bf2f(xs[lane + 64 * j]);
       ss += x[j] * x[j];
     }
     ss = wave_sum(ss);
     const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int e = lane + 64 * j;
-      x[j] = (e < HD) ? x[j] * inv * bf2f(nw[e]) : 0.f;
-    }
+    for (int j = 0; j < NS; ++j) x[j] = x[j] * inv * bf2f(nw[lane + 64 * j]);
     float y[NS];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const int e = lane + 64 * j;
-      float partner;
-      if (HD >= 128) {
-        partner = x[(j + HALF / 64) % NS];
-      } else {
-        partner = __shfl_xor(x[j], HALF, 64);
-      }
-      if (e < HALF) {
-        y[j] = x[j] * cs[e] - partner * sn[e];
-      } else {
-        const int jj = e - HALF;
-        y[j] = x[j] * cs[jj < HALF ? jj : 0] + partner * sn[jj < HALF ? jj : 0];
-      }
+      const float partner = (HD >= 128) ? x[(j + HALF / 64) % NS] : __shfl_xor(x[j], HALF, 64);
+      const float2 cs = tab[e < HALF ? e : e - HALF];
+      y[j] = (e < HALF) ? x[j] * cs.x - partner * cs.y : x[j] * cs.x + partner * cs.y;
     }
+    bf16_t* dst;
     if (isq) {
-      bf16_t* qd = a.q + ((long)r * a.H + hh) * HD;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const int e = lane + 64 * j;
-        if (e < HD) qd[e] = f2bf(y[j]);
-      }
+      dst = a.q + ((long)r * a.H + hh) * HD;
     } else {
-      const int g = hh - a.H;
-      bf16_t* kd = a.kdst + bidx * a.k_bstride + g * a.k_hstride + (long)(a.t_offset + tloc) * HD;
+      dst = a.kdst + bidx * a.k_bstride + (hh - a.H) * a.k_hstride + (long)(a.t_offset + tloc) * HD;
+    }
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const int e = lane + 64 * j;
-        if (e < HD) kd[e] = f2bf(y[j]);
-      }
+    for (int j = 0; j < NS; ++j) dst[lane + 64 * j] = f2bf(y[j]);
+  }
+}
+
+// V^T scatter: a workgroup moves 32 tokens x hd values of one kv head through
+// LDS so that every row of V^T (one dimension, 32 consecutive positions) is
+// written as one contiguous 64-byte run.
+template <int HD>
+__global__ __launch_bounds__(256) void vt_scatter_kernel(QkRopeArgs a) {
+  if (a.flag && *a.flag) return;
+  __shared__ bf16_t tile[32][HD + 2];
+  const int g = blockIdx.y;
+  const int t0 = blockIdx.x * 32;               // first row of the tile (rows of one batch element)
+  const int qkvd = (a.H + 2 * a.Hkv) * HD;
+  for (int i = threadIdx.x; i < 32 * HD; i += 256) {
+    const int tr = i / HD, e = i % HD;
+    const int r = min(t0 + tr, a.rows - 1);
+    tile[tr][e] = a.qkv[(long)r * qkvd + (a.H + a.Hkv + g) * HD + e];
+  }
+  __syncthreads();
+  const int bidx = t0 / a.per_batch, tloc0 = t0 % a.per_batch;
+  bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (a.t_offset + tloc0);
+  const int nval = min(32, a.rows - t0);
+  for (int i = threadIdx.x; i < HD * 16; i += 256) {     // HD rows x 16 pairs of positions
+    const int e = i >> 4, p = (i & 15) * 2;
+    if (p + 1 < nval) {
+      const uint32_t w = (uint32_t)tile[p][e] | ((uint32_t)tile[p + 1][e] << 16);
+      *reinterpret_cast<uint32_t*>(vt + (long)e * a.v_pitch + p) = w;
+    } else if (p < nval) {
+      vt[(long)e * a.v_pitch + p] = tile[p][e];
     }
   }
 }
 
 hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
+  if (a.per_batch % 32 != 0 && a.per_batch != a.rows) return hipErrorInvalidValue;
+  dim3 vg((a.rows + 31) / 32, a.Hkv);
   switch (a.hd) {
-    case 64: hipLaunchKernelGGL(qk_rope_kernel<64>, dim3(a.rows), dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(qk_rope_kernel<128>, dim3(a.rows), dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(qk_rope_kernel<256>, dim3(a.rows), dim3(256), 0, s, a); break;
+    case 64:
+      hipLaunchKernelGGL(qk_rope_kernel<64>, dim3(a.rows), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(vt_scatter_kernel<64>, vg, dim3(256), 0, s, a);
+      break;
+    case 128:
+      hipLaunchKernelGGL(qk_rope_kernel<128>, dim3(a.rows), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(vt_scatter_kernel<128>, vg, dim3(256), 0, s, a);
+      break;
+    case 256:
+      hipLaunchKernelGGL(qk_rope_kernel<256>, dim3(a.rows), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(vt_scatter_kernel<256>, vg, dim3(256), 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -177,69 +261,100 @@ hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Merge of key-split attention partials (scores kept in log2 units): per row,
 // the split weights 2^(m_s - M) / L of every head are formed once in LDS, then
-// the outputs are summed with coalesced reads of the partials.
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const float* ml, int splits, int rows,
-                                                         int H, int hd, bf16_t* out, const int32_t* flag) {
+// each thread sums its float4 columns over the splits.
+template <int NSP>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const float* ml, int rows, int H, int hd,
+                                                         bf16_t* out, const int32_t* flag) {
   if (flag && *flag) return;
-  __shared__ float wts[1024];
+  __shared__ float wts[64 * NSP];
   const int r = blockIdx.x;
   const long srow = (long)rows * H;
   for (int h = threadIdx.x; h < H; h += blockDim.x) {
     const long base = (long)r * H + h;
+    float mv[NSP], lv[NSP];
     float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[(s * srow + base) * 2]);
+#pragma unroll
+    for (int s = 0; s < NSP; ++s) {
+      mv[s] = ml[(s * srow + base) * 2];
+      lv[s] = ml[(s * srow + base) * 2 + 1];
+      M = fmaxf(M, mv[s]);
+    }
     float L = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float m = ml[(s * srow + base) * 2];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      wts[h * splits + s] = w;
-      L += w * ml[(s * srow + base) * 2 + 1];
+#pragma unroll
+    for (int s = 0; s < NSP; ++s) {
+      mv[s] = (mv[s] == -INFINITY) ? 0.f : exp2f(mv[s] - M);
+      L += mv[s] * lv[s];
     }
     const float il = L > 0.f ? 1.0f / L : 0.f;
-    for (int s = 0; s < splits; ++s) wts[h * splits + s] *= il;
+#pragma unroll
+    for (int s = 0; s < NSP; ++s) wts[h * NSP + s] = mv[s] * il;
   }
   __syncthreads();
   const long rowoff = (long)r * H * hd;
   const long sstride = srow * hd;
-  for (int idx = threadIdx.x; idx < H * hd; idx += blockDim.x) {
-    const int h = idx / hd;
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) acc += wts[h * splits + s] * op[s * sstride + rowoff + idx];
-    out[rowoff + idx] = f2bf(acc);
+  const int n4 = H * hd / 4;
+  for (int i4 = threadIdx.x; i4 < n4; i4 += blockDim.x) {
+    const int h = (4 * i4) / hd;
+    float4 vals[NSP];
+#pragma unroll
+    for (int s = 0; s < NSP; ++s) vals[s] = reinterpret_cast<const float4*>(op + s * sstride + rowoff)[i4];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int s = 0; s < NSP; ++s) acc = f4fma(wts[h * NSP + s], vals[s], acc);
+    store_bf16x4(out + rowoff + 4 * i4, acc);
   }
 }
 
 hipError_t attention_merge(const float* opart, const float* mlpart, int splits, int rows, int H, int hd,
                            bf16_t* out, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (H * splits > 1024) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(rows), dim3(256), 0, s, opart, mlpart, splits, rows, H, hd, out, flag);
+  if (H > 64 || hd % 4) return hipErrorInvalidValue;
+#define DG_MERGE_CASE(N)                                                                               \
+  case N:                                                                                              \
+    hipLaunchKernelGGL(attn_merge_kernel<N>, dim3(rows), dim3(256), 0, s, opart, mlpart, rows, H, hd, out, flag); \
+    break;
+  switch (splits) {
+    DG_MERGE_CASE(1) DG_MERGE_CASE(2) DG_MERGE_CASE(3) DG_MERGE_CASE(4) DG_MERGE_CASE(5) DG_MERGE_CASE(6)
+    DG_MERGE_CASE(7) DG_MERGE_CASE(8) DG_MERGE_CASE(9) DG_MERGE_CASE(10) DG_MERGE_CASE(11) DG_MERGE_CASE(12)
+    DG_MERGE_CASE(13) DG_MERGE_CASE(14) DG_MERGE_CASE(15) DG_MERGE_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef DG_MERGE_CASE
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Router: logits = hi-part + lo-part products (an fp32-accurate product from two
-// bf16 MFMA passes), top-k by repeated wavefront argmax (ties -> lower expert),
-// gates = softmax over the k selected logits.  One wave per token row.
-__global__ __launch_bounds__(256) void topk_kernel(Partials rl, int rows, int E, int k, int32_t* idx,
-                                                   float* gate, int32_t* idx_dump, float* gate_dump,
-                                                   const int32_t* flag) {
+// bf16 MFMA passes) summed over split-K partials, top-k by repeated wavefront
+// argmax (ties -> lower expert), gates = softmax over the k selected logits.
+// One wave per token row.
+template <int NS>
+__global__ __launch_bounds__(256) void topk_kernel(Partials rl, int rows, int E, int k, int32_t* idx, float* gate,
+                                                   int32_t* idx_dump, float* gate_dump, const int32_t* flag) {
   if (flag && *flag) return;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   float v[4];
+  float hv[4][NS], lv[4][NS];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    float hi = 0.f, lo = 0.f;
-    if (e < E) {
-      for (int s = 0; s < rl.n; ++s) {
-        hi += rl.p[s * rl.stride + (long)r * E + e];
-        lo += rl.p[s * rl.stride + (long)(rows + r) * E + e];
-      }
+    const int e = min(lane + 64 * j, E - 1);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      hv[j][s] = rl.p[s * rl.stride + (long)r * E + e];
+      lv[j][s] = rl.p[s * rl.stride + (long)(rows + r) * E + e];
     }
-    v[j] = (e < E) ? hi + lo : -INFINITY;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float hi = 0.f, lo = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      hi += hv[j][s];
+      lo += lv[j][s];
+    }
+    v[j] = (lane + 64 * j < E) ? hi + lo : -INFINITY;
   }
   float selv[16];
   int seli[16];
@@ -289,8 +404,17 @@ hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, floa
                        float* gate_dump, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (E > 256 || k > 16 || k > E) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(topk_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, rlog, rows, E, k, idx, gate, idx_dump,
-                     gate_dump, flag);
+#define DG_TOPK_CASE(N)                                                                                  \
+  case N:                                                                                                \
+    hipLaunchKernelGGL(topk_kernel<N>, dim3((rows + 3) / 4), dim3(256), 0, s, rlog, rows, E, k, idx, gate,  \
+                       idx_dump, gate_dump, flag);                                                       \
+    break;
+  switch (rlog.n) {
+    DG_TOPK_CASE(1) DG_TOPK_CASE(2) DG_TOPK_CASE(3) DG_TOPK_CASE(4)
+    DG_TOPK_CASE(5) DG_TOPK_CASE(6) DG_TOPK_CASE(7) DG_TOPK_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef DG_TOPK_CASE
   return hipGetLastError();
 }
 
@@ -382,50 +506,92 @@ hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* coun
 }
 
 // ---------------------------------------------------------------------------
+// h[r] += sum_s ys_s[r] + sum_j gate[r,j] * Y[slot[r,j]], then the next RMSNorm.
+template <int NS, int NK>
 __global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, const float* Y,
-                                                      const int32_t* slot_of, const float* gate, int d, int k,
+                                                      const int32_t* slot_of, const float* gate, int d,
                                                       const bf16_t* nw, float eps, bf16_t* xn, float* dump,
                                                       const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ float red[16];
-  __shared__ int slots[16];
-  __shared__ float gts[16];
   const int r = blockIdx.x;
-  if (threadIdx.x < k) {
-    slots[threadIdx.x] = slot_of[(long)r * k + threadIdx.x];
-    gts[threadIdx.x] = gate[(long)r * k + threadIdx.x];
+  const int d4 = d >> 2;
+  int sl[NK];
+  float gt[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    sl[j] = slot_of[(long)r * NK + j];
+    gt[j] = gate[(long)r * NK + j];
   }
-  __syncthreads();
-  float v[DG_MAXD_PER_THREAD];
+  float4* x4 = reinterpret_cast<float4*>(h + (long)r * d);
+  float4 v[DG_MAXC4];
   float ss = 0.f;
-  int n = 0;
-  for (int c = threadIdx.x; c < d; c += 256, ++n) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += gts[j] * Y[(long)slots[j] * d + c];
-    for (int s = 0; s < ys.n; ++s) acc += ys.p[s * ys.stride + (long)r * d + c];
-    const float x = h[(long)r * d + c] + acc;
-    h[(long)r * d + c] = x;
-    v[n] = x;
-    ss += x * x;
+#pragma unroll
+  for (int c = 0; c < DG_MAXC4; ++c) {
+    const int c4 = threadIdx.x + 256 * c;
+    if (c4 < d4) {
+      float4 yv[NK], pv[NS > 0 ? NS : 1];
+#pragma unroll
+      for (int j = 0; j < NK; ++j) yv[j] = reinterpret_cast<const float4*>(Y + (long)sl[j] * d)[c4];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) pv[s] = reinterpret_cast<const float4*>(ys.p + s * ys.stride + (long)r * d)[c4];
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < NK; ++j) acc = f4fma(gt[j], yv[j], acc);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) acc = f4add(acc, pv[s]);
+      v[c] = f4add(x4[c4], acc);
+      x4[c4] = v[c];
+      ss += f4dot(v[c]);
+    }
   }
   if (!nw && !dump) return;
   ss = block_sum(ss, red);
   const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  n = 0;
-  for (int c = threadIdx.x; c < d; c += 256, ++n) {
-    if (nw) xn[(long)r * d + c] = f2bf(v[n] * inv * bf2f(nw[c]));
-    if (dump) dump[(long)r * d + c] = v[n];
+#pragma unroll
+  for (int c = 0; c < DG_MAXC4; ++c) {
+    const int c4 = threadIdx.x + 256 * c;
+    if (c4 < d4) {
+      if (nw) {
+        const float4 wv = load_bf16x4(nw + 4 * c4);
+        store_bf16x4(xn + (long)r * d + 4 * c4, make_float4(v[c].x * inv * wv.x, v[c].y * inv * wv.y,
+                                                            v[c].z * inv * wv.z, v[c].w * inv * wv.w));
+      }
+      if (dump) reinterpret_cast<float4*>(dump + (long)r * d)[c4] = v[c];
+    }
   }
+}
+
+template <int NK>
+static hipError_t combine_k(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate,
+                            int rows, int d, const bf16_t* nw, float eps, bf16_t* xn, float* dump,
+                            const int32_t* flag, hipStream_t s) {
+#define DG_COMB_CASE(N)                                                                                   \
+  case N:                                                                                                 \
+    hipLaunchKernelGGL((combine_kernel<N, NK>), dim3(rows), dim3(256), 0, s, h, ys, Y, slot_of, gate, d, nw, eps, \
+                       xn, dump, flag);                                                                   \
+    break;
+  switch (ys.n) {
+    DG_COMB_CASE(0) DG_COMB_CASE(1) DG_COMB_CASE(2) DG_COMB_CASE(3) DG_COMB_CASE(4)
+    DG_COMB_CASE(5) DG_COMB_CASE(6) DG_COMB_CASE(7) DG_COMB_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef DG_COMB_CASE
+  return hipGetLastError();
 }
 
 hipError_t moe_combine(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate, int rows,
                        int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump, const int32_t* flag,
                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (d > 256 * DG_MAXD_PER_THREAD || k > 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(combine_kernel, dim3(rows), dim3(256), 0, s, h, ys, Y, slot_of, gate, d, k, next_w, eps, xn,
-                     dump, flag);
-  return hipGetLastError();
+  if (d > 1024 * DG_MAXC4 || d % 4) return hipErrorInvalidValue;
+  switch (k) {
+    case 1: return combine_k<1>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
+    case 2: return combine_k<2>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
+    case 4: return combine_k<4>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
+    case 8: return combine_k<8>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // ---------------------------------------------------------------------------

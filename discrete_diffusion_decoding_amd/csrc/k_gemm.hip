@@ -29,6 +29,18 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kStageElems = 2 * 64 * 64;  // A tile then B tile, 64 rows x 64 bf16 each
 
+// Workgroups are dealt to the 8 XCDs in turn (block b runs on XCD b mod 8).
+// The grid is padded to a multiple of 8 and renumbered so that every XCD works
+// through one contiguous range of logical tiles: the row chunks that share a
+// weight tile then run side by side on one XCD and share its L2.
+__device__ inline long xcd_logical_block(long total) {
+  const long per = gridDim.x >> 3;
+  const long b = blockIdx.x;
+  const long l = (b & 7) * per + (b >> 3);
+  return l < total ? l : -1;
+}
+static inline unsigned xcd_grid(long total) { return (unsigned)((total + 7) & ~7L); }
+
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) bf16_t S0[kStageElems];
@@ -41,7 +53,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   constexpr bool GEGLU = EPI == EPI_GEGLU_BF16;
   constexpr int NCOL = GEGLU ? 32 : 64;   // output columns per tile
   const int ntiles = (g.N + NCOL - 1) / NCOL;
-  const long bidx = blockIdx.x;
+  const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
+  if (bidx < 0) return;
   const int item = (int)(bidx % g.items_max);
   const long rest = bidx / g.items_max;
   const int tile = (int)(rest % ntiles);
@@ -110,32 +123,36 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-#define DG_COMPUTE(S)                                                                            \
-  do {                                                                                           \
-    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                              \
-      const int p_ = 4 * j + lg;                                                                 \
-      const bf16x8 bf = *reinterpret_cast<const bf16x8*>(&S[64 * 64 + brow * 64 + ((p_ ^ (brow & 7)) << 3)]); \
-      bf16x8 af[4];                                                                              \
-      _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                            \
-        const int arow = 16 * m + lr;                                                            \
-        af[m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);      \
-      }                                                                                          \
-      _Pragma("unroll") for (int m = 0; m < 4; ++m) acc[m] = mfma16x16x32(af[m], bf, acc[m]);    \
+#define DG_READ(S)                                                                               \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
+    const int p_ = 4 * j + lg;                                                                   \
+    bf[j] = *reinterpret_cast<const bf16x8*>(&S[64 * 64 + brow * 64 + ((p_ ^ (brow & 7)) << 3)]); \
+    _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                              \
+      const int arow = 16 * m + lr;                                                              \
+      af[j][m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);     \
     }                                                                                            \
-  } while (0)
+  }
+#define DG_MMA()                                                                                 \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
+    _Pragma("unroll") for (int m = 0; m < 4; ++m) acc[m] = mfma16x16x32(af[j][m], bf[j], acc[m]);
 
   // Every stage issues its loads unconditionally (stage index clamped to the
   // last one: the surplus loads land in a buffer that is not read again), so
   // exactly two younger stages (8 loads per lane) are pending when a stage is
-  // read and one constant wait suffices.
+  // read and one constant wait suffices.  The stage's LDS reads precede the
+  // next DMA issue (sched_barrier), so the compiler adds no wait of its own.
 #define DG_ITER(SI, CUR, NXT)                                                                    \
   do {                                                                                           \
     const int s_ = (SI);                                                                         \
     __builtin_amdgcn_s_waitcnt((8 & 0xF) | (0x7 << 4) | (0xF << 8));                             \
     __builtin_amdgcn_s_barrier();                                                                \
+    DG_READ(CUR);                                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
     DG_ISSUE(NXT, min(s_ + 3, nst - 1));                                                         \
-    DG_COMPUTE(CUR);                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    DG_MMA();                                                                                    \
   } while (0)
+  bf16x8 af[2][4], bf[2];
 
   if (nst > 0) {
     DG_ISSUE(S0, 0);
@@ -153,7 +170,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     if (s + 2 < nst) DG_ITER(s + 2, S2, S1);
   }
 #undef DG_ISSUE
-#undef DG_COMPUTE
+#undef DG_READ
+#undef DG_MMA
 #undef DG_ITER
 
   // ---- epilogue ------------------------------------------------------------------
@@ -204,7 +222,7 @@ static hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int ntiles = (a.N + NCOL - 1) / NCOL;
   const long total = (long)a.items_max * ntiles * a.k_split;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3((unsigned)total), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3(xcd_grid(total)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -219,6 +237,161 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s) {
     case EPI_GEGLU_BF16: return launch<EPI_GEGLU_BF16>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Wide variant for products whose activation side is large (the 256-row dense
+// projections, the LM head and the soft-prediction embedding): a workgroup of
+// 8 waves owns 256 activation rows x 128 weight rows, so every weight byte is
+// streamed once per 256 rows.  Stages of 64 columns (A 32 KB + B 16 KB) go
+// through a 3-deep LDS ring (144 KB: one workgroup per CU, two stages in
+// flight).  Wave w multiplies weight rows 64*(w&1) .. +63 by activation rows
+// 64*(w>>1) .. +63 (4 x 4 MFMA tiles).  Only plain stores: split-K slices are
+// written as partial tiles and summed by the consumer.
+constexpr int kFatA = 256 * 64, kFatStage = (256 + 128) * 64;
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[kFatStage];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[kFatStage];
+  __shared__ __attribute__((aligned(1024))) bf16_t S2[kFatStage];
+  if (g.flag && *g.flag) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntiles = (g.N + 127) / 128;
+  const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
+  if (bidx < 0) return;
+  const int item = (int)(bidx % g.items_max);
+  const long rest = bidx / g.items_max;
+  const int tile = (int)(rest % ntiles);
+  const int zk = (int)(rest / ntiles);
+  const int r0 = item * 256;
+  const int nrows = min(256, g.M - r0);
+  if (nrows <= 0) return;
+  const int n_base = tile * 128;
+  const int kb = zk * g.k_chunk;
+  const int ke = min(g.K, kb + g.k_chunk);
+  const int nst = (ke - kb) >> 6;
+  if (nst <= 0) return;
+
+  // DMA: wave w moves A row groups 4w..4w+3 and B row groups 2w, 2w+1 (8 rows
+  // each).  Addresses = wave-uniform base (advanced per stage, kept in SGPRs)
+  // + per-lane 32-bit byte offsets fixed for the whole loop.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int part = lslot ^ lrow;
+  int aoff[4], boff[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * wave + j) * 8 + lrow;   // 0..255
+    aoff[j] = (int)(((long)min(row, nrows - 1) * g.lda + part * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 8 + lrow;   // 0..127
+    boff[j] = (int)(((long)(min(n_base + row, g.N - 1) - n_base) * g.ldw + part * 8) * 2);
+  }
+  const char* abase = reinterpret_cast<const char*>(g.A + (long)r0 * g.lda + kb);
+  const char* bbase = reinterpret_cast<const char*>(g.W + (long)n_base * g.ldw + kb);
+  const int dst_a = (4 * wave) * 512, dst_b = kFatA + (2 * wave) * 512;
+#define DG_FISSUE(S, ST)                                                                                   \
+  do {                                                                                                     \
+    const char* ab_ = abase + ((long)(ST) << 7);                                                           \
+    const char* bb_ = bbase + ((long)(ST) << 7);                                                           \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
+      __builtin_amdgcn_global_load_lds((const void*)(ab_ + aoff[j]), (lds_void_t*)&S[dst_a + 512 * j], 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                          \
+      __builtin_amdgcn_global_load_lds((const void*)(bb_ + boff[j]), (lds_void_t*)&S[dst_b + 512 * j], 16, 0, 0); \
+  } while (0)
+
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  // B-operand row offsets computed once: derived inside the read macro, the
+  // compiler lost track of which LDS array one of the reads targets and made
+  // it wait for every DMA in flight.
+  int boffr[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) boffr[n] = (64 * wn + 16 * n + lr) * 64;
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // Operand reads of the current stage are all issued before the next stage's
+  // DMA (sched_barrier keeps that order): an LDS read after a DMA that the
+  // compiler cannot prove disjoint would make it wait for every DMA in flight.
+#define DG_FREAD(S)                                                                                        \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                          \
+    const int p_ = 4 * j + lg;                                                                             \
+    _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                                        \
+      const int arow = 64 * wm + 16 * m + lr;                                                              \
+      af[j][m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);               \
+    }                                                                                                      \
+    _Pragma("unroll") for (int n = 0; n < 4; ++n) {                                                        \
+      bfr[j][n] = *reinterpret_cast<const bf16x8*>(&S[kFatA + boffr[n] + ((p_ ^ (lr & 7)) << 3)]);         \
+    }                                                                                                      \
+  }
+#define DG_FMMA()                                                                                          \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                            \
+    _Pragma("unroll") for (int m = 0; m < 4; ++m)                                                          \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[j][m], bfr[j][n], acc[m][n]);
+  // two stages in flight: when stage s is read, only stage s+1 (6 loads per lane) may be pending
+#define DG_FITER(SI, CUR, NXT)                                                                             \
+  do {                                                                                                     \
+    const int s_ = (SI);                                                                                   \
+    __builtin_amdgcn_s_waitcnt((6 & 0xF) | (0x7 << 4) | (0xF << 8));                                       \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    DG_FREAD(CUR);                                                                                         \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+    DG_FISSUE(NXT, min(s_ + 2, nst - 1));                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+    DG_FMMA();                                                                                             \
+  } while (0)
+  bf16x8 af[2][4], bfr[2][4];
+
+  DG_FISSUE(S0, 0);
+  DG_FISSUE(S1, min(1, nst - 1));
+  int s = 0;
+  for (; s + 3 <= nst; s += 3) {
+    DG_FITER(s, S0, S2);
+    DG_FITER(s + 1, S1, S0);
+    DG_FITER(s + 2, S2, S1);
+  }
+  if (s < nst) DG_FITER(s, S0, S2);
+  if (s + 1 < nst) DG_FITER(s + 1, S1, S0);
+#undef DG_FISSUE
+#undef DG_FREAD
+#undef DG_FMMA
+#undef DG_FITER
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = n_base + 64 * wn + 16 * n + lr;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 64 * wm + 16 * m + 4 * lg + i;
+        if (rl >= nrows) continue;
+        const long off = (long)(r0 + rl) * g.ldc + col;
+        if (EPI == EPI_STORE_BF16) reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(acc[m][n][i]);
+        else reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = acc[m][n][i];
+      }
+    }
+  }
+}
+
+hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
+  if (a.lda % 8 != 0 || a.ldw % 8 != 0 || a.items || a.a_rows) return hipErrorInvalidValue;
+  const long total = (long)a.items_max * ((a.N + 127) / 128) * a.k_split;
+  if (total <= 0) return hipSuccess;
+  switch (epi) {
+    case EPI_STORE_F32: hipLaunchKernelGGL(gemm_fat_kernel<EPI_STORE_F32>, dim3(xcd_grid(total)), dim3(512), 0, s, a); break;
+    case EPI_STORE_BF16: hipLaunchKernelGGL(gemm_fat_kernel<EPI_STORE_BF16>, dim3(xcd_grid(total)), dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dg

@@ -30,7 +30,7 @@
  *   - Restrictions of this implementation: head_dim in {64, 128, 256};
  *     n_heads / n_kv_heads in {1, 2, 4}; d_model, d_expert, d_shared and
  *     n_heads*head_dim multiples of 64 and d_model <= 4096; n_experts <= 255;
- *     top_k <= 16; canvas length T a multiple of 32 and <= 1024; prefix
+ *     top_k in {1, 2, 4, 8}; canvas length T a multiple of 32 and <= 1024; prefix
  *     lengths P and capacities P_max multiples of 32; batch B <= 16; vocab a
  *     multiple of 128.
  */
