@@ -144,6 +144,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one elementwise copy of 256 MiB fp32 first (reads and writes 256 MiB each): "
+                         "the reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for {args.gpus})",
@@ -164,6 +167,12 @@ def main():
     B, T, P, Bp = wl.batch, wl.canvas_len, wl.prefix_len, wl.prefix_batch
     torch.cuda.set_device(0)
     dg.lib()
+    if args.copy_calibration:
+        xs = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        ys = torch.empty_like(xs)
+        torch.mul(xs, 1.0, out=ys)
+        torch.cuda.synchronize()
+        del xs, ys
     t0 = time.perf_counter()
     log(f"generating and uploading the {m.param_counts()['total'] / 1e9:.2f}B-parameter model")
     dm = DeviceModel(m, args.seed)
@@ -256,7 +265,7 @@ def main():
         kh = kernel_hash()
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(kh),
-                "kernel": "grouped expert gate/up GEMM (gemm_kernel<GEGLU>)",
+                "kernel": "grouped expert gate/up GEMM (dg::gemm_kernel<4, true>)",
                 "bytes_per_launch": int(bytes_l), "avg_launch_ms": round(per_launch_ms, 4),
                 "kernel_source_sha256_16": kh}
 

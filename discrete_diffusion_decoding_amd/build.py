@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     # packed fp32 instructions stay off (hipcc would otherwise form them itself)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # a variable read before it is set (e.g. a macro-local shadowing its
+    # argument) is an error, not a warning
+    "-Wall", "-Werror=uninitialized", "-Werror=sometimes-uninitialized",
 ]
 
 

@@ -18,6 +18,18 @@ typedef uint16_t bf16_t;
 
 #define DG_WAVE 64
 
+// Workgroups are dealt to the 8 XCDs in turn (block b runs on XCD b mod 8).
+// The grid is padded to a multiple of 8 and renumbered so that every XCD works
+// through one contiguous range of logical tiles: workgroups that read the same
+// operand tiles then run side by side on one XCD and share its L2.
+__device__ inline long xcd_logical_block(long total) {
+  const long b = blockIdx.x;
+  const long per = gridDim.x >> 3;
+  const long l = (b & 7) * per + (b >> 3);
+  return l < total ? l : -1;
+}
+static inline unsigned xcd_grid(long total) { return (unsigned)((total + 7) & ~7L); }
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
 // round to nearest even (finite inputs)

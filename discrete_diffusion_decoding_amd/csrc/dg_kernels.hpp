@@ -7,7 +7,7 @@
 
 namespace dg {
 
-enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_ADD_F32 = 2, EPI_ADD_GATED_F32 = 3, EPI_GEGLU_BF16 = 4 };
+enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GEGLU_BF16 = 4 };
 
 // C[r, n] (op)= sum_k A[row(r), k] * W_g[n, k] over row chunks ("items").
 // A: bf16 rows of pitch lda; row(r) = a_rows ? a_rows[r] : r.
@@ -32,10 +32,11 @@ struct GemmArgs {
   int items_max;
   int M;
   int k_split;
+  int tile_rows;   // 64-row kernel: activation rows per tile (64; also the work-list chunk size)
+  int ring;        // and its LDS ring depth (4 | 5)
   void* C;
   long ldc;
   long c_kstride;
-  const bf16_t* col_gate;
   const int32_t* flag;
 };
 
@@ -44,6 +45,10 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
 // ceil(M / 256)); epilogues EPI_STORE_F32 (split-K partials) and EPI_STORE_BF16
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s);
 constexpr int kFatRowChunk = 256;
+// the 256-row kernel addresses a tile with 32-bit byte offsets from its first row
+inline bool gemm_fat_pitch_ok(long lda, long ldw) {
+  return (long)kFatRowChunk * lda * 2 < 0x7FFFFFFFL && 128L * ldw * 2 < 0x7FFFFFFFL;
+}
 constexpr int kGemmRowChunk = 64;
 
 // ---- elementwise / reduction kernels (k_elem.hip) ----

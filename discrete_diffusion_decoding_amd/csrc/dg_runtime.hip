@@ -58,6 +58,8 @@ struct dg_model {
   dg_layer_layout lay;
   mutable Prof prof;
   bool use_graphs = true;
+  // 64-row GEMM kernel variants: grouped expert products (tile rows, ring) and dense (ring)
+  int x_rows = 64, x_ring = 5, d_ring = 4;
   std::vector<GraphEntry> graphs;
   unsigned long long use_clock = 0;
 };
@@ -216,12 +218,35 @@ static int choose_ksplit(long tiles_times_items, int K, int max_split, int* k_ch
   return cdiv(K, kc);
 }
 
+// Products with at least this many rows run on the 256-row tile kernel: every
+// weight byte then enters one workgroup only, where the 64-row kernel fetches
+// it once per 64-row chunk.
+static const int kFatMinRows = 192;
+static bool fat_rows(int rows) { return rows >= kFatMinRows; }
+
+// Soft-embedding product (K = vocab): split so that ~256 (256-row tiles, one
+// per CU) or ~1024 (64-row tiles) workgroups share the contraction.
 static void soft_split(const dg_model_desc& d, int rows, int* ksplit, int* kchunk) {
-  const int items = cdiv(d.d_model, 128) * cdiv(rows, 64);
-  int ks = std::max(1, std::min(32, cdiv(1024, items)));
+  const bool fat = fat_rows(rows);
+  const int items = fat ? cdiv(d.d_model, 128) * cdiv(rows, kFatRowChunk) : cdiv(d.d_model, 64) * cdiv(rows, 64);
+  int ks = std::max(1, std::min(32, cdiv(fat ? 352 : 1024, items)));
   int kc = cdiv(cdiv(d.vocab, ks), 64) * 64;
   *kchunk = kc;
   *ksplit = cdiv(d.vocab, kc);
+}
+
+// Dense product C = A W^T over rows [0, M) on the kernel suited to M.
+static hipError_t dense_gemm(int epi, GemmArgs g, int M, hipStream_t st) {
+  g.M = M;
+  g.items = nullptr;
+  g.n_items = nullptr;
+  if (fat_rows(M) && (epi == EPI_STORE_F32 || epi == EPI_STORE_BF16) && !g.a_rows &&
+      gemm_fat_pitch_ok(g.lda, g.ldw)) {
+    g.items_max = cdiv(M, kFatRowChunk);
+    return gemm_fat(epi, g, st);
+  }
+  g.items_max = cdiv(M, kGemmRowChunk);
+  return gemm(epi, g, st);
 }
 
 static int vsplit_of(int rows, int V) {
@@ -260,7 +285,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.off = take((E + 1) * 4);
   p.slot_of = take(R * k * 4);
   p.slot_row = take(R * k * 4);
-  p.items = take((E + (R * k + kGemmRowChunk - 1) / kGemmRowChunk) * 16);
+  p.items = take((E + (R * k + 31) / 32) * 16);   // work list for chunks of >= 32 rows
   p.nitems = take(16);
   p.hbuf = take(R * k * d.d_expert * 2);
   p.ybuf = take(R * k * D * 4);
@@ -313,6 +338,8 @@ static GemmArgs gargs() {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.k_split = 1;
+  g.tile_rows = 64;
+  g.ring = 4;
   return g;
 }
 
@@ -348,7 +375,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   int32_t* slot_row = at<int32_t>(ws, p.slot_row);
   int4* items = at<int4>(ws, p.items);
   int32_t* nitems = at<int32_t>(ws, p.nitems);
-  const int items_max = E + cdiv((long)R * k, kGemmRowChunk);
+  const int items_max = E + cdiv((long)R * k, m->x_rows);
   bf16_t* hbuf = at<bf16_t>(ws, p.hbuf);
   float* ybuf = at<float>(ws, p.ybuf);
   bf16_t* hs = at<bf16_t>(ws, p.hs);
@@ -374,6 +401,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     // QKV
     {
       GemmArgs g = gargs();
+      g.ring = m->d_ring;
       g.A = xn; g.lda = D; g.W = lw(m, l, m->lay.w_qkv); g.ldw = D; g.K = D; g.N = qkvd; g.k_chunk = D;
       dense_rows(g, R); g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_DENSE, st);
@@ -433,6 +461,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     Partials opp{at<float>(ws, p.dpart), 1, (long)R * D};
     {
       GemmArgs g = gargs();
+      g.ring = m->d_ring;
       g.A = o; g.lda = H * hd; g.W = lw(m, l, m->lay.w_o); g.ldw = H * hd; g.K = H * hd; g.N = D;
       dense_rows(g, R);
       g.k_split = choose_ksplit((long)g.items_max * cdiv(D, 64), H * hd, kMaxDenseSplit, &g.k_chunk);
@@ -450,6 +479,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     Partials rlp{rlog, 1, (long)2 * R * E};
     {
       GemmArgs g = gargs();
+      g.ring = m->d_ring;
       g.A = xr; g.lda = D; g.W = lw(m, l, m->lay.w_router); g.ldw = D; g.K = D; g.N = E;
       dense_rows(g, 2 * R);
       g.k_split = choose_ksplit((long)g.items_max * cdiv(E, 64), D, kMaxRouterSplit, &g.k_chunk);
@@ -462,14 +492,14 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       ProfScope psr_(m, DG_PROF_ROUTER, st);
       DG_CK(router_topk(rlp, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
                         ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
-      DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, kGemmRowChunk, ps.flag, st));
+      DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
     }
     // experts: gate/up (GEGLU) then down, grouped by expert over the permuted slots
     {
       GemmArgs g = gargs();
       g.A = xn2; g.lda = D; g.a_rows = slot_row; g.W = lw(m, l, m->lay.w_gate); g.W2 = lw(m, l, m->lay.w_up);
       g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D;
-      g.items = items; g.n_items = nitems; g.items_max = items_max;
+      g.items = items; g.n_items = nitems; g.items_max = items_max; g.tile_rows = m->x_rows; g.ring = m->x_ring;
       g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_GATEUP, st);
       DG_CK(gemm(EPI_GEGLU_BF16, g, st));
@@ -478,6 +508,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g = gargs();
       g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
       g.N = D; g.k_chunk = fe; g.items = items; g.n_items = nitems; g.items_max = items_max;
+      g.tile_rows = m->x_rows; g.ring = m->x_ring;
       g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_F32, g, st));
@@ -486,10 +517,12 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     if (fs) {
       ProfScope ps_(m, DG_PROF_SHARED, st);
       GemmArgs g = gargs();
+      g.ring = m->d_ring;
       g.A = xn2; g.lda = D; g.W = lw(m, l, m->lay.w_gate_sh); g.W2 = lw(m, l, m->lay.w_up_sh); g.ldw = D;
       g.K = D; g.N = fs; g.k_chunk = D; dense_rows(g, R); g.C = hs; g.ldc = fs; g.flag = ps.flag;
       DG_CK(gemm(EPI_GEGLU_BF16, g, st));
       GemmArgs g2 = gargs();
+      g2.ring = m->d_ring;
       g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
       dense_rows(g2, R);
       g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, 64), fs, kMaxDenseSplit, &g2.k_chunk);
@@ -638,6 +671,7 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   Partials scp{at<float>(ws, p.dpart), 0, (long)R * D};
   if (d.self_cond) {
     GemmArgs g = gargs();
+    g.ring = m->d_ring;
     g.A = (const bf16_t*)c->self_cond; g.lda = D; g.W = (const bf16_t*)m->w.self_cond_w; g.ldw = D; g.K = D;
     g.N = D; dense_rows(g, R);
     g.k_split = choose_ksplit((long)g.items_max * cdiv(D, 64), D, kMaxDenseSplit, &g.k_chunk);
@@ -659,9 +693,10 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   float* logits = c->logits_dump ? c->logits_dump : at<float>(ws, p.logits);
   {
     GemmArgs g = gargs();
-    g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D; dense_rows(g, R); g.C = logits; g.ldc = V; g.flag = flag;
+    g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D;
+    g.C = logits; g.ldc = V; g.flag = flag;
     ProfScope ps_(m, DG_PROF_LMHEAD, st);
-    DG_CK(gemm(EPI_STORE_F32, g, st));
+    DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
   }
   float* rowstat = at<float>(ws, p.rowstat);
   SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, rowstat,
@@ -677,9 +712,9 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, flag, st));
     GemmArgs g = gargs();
     g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
-    g.k_split = p.ksplit; dense_rows(g, R); g.C = at<float>(ws, p.separt); g.ldc = D;
+    g.k_split = p.ksplit; g.C = at<float>(ws, p.separt); g.ldc = D;
     g.c_kstride = (long)R * D; g.flag = flag;
-    DG_CK(gemm(EPI_STORE_F32, g, st));
+    DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
     DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, c->stopped, T, flag,
                             st));
   }
@@ -852,12 +887,11 @@ extern "C" dg_status dg_init_canvas(const dg_model* m, dg_canvas* c, int32_t B, 
 extern "C" dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t M, int32_t N,
                                   int32_t K, float* Cm, int64_t ldc, dg_stream_t stream) {
   if (!A || !W || !Cm || M < 1 || N < 1 || K < 1 || lda < K || ldw < K || ldc < N) return DG_ERR_ARG;
-  if (K % 64) return DG_ERR_SHAPE;
+  if (K % 64 || lda % 8 || ldw % 8) return DG_ERR_SHAPE;
   GemmArgs g = gargs();
   g.A = (const bf16_t*)A; g.lda = lda; g.W = (const bf16_t*)W; g.ldw = ldw; g.K = K; g.N = N; g.k_chunk = K;
   g.C = Cm; g.ldc = ldc;
-  dense_rows(g, M);
-  DG_CK(gemm(EPI_STORE_F32, g, (hipStream_t)stream));
+  DG_CK(dense_gemm(EPI_STORE_F32, g, M, (hipStream_t)stream));
   return DG_OK;
 }
 

@@ -39,10 +39,16 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int GQ = a.H / a.Hkv;
   const int qpw = 128 / GQ;                      // queries per workgroup
-  const int g = blockIdx.y % a.Hkv, split = blockIdx.y / a.Hkv;
-  const int b = blockIdx.z;
   const int R = a.rows_per_batch;
-  const int q0wg = blockIdx.x * qpw;
+  const int nqb = (R + qpw - 1) / qpw;
+  // query blocks fastest: the blocks that read one (kv head, key split) share an XCD
+  const long lb = xcd_logical_block((long)nqb * a.Hkv * a.splits * a.B);
+  if (lb < 0) return;
+  const int qb = (int)(lb % nqb);
+  const int gy = (int)((lb / nqb) % (a.Hkv * a.splits));
+  const int b = (int)(lb / ((long)nqb * a.Hkv * a.splits));
+  const int g = gy % a.Hkv, split = gy / a.Hkv;
+  const int q0wg = qb * qpw;
   const int hq = wave % GQ, qf = wave / GQ;      // this wave's head and query fragment
   const int h = g * GQ + hq;
   const int qrow0 = q0wg + qf * 16;
@@ -74,7 +80,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   // K and two of V^T per thread (hd <= 256), written out slot by slot so the
   // staging values stay in registers
   static_assert(KPT <= 2 && VPT <= 2, "tile staging assumes hd <= 256");
-  uint4 ks0v, ks1v, vs0v, vs1v;
+  uint4 ka0, ka1, va0, va1, kb0, kb1, vb0, vb1;   // two staging sets: tiles t+1 and t+2 in flight
 #define DG_K_SRC(C)                                                                                \
   ({                                                                                               \
     const int kc_ = min(kt_ + min((C) / (HD / 8), 31), nk - 1);                                    \
@@ -86,13 +92,13 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
     (kt_ < a.n1 ? V1 + (long)(c_ >> 2) * a.v1_pitch + kt_ : V2 + (long)(c_ >> 2) * a.v2_pitch + (kt_ - a.n1)) \
         + (c_ & 3) * 8;                                                                            \
   })
-#define DG_ATTN_ISSUE(KT)                                                                          \
+#define DG_ATTN_ISSUE(KT, K0, K1_, V0, V1_)                                                        \
   do {                                                                                             \
     const int kt_ = (KT);                                                                          \
-    ks0v = *reinterpret_cast<const uint4*>(DG_K_SRC(tid));                                         \
-    if (KPT > 1) ks1v = *reinterpret_cast<const uint4*>(DG_K_SRC(tid + 512));                      \
-    vs0v = *reinterpret_cast<const uint4*>(DG_V_SRC(tid));                                         \
-    if (VPT > 1) vs1v = *reinterpret_cast<const uint4*>(DG_V_SRC(tid + 512));                      \
+    K0 = *reinterpret_cast<const uint4*>(DG_K_SRC(tid));                                           \
+    if (KPT > 1) K1_ = *reinterpret_cast<const uint4*>(DG_K_SRC(tid + 512));                       \
+    V0 = *reinterpret_cast<const uint4*>(DG_V_SRC(tid));                                           \
+    if (VPT > 1) V1_ = *reinterpret_cast<const uint4*>(DG_V_SRC(tid + 512));                       \
   } while (0)
 #define DG_K_PUT(BUF, C, V)                                                                        \
   do {                                                                                             \
@@ -114,12 +120,12 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
       *reinterpret_cast<uint4*>(&Vs[BUF][((C) >> 2) * VP + ((C) & 3) * 8]) = v;                    \
     }                                                                                              \
   } while (0)
-#define DG_ATTN_STORE(BUF, KT)                                                                     \
+#define DG_ATTN_STORE(BUF, KT, K0, K1_, V0, V1_)                                                   \
   do {                                                                                             \
-    DG_K_PUT(BUF, tid, ks0v);                                                                      \
-    if (KPT > 1) DG_K_PUT(BUF, tid + 512, ks1v);                                                   \
-    DG_V_PUT(BUF, KT, tid, vs0v);                                                                  \
-    if (VPT > 1) DG_V_PUT(BUF, KT, tid + 512, vs1v);                                               \
+    DG_K_PUT(BUF, tid, K0);                                                                        \
+    if (KPT > 1) DG_K_PUT(BUF, tid + 512, K1_);                                                    \
+    DG_V_PUT(BUF, KT, tid, V0);                                                                    \
+    if (VPT > 1) DG_V_PUT(BUF, KT, tid + 512, V1_);                                                \
   } while (0)
 
   floatx4 O[HD / 16];
@@ -128,83 +134,93 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * 1.4426950408889634f;
 
+  // Tile t sits in LDS buffer t & 1; the loads of tiles t+1 and t+2 are in
+  // flight in the two staging sets.  Issues are unconditional with the tile
+  // start clamped to the last tile, so the compiler's wait before each store
+  // only covers the older set.
+  const int klast = kbeg + 32 * max(ntile - 1, 0);
+#define DG_ATTN_TILE(BUF, KT)                                                                      \
+  do {                                                                                             \
+    const int kt_t_ = (KT);                                                                           \
+    if (wave_live) {                                                                               \
+      floatx4 s[2];                                                                                \
+      _Pragma("unroll") for (int kf = 0; kf < 2; ++kf) {                                           \
+        const bf16_t* kp = &Ks[BUF][(kf * 16 + lr) * KP + lg * 8];                                 \
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};                                                        \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(load_bf16x8(kp + 32 * ks), qfr[ks], acc); \
+        s[kf] = acc;                                                                               \
+      }                                                                                            \
+      float p[8];                                                                                  \
+      float mx = -INFINITY;                                                                        \
+      _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                             \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+          const int key = kt_t_ + kf * 16 + lg * 4 + i;                                               \
+          const bool ok = key < kend && (!a.causal || key <= qpos);                                \
+          const float v = ok ? s[kf][i] * sl2 : -INFINITY;                                         \
+          p[kf * 4 + i] = v;                                                                       \
+          mx = fmaxf(mx, v);                                                                       \
+        }                                                                                          \
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));                                                      \
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                      \
+      const float m_new = fmaxf(m_run, mx);                                                        \
+      const bool live = m_new != -INFINITY;                                                        \
+      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;                                      \
+      float ps = 0.f;                                                                              \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                              \
+        p[e] = live ? exp2f(p[e] - m_new) : 0.f;                                                   \
+        ps += p[e];                                                                                \
+      }                                                                                            \
+      ps += __shfl_xor(ps, 16, 64);                                                                \
+      ps += __shfl_xor(ps, 32, 64);                                                                \
+      l_run = l_run * alpha + ps;                                                                  \
+      m_run = m_new;                                                                               \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
+        const float ai = __shfl(alpha, lg * 4 + i, 64);                                            \
+        _Pragma("unroll") for (int nf = 0; nf < HD / 16; ++nf) O[nf][i] *= ai;                     \
+      }                                                                                            \
+      bf16x8 pf;                                                                                   \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];                          \
+      _Pragma("unroll") for (int nf = 0; nf < HD / 16; ++nf) {                                     \
+        const bf16_t* vp = &Vs[BUF][(nf * 16 + lr) * VP + lg * 4];                                 \
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp);                                      \
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);                                 \
+        bf16x8 vb;                                                                                 \
+        vb[0] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x & 0xFFFF));                             \
+        vb[1] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x >> 16));                                \
+        vb[2] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y & 0xFFFF));                             \
+        vb[3] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y >> 16));                                \
+        vb[4] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x & 0xFFFF));                             \
+        vb[5] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x >> 16));                                \
+        vb[6] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y & 0xFFFF));                             \
+        vb[7] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y >> 16));                                \
+        O[nf] = mfma16x16x32(pf, vb, O[nf]);                                                       \
+      }                                                                                            \
+    }                                                                                              \
+  } while (0)
+
   if (ntile > 0) {
-    DG_ATTN_ISSUE(kbeg);
-    DG_ATTN_STORE(0, kbeg);
+    DG_ATTN_ISSUE(kbeg, ka0, ka1, va0, va1);
+    DG_ATTN_ISSUE(min(kbeg + 32, klast), kb0, kb1, vb0, vb1);
+    DG_ATTN_STORE(0, kbeg, ka0, ka1, va0, va1);
   }
   __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    const int buf = t & 1;
+  for (int t = 0; t < ntile; t += 2) {
     const int kt = kbeg + 32 * t;
-    if (t + 1 < ntile) DG_ATTN_ISSUE(kt + 32);
-    if (wave_live) {
-      floatx4 s[2];
-#pragma unroll
-      for (int kf = 0; kf < 2; ++kf) {
-        const bf16_t* kp = &Ks[buf][(kf * 16 + lr) * KP + lg * 8];
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(load_bf16x8(kp + 32 * ks), qfr[ks], acc);
-        s[kf] = acc;
-      }
-      float p[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kf = 0; kf < 2; ++kf)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt + kf * 16 + lg * 4 + i;
-          const bool ok = key < kend && (!a.causal || key <= qpos);
-          const float v = ok ? s[kf][i] * sl2 : -INFINITY;
-          p[kf * 4 + i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const bool live = m_new != -INFINITY;
-      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = live ? exp2f(p[e] - m_new) : 0.f;
-        ps += p[e];
-      }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l_run = l_run * alpha + ps;
-      m_run = m_new;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, lg * 4 + i, 64);
-#pragma unroll
-        for (int nf = 0; nf < HD / 16; ++nf) O[nf][i] *= ai;
-      }
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];
-#pragma unroll
-      for (int nf = 0; nf < HD / 16; ++nf) {
-        const bf16_t* vp = &Vs[buf][(nf * 16 + lr) * VP + lg * 4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        bf16x8 vb;
-        vb[0] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x & 0xFFFF));
-        vb[1] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x >> 16));
-        vb[2] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y & 0xFFFF));
-        vb[3] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y >> 16));
-        vb[4] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x & 0xFFFF));
-        vb[5] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x >> 16));
-        vb[6] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y & 0xFFFF));
-        vb[7] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y >> 16));
-        O[nf] = mfma16x16x32(pf, vb, O[nf]);
-      }
-    }
-    if (t + 1 < ntile) DG_ATTN_STORE(buf ^ 1, kt + 32);
+    // even tile t: buffer 0; set b holds tile t+1; set a takes tile t+2
+    DG_ATTN_ISSUE(min(kt + 64, klast), ka0, ka1, va0, va1);
+    DG_ATTN_TILE(0, kt);
+    if (t + 1 < ntile) DG_ATTN_STORE(1, kt + 32, kb0, kb1, vb0, vb1);
+    __syncthreads();
+    if (t + 1 >= ntile) break;
+    // odd tile t+1: buffer 1; set a holds tile t+2; set b takes tile t+3
+    DG_ATTN_ISSUE(min(kt + 96, klast), kb0, kb1, vb0, vb1);
+    DG_ATTN_TILE(1, kt + 32);
+    if (t + 2 < ntile) DG_ATTN_STORE(0, kt + 64, ka0, ka1, va0, va1);
     __syncthreads();
   }
 
 #undef DG_ATTN_ISSUE
+#undef DG_ATTN_TILE
 #undef DG_ATTN_STORE
 #undef DG_K_SRC
 #undef DG_V_SRC
@@ -232,7 +248,9 @@ hipError_t attention(const AttnArgs& a, hipStream_t s) {
   if (a.H % a.Hkv != 0 || (GQ != 1 && GQ != 2 && GQ != 4)) return hipErrorInvalidValue;
   if (a.split_len % 32 != 0 || a.rows_per_batch <= 0 || (a.n2 > 0 && a.n1 % 32 != 0)) return hipErrorInvalidValue;
   const int qpw = 128 / GQ;
-  dim3 grid((a.rows_per_batch + qpw - 1) / qpw, a.Hkv * a.splits, a.B);
+  const long total = (long)((a.rows_per_batch + qpw - 1) / qpw) * a.Hkv * a.splits * a.B;
+  if (total <= 0) return hipSuccess;
+  const dim3 grid(xcd_grid(total));
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(512), 0, s, a); break;
     case 128: hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(512), 0, s, a); break;

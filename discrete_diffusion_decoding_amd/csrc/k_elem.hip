@@ -325,96 +325,108 @@ hipError_t attention_merge(const float* opart, const float* mlpart, int splits, 
 
 // ---------------------------------------------------------------------------
 // Router: logits = hi-part + lo-part products (an fp32-accurate product from two
-// bf16 MFMA passes) summed over split-K partials, top-k by repeated wavefront
-// argmax (ties -> lower expert), gates = softmax over the k selected logits.
-// One wave per token row.
-template <int NS>
-__global__ __launch_bounds__(256) void topk_kernel(Partials rl, int rows, int E, int k, int32_t* idx, float* gate,
+// bf16 MFMA passes) summed over split-K partials; top-k by rank: the rank of
+// expert e is the number of experts that order before it (larger logit, or an
+// equal logit and a lower index), so the k experts of rank < k are the top-k in
+// the order of repeated argmax with ties to the lower index.  Gates = softmax
+// over the k selected logits.  One wave per token row; every lane ranks its
+// experts against all logits of the row, read back from LDS as broadcasts.
+template <int NS, int NK>
+__global__ __launch_bounds__(256) void topk_kernel(Partials rl, int rows, int E, int32_t* idx, float* gate,
                                                    int32_t* idx_dump, float* gate_dump, const int32_t* flag) {
   if (flag && *flag) return;
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  float v[4];
-  float hv[4][NS], lv[4][NS];
+  __shared__ __attribute__((aligned(16))) float lv_s[4][256];
+  __shared__ float sel_v[4][NK];
+  __shared__ int sel_i[4][NK];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = min((int)blockIdx.x * 4 + w, rows - 1);   // surplus waves redo the last row, store nothing
+  const bool store = (int)blockIdx.x * 4 + w < rows;
+  float hv[4][NS], lo[4][NS];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = min(lane + 64 * j, E - 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       hv[j][s] = rl.p[s * rl.stride + (long)r * E + e];
-      lv[j][s] = rl.p[s * rl.stride + (long)(rows + r) * E + e];
+      lo[j][s] = rl.p[s * rl.stride + (long)(rows + r) * E + e];
+    }
+  }
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float h = 0.f, l = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      h += hv[j][s];
+      l += lo[j][s];
+    }
+    v[j] = h + l;
+    lv_s[w][lane + 64 * j] = (lane + 64 * j < E) ? v[j] : -INFINITY;
+  }
+  __syncthreads();
+  int rank[4] = {0, 0, 0, 0};
+  const float4* row4 = reinterpret_cast<const float4*>(lv_s[w]);
+  const int E4 = (E + 3) >> 2;
+  for (int q = 0; q < E4; ++q) {
+    const float4 o = row4[q];
+    const float ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int eo = 4 * q + t;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        rank[j] += (ov[t] > v[j] || (ov[t] == v[j] && eo < e)) ? 1 : 0;
+      }
     }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float hi = 0.f, lo = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      hi += hv[j][s];
-      lo += lv[j][s];
+    const int e = lane + 64 * j;
+    if (e < E && rank[j] < NK) {
+      sel_v[w][rank[j]] = v[j];
+      sel_i[w][rank[j]] = e;
     }
-    v[j] = (lane + 64 * j < E) ? hi + lo : -INFINITY;
   }
-  float selv[16];
-  int seli[16];
-  for (int t = 0; t < k; ++t) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  __syncthreads();
+  if (lane < NK && store) {
+    const float m = sel_v[w][0];
+    float den = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && (v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    selv[t] = bv;
-    seli[t] = bi;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j == bi) v[j] = -INFINITY;
-  }
-  if (lane == 0) {
-    float s = 0.f, ex[16];
-    for (int t = 0; t < k; ++t) {
-      ex[t] = expf(selv[t] - selv[0]);
-      s += ex[t];
-    }
-    for (int t = 0; t < k; ++t) {
-      const float gt = ex[t] / s;
-      idx[(long)r * k + t] = seli[t];
-      gate[(long)r * k + t] = gt;
-      if (idx_dump) idx_dump[(long)r * k + t] = seli[t];
-      if (gate_dump) gate_dump[(long)r * k + t] = gt;
-    }
+    for (int t = 0; t < NK; ++t) den += expf(sel_v[w][t] - m);
+    const float gt = expf(sel_v[w][lane] - m) / den;
+    const int e = sel_i[w][lane];
+    idx[(long)r * NK + lane] = e;
+    gate[(long)r * NK + lane] = gt;
+    if (idx_dump) idx_dump[(long)r * NK + lane] = e;
+    if (gate_dump) gate_dump[(long)r * NK + lane] = gt;
   }
 }
 
 hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
                        float* gate_dump, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (E > 256 || k > 16 || k > E) return hipErrorInvalidValue;
-#define DG_TOPK_CASE(N)                                                                                  \
-  case N:                                                                                                \
-    hipLaunchKernelGGL(topk_kernel<N>, dim3((rows + 3) / 4), dim3(256), 0, s, rlog, rows, E, k, idx, gate,  \
-                       idx_dump, gate_dump, flag);                                                       \
-    break;
-  switch (rlog.n) {
-    DG_TOPK_CASE(1) DG_TOPK_CASE(2) DG_TOPK_CASE(3) DG_TOPK_CASE(4)
-    DG_TOPK_CASE(5) DG_TOPK_CASE(6) DG_TOPK_CASE(7) DG_TOPK_CASE(8)
+  if (E > 256 || k > E || rlog.n < 1 || rlog.n > 8) return hipErrorInvalidValue;
+  const dim3 grid((rows + 3) / 4), block(256);
+#define DG_TOPK_NS(NK)                                                                                   \
+  switch (rlog.n) {                                                                                      \
+    case 1: hipLaunchKernelGGL((topk_kernel<1, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 2: hipLaunchKernelGGL((topk_kernel<2, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 3: hipLaunchKernelGGL((topk_kernel<3, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 4: hipLaunchKernelGGL((topk_kernel<4, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 5: hipLaunchKernelGGL((topk_kernel<5, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 6: hipLaunchKernelGGL((topk_kernel<6, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 7: hipLaunchKernelGGL((topk_kernel<7, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    default: hipLaunchKernelGGL((topk_kernel<8, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+  }
+  switch (k) {
+    case 1: DG_TOPK_NS(1) break;
+    case 2: DG_TOPK_NS(2) break;
+    case 4: DG_TOPK_NS(4) break;
+    case 8: DG_TOPK_NS(8) break;
     default: return hipErrorInvalidValue;
   }
-#undef DG_TOPK_CASE
+#undef DG_TOPK_NS
   return hipGetLastError();
 }
 
@@ -466,17 +478,43 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
     if (valid) slot_of[a] = wcnt[wave][e] + rank;
     __syncthreads();
   }
-  if (tid == 0) {
-    int run = 0, ni = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e] = run;
-      ibase[e] = ni;
-      run += cnt[e];
-      ni += (cnt[e] + chunk - 1) / chunk;
+  // exclusive scans over the experts of the row counts and of the item counts:
+  // waves 0-3 scan 64 experts each (shuffle scan), then add the wave totals
+  __shared__ int wtot[4][2];
+  int c = 0, ni = 0, ic = 0, ii = 0;
+  if (tid < 256) {
+    c = tid < E ? cnt[tid] : 0;
+    ni = (c + chunk - 1) / chunk;
+    ic = c;
+    ii = ni;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int uc = __shfl_up(ic, o, 64), ui = __shfl_up(ii, o, 64);
+      if (lane >= o) {
+        ic += uc;
+        ii += ui;
+      }
     }
-    off[E] = run;
-    ibase[E] = ni;
-    *n_items = ni;
+    if (lane == 63) {
+      wtot[wave][0] = ic;
+      wtot[wave][1] = ii;
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    for (int w = 0; w < wave; ++w) {
+      ic += wtot[w][0];
+      ii += wtot[w][1];
+    }
+    if (tid < E) {
+      off[tid] = ic - c;
+      ibase[tid] = ii - ni;
+    }
+    if (tid == E - 1) {
+      off[E] = ic;
+      ibase[E] = ii;
+      *n_items = ii;
+    }
   }
   __syncthreads();
   for (int e = tid; e <= E; e += 1024) {

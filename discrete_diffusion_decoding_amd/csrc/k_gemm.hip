@@ -27,26 +27,29 @@ namespace dg {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kStageElems = 2 * 64 * 64;  // A tile then B tile, 64 rows x 64 bf16 each
+// s_waitcnt immediate (gfx9 layout): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt_hi[15:14]; only the vector-memory count is waited for.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Workgroups are dealt to the 8 XCDs in turn (block b runs on XCD b mod 8).
-// The grid is padded to a multiple of 8 and renumbered so that every XCD works
-// through one contiguous range of logical tiles: the row chunks that share a
-// weight tile then run side by side on one XCD and share its L2.
-__device__ inline long xcd_logical_block(long total) {
-  const long per = gridDim.x >> 3;
-  const long b = blockIdx.x;
-  const long l = (b & 7) * per + (b >> 3);
-  return l < total ? l : -1;
-}
-static inline unsigned xcd_grid(long total) { return (unsigned)((total + 7) & ~7L); }
-
-template <int EPI>
+// ITEMS: rows come from the expert work list (grouped expert products);
+// otherwise dense rows in AR-row chunks.  AR: activation rows per tile (32 or
+// 64).  NS: depth of the LDS ring (NS - 1 stages in flight).
+template <int EPI, bool ITEMS, int AR, int NS>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) bf16_t S0[kStageElems];
-  __shared__ __attribute__((aligned(1024))) bf16_t S1[kStageElems];
-  __shared__ __attribute__((aligned(1024))) bf16_t S2[kStageElems];
-  __shared__ __attribute__((aligned(1024))) bf16_t S3[kStageElems];
+  static_assert(AR == 32 || AR == 64, "activation tile of 32 or 64 rows");
+  static_assert(NS >= 3 && NS <= 6, "ring of 3..6 stages");
+  constexpr int SE = (AR + 64) * 64;         // stage: AR activation rows then 64 weight rows, 64 bf16 each
+  constexpr int NG = (AR + 64) / 8;          // 8-row groups per stage (one 1 KB DMA each)
+  constexpr int GPW = NG / 4;                // groups per wave
+  constexpr int NAF = AR / 16;               // activation fragments
+  static_assert(NG % 4 == 0, "groups split evenly over 4 waves");
+  static_assert(NS * SE * 2 <= 80 * 1024, "two workgroups per CU");
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S2[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S3[NS > 3 ? SE : 1];
+  __shared__ __attribute__((aligned(1024))) bf16_t S4[NS > 4 ? SE : 1];
+  __shared__ __attribute__((aligned(1024))) bf16_t S5[NS > 5 ? SE : 1];
   if (g.flag && *g.flag) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int zk = (int)(rest / ntiles);
 
   int grp, r0, nrows;
-  if (g.items) {
+  if (ITEMS) {
     if (item >= *g.n_items) return;
     const int4 it = g.items[item];
     grp = it.x;
@@ -69,106 +72,141 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     nrows = it.z;
   } else {
     grp = 0;
-    r0 = item * 64;
-    nrows = min(64, g.M - r0);
+    r0 = item * AR;
+    nrows = min(AR, g.M - r0);
   }
   if (nrows <= 0) return;
-  const int nmf = (nrows + 15) >> 4;
   const int n_base = tile * NCOL;
   const int kb = zk * g.k_chunk;
   const int ke = min(g.K, kb + g.k_chunk);
   const int nst = (ke - kb) >> 6;   // 64-column stages
 
   // ---- per-lane global addresses of this wave's DMA rows --------------------
-  // wave w moves row groups 2w and 2w+1 (8 rows each) of both the A and the B
-  // tile; lane l fills LDS slot l%8 of row l/8 with global 16-byte part
-  // (l%8) ^ (row%8) of that row.
+  // the stage's 8-row groups (activation groups first, then weight groups) are
+  // dealt to the waves in turn: wave w moves groups w, w+4, ...; lane l fills
+  // LDS slot l%8 of row l/8 of its group with global 16-byte part (l%8)^(row%8).
   const int lrow = lane >> 3, lslot = lane & 7;
   const int part = lslot ^ lrow;
-  const bf16_t* asrc[2];
-  const bf16_t* bsrc[2];
+  const bf16_t* src[GPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (2 * wave + j) * 8 + lrow;       // 0..63
-    const int ar_l = r0 + min(row, nrows - 1);
-    const int ar = g.a_rows ? g.a_rows[ar_l] : ar_l;
-    asrc[j] = g.A + (long)ar * g.lda + kb + part * 8;
-    int wrow;
-    const bf16_t* Wb;
-    if (GEGLU) {
-      wrow = min(n_base + (row & 31), g.N - 1);
-      Wb = row < 32 ? g.W : g.W2;
+  for (int j = 0; j < GPW; ++j) {
+    const int gi = wave + 4 * j;
+    if (gi < AR / 8) {
+      const int row = gi * 8 + lrow;
+      const int ar_l = r0 + min(row, nrows - 1);
+      const int ar = g.a_rows ? g.a_rows[ar_l] : ar_l;
+      src[j] = g.A + (long)ar * g.lda + kb + part * 8;
     } else {
-      wrow = min(n_base + row, g.N - 1);
-      Wb = g.W;
+      const int row = (gi - AR / 8) * 8 + lrow;   // 0..63
+      int wrow;
+      const bf16_t* Wb;
+      if (GEGLU) {
+        wrow = min(n_base + (row & 31), g.N - 1);
+        Wb = row < 32 ? g.W : g.W2;
+      } else {
+        wrow = min(n_base + row, g.N - 1);
+        Wb = g.W;
+      }
+      src[j] = Wb + (long)grp * g.w_gstride + (long)wrow * g.ldw + kb + part * 8;
     }
-    bsrc[j] = Wb + (long)grp * g.w_gstride + (long)wrow * g.ldw + kb + part * 8;
   }
-  const int dst_a = (2 * wave) * 8 * 64;              // element offset of this wave's first A row group
-  const int dst_b = 64 * 64 + dst_a;
 
 #define DG_ISSUE(S, ST)                                                                          \
   do {                                                                                           \
     const int co_ = (ST) << 6;                                                                   \
-    __builtin_amdgcn_global_load_lds((const void*)(asrc[0] + co_), (lds_void_t*)&S[dst_a], 16, 0, 0);       \
-    __builtin_amdgcn_global_load_lds((const void*)(asrc[1] + co_), (lds_void_t*)&S[dst_a + 512], 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds((const void*)(bsrc[0] + co_), (lds_void_t*)&S[dst_b], 16, 0, 0);       \
-    __builtin_amdgcn_global_load_lds((const void*)(bsrc[1] + co_), (lds_void_t*)&S[dst_b + 512], 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < GPW; ++j)                                              \
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + co_), (lds_void_t*)&S[(wave + 4 * j) * 512], 16, 0, 0); \
   } while (0)
 
   // ---- MFMA operand reads ------------------------------------------------------
   const int lr = lane & 15, lg = lane >> 4;
   const int brow = 16 * wave + lr;                    // weight row in the B tile
-  floatx4 acc[4];
+  floatx4 acc[NAF];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < NAF; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
 #define DG_READ(S)                                                                               \
   _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
     const int p_ = 4 * j + lg;                                                                   \
-    bf[j] = *reinterpret_cast<const bf16x8*>(&S[64 * 64 + brow * 64 + ((p_ ^ (brow & 7)) << 3)]); \
-    _Pragma("unroll") for (int m = 0; m < 4; ++m) {                                              \
+    bf[j] = *reinterpret_cast<const bf16x8*>(&S[AR * 64 + brow * 64 + ((p_ ^ (brow & 7)) << 3)]); \
+    _Pragma("unroll") for (int m = 0; m < NAF; ++m) {                                            \
       const int arow = 16 * m + lr;                                                              \
       af[j][m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);     \
     }                                                                                            \
   }
 #define DG_MMA()                                                                                 \
   _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
-    _Pragma("unroll") for (int m = 0; m < 4; ++m) acc[m] = mfma16x16x32(af[j][m], bf[j], acc[m]);
+    _Pragma("unroll") for (int m = 0; m < NAF; ++m) acc[m] = mfma16x16x32(af[j][m], bf[j], acc[m]);
 
   // Every stage issues its loads unconditionally (stage index clamped to the
   // last one: the surplus loads land in a buffer that is not read again), so
-  // exactly two younger stages (8 loads per lane) are pending when a stage is
-  // read and one constant wait suffices.  The stage's LDS reads precede the
-  // next DMA issue (sched_barrier), so the compiler adds no wait of its own.
+  // exactly NS - 2 younger stages are pending when a stage is read and one
+  // constant wait suffices.  The stage's LDS reads precede the next DMA issue
+  // (sched_barrier), so the compiler adds no wait of its own.
 #define DG_ITER(SI, CUR, NXT)                                                                    \
   do {                                                                                           \
     const int s_ = (SI);                                                                         \
-    __builtin_amdgcn_s_waitcnt((8 & 0xF) | (0x7 << 4) | (0xF << 8));                             \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * GPW));                                      \
     __builtin_amdgcn_s_barrier();                                                                \
     DG_READ(CUR);                                                                                \
     __builtin_amdgcn_sched_barrier(0);                                                           \
-    DG_ISSUE(NXT, min(s_ + 3, nst - 1));                                                         \
+    DG_ISSUE(NXT, min(s_ + NS - 1, nst - 1));                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                           \
     DG_MMA();                                                                                    \
   } while (0)
-  bf16x8 af[2][4], bf[2];
+  // after the last full round every stage has been issued: the remaining
+  // stages only drain the ring (the first wait covers all of them)
+#define DG_TAIL(CUR)                                                                             \
+  do {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                                   \
+    __builtin_amdgcn_s_barrier();                                                                \
+    DG_READ(CUR);                                                                                \
+    DG_MMA();                                                                                    \
+  } while (0)
+  bf16x8 af[2][NAF], bf[2];
 
   if (nst > 0) {
     DG_ISSUE(S0, 0);
     DG_ISSUE(S1, min(1, nst - 1));
-    DG_ISSUE(S2, min(2, nst - 1));
+    if (NS > 3) DG_ISSUE(S2, min(2, nst - 1));
+    if (NS > 4) DG_ISSUE(S3, min(3, nst - 1));
+    if (NS > 5) DG_ISSUE(S4, min(4, nst - 1));
     int s = 0;
-    for (; s + 4 <= nst; s += 4) {
-      DG_ITER(s, S0, S3);
-      DG_ITER(s + 1, S1, S0);
-      DG_ITER(s + 2, S2, S1);
-      DG_ITER(s + 3, S3, S2);
+    if (NS == 3) {
+      for (; s + 3 <= nst; s += 3) {
+        DG_ITER(s, S0, S2); DG_ITER(s + 1, S1, S0); DG_ITER(s + 2, S2, S1);
+      }
+      if (s < nst) DG_TAIL(S0);
+      if (s + 1 < nst) DG_TAIL(S1);
+    } else if (NS == 4) {
+      for (; s + 4 <= nst; s += 4) {
+        DG_ITER(s, S0, S3); DG_ITER(s + 1, S1, S0); DG_ITER(s + 2, S2, S1); DG_ITER(s + 3, S3, S2);
+      }
+      if (s < nst) DG_TAIL(S0);
+      if (s + 1 < nst) DG_TAIL(S1);
+      if (s + 2 < nst) DG_TAIL(S2);
+    } else if (NS == 5) {
+      for (; s + 5 <= nst; s += 5) {
+        DG_ITER(s, S0, S4); DG_ITER(s + 1, S1, S0); DG_ITER(s + 2, S2, S1); DG_ITER(s + 3, S3, S2);
+        DG_ITER(s + 4, S4, S3);
+      }
+      if (s < nst) DG_TAIL(S0);
+      if (s + 1 < nst) DG_TAIL(S1);
+      if (s + 2 < nst) DG_TAIL(S2);
+      if (s + 3 < nst) DG_TAIL(S3);
+    } else {
+      for (; s + 6 <= nst; s += 6) {
+        DG_ITER(s, S0, S5); DG_ITER(s + 1, S1, S0); DG_ITER(s + 2, S2, S1); DG_ITER(s + 3, S3, S2);
+        DG_ITER(s + 4, S4, S3); DG_ITER(s + 5, S5, S4);
+      }
+      if (s < nst) DG_TAIL(S0);
+      if (s + 1 < nst) DG_TAIL(S1);
+      if (s + 2 < nst) DG_TAIL(S2);
+      if (s + 3 < nst) DG_TAIL(S3);
+      if (s + 4 < nst) DG_TAIL(S4);
     }
-    if (s < nst) DG_ITER(s, S0, S3);
-    if (s + 1 < nst) DG_ITER(s + 1, S1, S0);
-    if (s + 2 < nst) DG_ITER(s + 2, S2, S1);
   }
+#undef DG_TAIL
 #undef DG_ISSUE
 #undef DG_READ
 #undef DG_MMA
@@ -183,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     floatx4* red = reinterpret_cast<floatx4*>(S0);
     if (wave >= 2) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) red[((wave - 2) * 4 + m) * 64 + lane] = acc[m];
+      for (int m = 0; m < NAF; ++m) red[((wave - 2) * NAF + m) * 64 + lane] = acc[m];
     }
     __syncthreads();
     if (wave >= 2) return;
@@ -191,10 +229,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int col = n_base + 16 * wave + lr;
   if (col >= g.N) return;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (m >= nmf) continue;
+  for (int m = 0; m < NAF; ++m) {
     floatx4 u = {0.f, 0.f, 0.f, 0.f};
-    if (GEGLU) u = reinterpret_cast<floatx4*>(S0)[(wave * 4 + m) * 64 + lane];
+    if (GEGLU) u = reinterpret_cast<floatx4*>(S0)[(wave * NAF + m) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rl = 16 * m + 4 * lg + i;
@@ -205,10 +242,6 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
         reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(v);
       } else if (EPI == EPI_STORE_F32) {
         reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = v;
-      } else if (EPI == EPI_ADD_F32) {
-        reinterpret_cast<float*>(g.C)[off] += v;
-      } else if (EPI == EPI_ADD_GATED_F32) {
-        reinterpret_cast<float*>(g.C)[off] += sigmoidf_(bf2f(g.col_gate[col])) * v;
       } else {
         reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(gelu_tanh(v) * u[i]);
       }
@@ -216,25 +249,39 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int EPI>
-static hipError_t launch(const GemmArgs& a, hipStream_t s) {
+template <int EPI, bool ITEMS, int AR, int NS>
+static hipError_t launch_v(GemmArgs a, hipStream_t s) {
   constexpr int NCOL = (EPI == EPI_GEGLU_BF16) ? 32 : 64;
+  if (!ITEMS) a.items_max = (a.M + AR - 1) / AR;
   const int ntiles = (a.N + NCOL - 1) / NCOL;
   const long total = (long)a.items_max * ntiles * a.k_split;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3(xcd_grid(total)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<EPI, ITEMS, AR, NS>), dim3(xcd_grid(total)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// variant (activation rows, ring depth) chosen by the caller: a.tile_rows, a.ring
+template <int EPI, bool ITEMS>
+static hipError_t launch(const GemmArgs& a, hipStream_t s) {
+  // measured on the 2816-wide model: tile rows and ring depth barely move the
+  // weight stream (the activation tile's L2 traffic and the MFMA/LDS work bound
+  // it); the grouped expert products run a 5-deep ring, dense ones 4
+  if (a.tile_rows != 64) return hipErrorInvalidValue;
+  switch (a.ring) {
+    case 4: return launch_v<EPI, ITEMS, 64, 4>(a, s);
+    case 5: return launch_v<EPI, ITEMS, 64, 5>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
   if (a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;   // 16-byte aligned rows
+  const bool it = a.items != nullptr;
   switch (epi) {
-    case EPI_STORE_BF16: return launch<EPI_STORE_BF16>(a, s);
-    case EPI_STORE_F32: return launch<EPI_STORE_F32>(a, s);
-    case EPI_ADD_F32: return launch<EPI_ADD_F32>(a, s);
-    case EPI_ADD_GATED_F32: return launch<EPI_ADD_GATED_F32>(a, s);
-    case EPI_GEGLU_BF16: return launch<EPI_GEGLU_BF16>(a, s);
+    case EPI_STORE_BF16: return it ? launch<EPI_STORE_BF16, true>(a, s) : launch<EPI_STORE_BF16, false>(a, s);
+    case EPI_STORE_F32: return it ? launch<EPI_STORE_F32, true>(a, s) : launch<EPI_STORE_F32, false>(a, s);
+    case EPI_GEGLU_BF16: return it ? launch<EPI_GEGLU_BF16, true>(a, s) : launch<EPI_GEGLU_BF16, false>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -338,7 +385,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
 #define DG_FITER(SI, CUR, NXT)                                                                             \
   do {                                                                                                     \
     const int s_ = (SI);                                                                                   \
-    __builtin_amdgcn_s_waitcnt((6 & 0xF) | (0x7 << 4) | (0xF << 8));                                       \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(6));                                                             \
     __builtin_amdgcn_s_barrier();                                                                          \
     DG_FREAD(CUR);                                                                                         \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
@@ -356,8 +403,17 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
     DG_FITER(s + 1, S1, S0);
     DG_FITER(s + 2, S2, S1);
   }
-  if (s < nst) DG_FITER(s, S0, S2);
-  if (s + 1 < nst) DG_FITER(s + 1, S1, S0);
+  // every stage has been issued: the tail only drains the ring
+#define DG_FTAIL(CUR)                                                                                      \
+  do {                                                                                                     \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                                             \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    DG_FREAD(CUR);                                                                                         \
+    DG_FMMA();                                                                                             \
+  } while (0)
+  if (s < nst) DG_FTAIL(S0);
+  if (s + 1 < nst) DG_FTAIL(S1);
+#undef DG_FTAIL
 #undef DG_FISSUE
 #undef DG_FREAD
 #undef DG_FMMA
@@ -384,6 +440,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
   if (a.lda % 8 != 0 || a.ldw % 8 != 0 || a.items || a.a_rows) return hipErrorInvalidValue;
+  if (!gemm_fat_pitch_ok(a.lda, a.ldw)) return hipErrorInvalidValue;   // 32-bit per-lane offsets
   const long total = (long)a.items_max * ((a.N + 127) / 128) * a.k_split;
   if (total <= 0) return hipSuccess;
   switch (epi) {

@@ -278,7 +278,7 @@ hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* see
 }
 
 __global__ void set_step_kernel(int32_t* steps, const int32_t* stopped, int B, int step) {
-  if (threadIdx.x < B && !stopped[threadIdx.x]) steps[threadIdx.x] = step;
+  if ((int)threadIdx.x < B && !stopped[threadIdx.x]) steps[threadIdx.x] = step;
 }
 
 hipError_t set_step(int32_t* steps, const int32_t* stopped, int B, int step, hipStream_t s) {

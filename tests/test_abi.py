@@ -112,6 +112,16 @@ def test_step_rejects_bad_arguments_before_any_device_work():
     dg.dg_model_destroy(h)
 
 
+def test_gemm_rejects_bad_shapes_before_any_device_work():
+    L = dg.lib()
+    p = C.c_void_p(0x4000)
+    # K not a multiple of 64; row pitches not multiples of 8 (16-byte rows)
+    assert L.dg_gemm_bf16(p, 96, p, 96, 256, 64, 96, p, 64, None) == dg.DG_ERR_SHAPE
+    assert L.dg_gemm_bf16(p, 132, p, 128, 256, 64, 128, p, 64, None) == dg.DG_ERR_SHAPE
+    assert L.dg_gemm_bf16(p, 128, p, 130, 8, 64, 128, p, 64, None) == dg.DG_ERR_SHAPE
+    assert L.dg_gemm_bf16(p, 64, p, 128, 8, 64, 128, p, 64, None) == dg.DG_ERR_ARG   # lda < K
+
+
 def test_host_philox_equals_oracle_definition():
     g = np.random.default_rng(0)
     for _ in range(200):
