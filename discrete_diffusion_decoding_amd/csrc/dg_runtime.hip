@@ -59,7 +59,12 @@ struct dg_model {
   mutable Prof prof;
   bool use_graphs = true;
   // 64-row GEMM kernel variants: grouped expert products (tile rows, ring) and dense (ring)
-  int x_rows = 64, x_ring = 5, d_ring = 4;
+  int x_rows = 64, x_cols = 64, x_ring = 5, d_ring = 4;
+  // second stream (default priority) for the shared FFN, which runs beside the
+  // routed path; created on first use, with its fork / join events
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  bool side_failed = false;
   std::vector<GraphEntry> graphs;
   unsigned long long use_clock = 0;
 };
@@ -178,6 +183,9 @@ extern "C" dg_status dg_model_create(const dg_model_desc* d, const dg_weights* w
 
 extern "C" void dg_model_destroy(dg_model* m) {
   if (!m) return;
+  if (m->side) (void)hipStreamDestroy(m->side);
+  if (m->ev_fork) (void)hipEventDestroy(m->ev_fork);
+  if (m->ev_join) (void)hipEventDestroy(m->ev_join);
   for (hipEvent_t e : m->prof.pool) (void)hipEventDestroy(e);
   for (GraphEntry& g : m->graphs) (void)hipGraphExecDestroy(g.exec);
   delete m;
@@ -339,6 +347,7 @@ static GemmArgs gargs() {
   memset(&g, 0, sizeof(g));
   g.k_split = 1;
   g.tile_rows = 64;
+  g.tile_cols = 64;
   g.ring = 4;
   return g;
 }
@@ -349,6 +358,23 @@ static void dense_rows(GemmArgs& g, int M) {
   g.items = nullptr;
   g.n_items = nullptr;
   g.items_max = cdiv(M, kGemmRowChunk);
+}
+
+// the side stream, created on first use; false (run serially) if it cannot be made
+static bool side_stream(const dg_model* mc) {
+  dg_model* m = const_cast<dg_model*>(mc);
+  if (m->side) return true;
+  if (m->side_failed) return false;
+  if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&m->ev_join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    m->side_failed = true;
+    if (m->side) (void)hipStreamDestroy(m->side);
+    m->side = nullptr;
+    return false;
+  }
+  return true;
 }
 
 static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pass& ps, hipStream_t st) {
@@ -475,6 +501,34 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, opp, nullptr, ps.flag,
                          st));
     }
+    // shared FFN: independent of the routed path, so (outside profiling) it runs
+    // on the side stream, forked here and joined before the combine
+    Partials ysp{ys, 0, (long)R * D};
+    bool forked = false;
+    if (fs) {
+      hipStream_t ss = st;
+      if (!m->prof.on && side_stream(m)) {
+        DG_CK(hipEventRecord(m->ev_fork, st));
+        DG_CK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+        ss = m->side;
+        forked = true;
+      }
+      ProfScope ps_(m, DG_PROF_SHARED, ss);
+      GemmArgs g = gargs();
+      g.ring = m->d_ring;
+      g.A = xn2; g.lda = D; g.W = lw(m, l, m->lay.w_gate_sh); g.W2 = lw(m, l, m->lay.w_up_sh); g.ldw = D;
+      g.K = D; g.N = fs; g.k_chunk = D; dense_rows(g, R); g.C = hs; g.ldc = fs; g.flag = ps.flag;
+      DG_CK(gemm(EPI_GEGLU_BF16, g, ss));
+      GemmArgs g2 = gargs();
+      g2.ring = m->d_ring;
+      g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
+      dense_rows(g2, R);
+      g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, 64), fs, kMaxDenseSplit, &g2.k_chunk);
+      ysp.n = g2.k_split;
+      g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
+      DG_CK(gemm(EPI_STORE_F32, g2, ss));
+      if (forked) DG_CK(hipEventRecord(m->ev_join, ss));
+    }
     // router logits (hi and lo rows, split-K partials) and top-k
     Partials rlp{rlog, 1, (long)2 * R * E};
     {
@@ -499,7 +553,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g = gargs();
       g.A = xn2; g.lda = D; g.a_rows = slot_row; g.W = lw(m, l, m->lay.w_gate); g.W2 = lw(m, l, m->lay.w_up);
       g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D;
-      g.items = items; g.n_items = nitems; g.items_max = items_max; g.tile_rows = m->x_rows; g.ring = m->x_ring;
+      g.items = items; g.n_items = nitems; g.items_max = items_max; g.tile_rows = m->x_rows; g.tile_cols = m->x_cols; g.ring = m->x_ring;
       g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_GATEUP, st);
       DG_CK(gemm(EPI_GEGLU_BF16, g, st));
@@ -508,28 +562,12 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g = gargs();
       g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
       g.N = D; g.k_chunk = fe; g.items = items; g.n_items = nitems; g.items_max = items_max;
-      g.tile_rows = m->x_rows; g.ring = m->x_ring;
+      g.tile_rows = m->x_rows; g.tile_cols = 128; g.ring = 3;   // 128 weight rows per tile: 22 tiles of d
       g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_F32, g, st));
     }
-    Partials ysp{ys, 0, (long)R * D};
-    if (fs) {
-      ProfScope ps_(m, DG_PROF_SHARED, st);
-      GemmArgs g = gargs();
-      g.ring = m->d_ring;
-      g.A = xn2; g.lda = D; g.W = lw(m, l, m->lay.w_gate_sh); g.W2 = lw(m, l, m->lay.w_up_sh); g.ldw = D;
-      g.K = D; g.N = fs; g.k_chunk = D; dense_rows(g, R); g.C = hs; g.ldc = fs; g.flag = ps.flag;
-      DG_CK(gemm(EPI_GEGLU_BF16, g, st));
-      GemmArgs g2 = gargs();
-      g2.ring = m->d_ring;
-      g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
-      dense_rows(g2, R);
-      g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, 64), fs, kMaxDenseSplit, &g2.k_chunk);
-      ysp.n = g2.k_split;
-      g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
-      DG_CK(gemm(EPI_STORE_F32, g2, st));
-    }
+    if (forked) DG_CK(hipStreamWaitEvent(st, m->ev_join, 0));
     const bf16_t* nw = nullptr;
     if (l + 1 < d.n_layers) nw = lw(m, l + 1, m->lay.attn_norm);
     else if (ps.final_norm) nw = (const bf16_t*)m->w.final_norm;

@@ -33,15 +33,22 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >
 
 // ITEMS: rows come from the expert work list (grouped expert products);
 // otherwise dense rows in AR-row chunks.  AR: activation rows per tile (32 or
-// 64).  NS: depth of the LDS ring (NS - 1 stages in flight).
-template <int EPI, bool ITEMS, int AR, int NS>
+// 64).  BW: weight rows per tile (64 or 128; each of the 4 waves multiplies BW/4
+// of them by all AR activation rows).  NS: depth of the LDS ring (NS - 1
+// stages in flight).  The weight stream is what the product is bound by; the
+// activation tile is re-read from L2 for every weight tile, so a wider BW
+// spends fewer DMA and LDS cycles per weight byte.
+template <int EPI, bool ITEMS, int AR, int BW, int NS>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   static_assert(AR == 32 || AR == 64, "activation tile of 32 or 64 rows");
+  static_assert(BW == 64 || BW == 128, "weight tile of 64 or 128 rows");
   static_assert(NS >= 3 && NS <= 6, "ring of 3..6 stages");
-  constexpr int SE = (AR + 64) * 64;         // stage: AR activation rows then 64 weight rows, 64 bf16 each
-  constexpr int NG = (AR + 64) / 8;          // 8-row groups per stage (one 1 KB DMA each)
+  constexpr int SE = (AR + BW) * 64;         // stage: AR activation rows then BW weight rows, 64 bf16 each
+  constexpr int NG = (AR + BW) / 8;          // 8-row groups per stage (one 1 KB DMA each)
   constexpr int GPW = NG / 4;                // groups per wave
   constexpr int NAF = AR / 16;               // activation fragments
+  constexpr int WPW = BW / 4;                // weight rows per wave
+  constexpr int NBF = WPW / 16;              // weight fragments per wave
   static_assert(NG % 4 == 0, "groups split evenly over 4 waves");
   static_assert(NS * SE * 2 <= 80 * 1024, "two workgroups per CU");
   __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr bool GEGLU = EPI == EPI_GEGLU_BF16;
-  constexpr int NCOL = GEGLU ? 32 : 64;   // output columns per tile
+  constexpr int NCOL = GEGLU ? BW / 2 : BW;   // output columns per tile
   const int ntiles = (g.N + NCOL - 1) / NCOL;
   const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
   if (bidx < 0) return;
@@ -85,6 +92,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   // the stage's 8-row groups (activation groups first, then weight groups) are
   // dealt to the waves in turn: wave w moves groups w, w+4, ...; lane l fills
   // LDS slot l%8 of row l/8 of its group with global 16-byte part (l%8)^(row%8).
+  // GEGLU tiles hold NCOL gate rows, then the NCOL matching up rows.
   const int lrow = lane >> 3, lslot = lane & 7;
   const int part = lslot ^ lrow;
   const bf16_t* src[GPW];
@@ -97,12 +105,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
       const int ar = g.a_rows ? g.a_rows[ar_l] : ar_l;
       src[j] = g.A + (long)ar * g.lda + kb + part * 8;
     } else {
-      const int row = (gi - AR / 8) * 8 + lrow;   // 0..63
+      const int row = (gi - AR / 8) * 8 + lrow;   // 0..BW-1
       int wrow;
       const bf16_t* Wb;
       if (GEGLU) {
-        wrow = min(n_base + (row & 31), g.N - 1);
-        Wb = row < 32 ? g.W : g.W2;
+        wrow = min(n_base + (row % NCOL), g.N - 1);
+        Wb = row < NCOL ? g.W : g.W2;
       } else {
         wrow = min(n_base + row, g.N - 1);
         Wb = g.W;
@@ -120,15 +128,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 
   // ---- MFMA operand reads ------------------------------------------------------
   const int lr = lane & 15, lg = lane >> 4;
-  const int brow = 16 * wave + lr;                    // weight row in the B tile
-  floatx4 acc[NAF];
+  // weight-row offsets computed once: derived inside the read macro, the
+  // compiler lost track of which LDS array a read targets and made it wait for
+  // every DMA in flight
+  int boff[NBF];
 #pragma unroll
-  for (int m = 0; m < NAF; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NBF; ++n) boff[n] = AR * 64 + (WPW * wave + 16 * n + lr) * 64;
+  floatx4 acc[NAF][NBF];
+#pragma unroll
+  for (int m = 0; m < NAF; ++m)
+#pragma unroll
+    for (int n = 0; n < NBF; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
 #define DG_READ(S)                                                                               \
   _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
     const int p_ = 4 * j + lg;                                                                   \
-    bf[j] = *reinterpret_cast<const bf16x8*>(&S[AR * 64 + brow * 64 + ((p_ ^ (brow & 7)) << 3)]); \
+    _Pragma("unroll") for (int n = 0; n < NBF; ++n)                                              \
+      bf[j][n] = *reinterpret_cast<const bf16x8*>(&S[boff[n] + ((p_ ^ (lr & 7)) << 3)]);         \
     _Pragma("unroll") for (int m = 0; m < NAF; ++m) {                                            \
       const int arow = 16 * m + lr;                                                              \
       af[j][m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);     \
@@ -136,7 +152,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   }
 #define DG_MMA()                                                                                 \
   _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
-    _Pragma("unroll") for (int m = 0; m < NAF; ++m) acc[m] = mfma16x16x32(af[j][m], bf[j], acc[m]);
+    _Pragma("unroll") for (int m = 0; m < NAF; ++m)                                              \
+      _Pragma("unroll") for (int n = 0; n < NBF; ++n) acc[m][n] = mfma16x16x32(af[j][m], bf[j][n], acc[m][n]);
 
   // Every stage issues its loads unconditionally (stage index clamped to the
   // last one: the surplus loads land in a buffer that is not read again), so
@@ -163,7 +180,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     DG_READ(CUR);                                                                                \
     DG_MMA();                                                                                    \
   } while (0)
-  bf16x8 af[2][NAF], bf[2];
+  bf16x8 af[2][NAF], bf[2][NBF];
 
   if (nst > 0) {
     DG_ISSUE(S0, 0);
@@ -213,7 +230,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 #undef DG_ITER
 
   // ---- epilogue ------------------------------------------------------------------
-  // lane holds rows 4*lg + i of each 16-row fragment, column lr of the wave's 16
+  // lane holds rows 4*lg + i of each 16-row fragment, column lr of each of the
+  // wave's 16-column fragments
   if (GEGLU) {
     // waves 2,3 hold the up projections of the columns of waves 0,1
     __builtin_amdgcn_s_waitcnt(0);
@@ -221,55 +239,60 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
     floatx4* red = reinterpret_cast<floatx4*>(S0);
     if (wave >= 2) {
 #pragma unroll
-      for (int m = 0; m < NAF; ++m) red[((wave - 2) * NAF + m) * 64 + lane] = acc[m];
+      for (int m = 0; m < NAF; ++m)
+#pragma unroll
+        for (int n = 0; n < NBF; ++n) red[(((wave - 2) * NAF + m) * NBF + n) * 64 + lane] = acc[m][n];
     }
     __syncthreads();
     if (wave >= 2) return;
   }
-  const int col = n_base + 16 * wave + lr;
-  if (col >= g.N) return;
 #pragma unroll
-  for (int m = 0; m < NAF; ++m) {
-    floatx4 u = {0.f, 0.f, 0.f, 0.f};
-    if (GEGLU) u = reinterpret_cast<floatx4*>(S0)[(wave * NAF + m) * 64 + lane];
+  for (int n = 0; n < NBF; ++n) {
+    const int col = n_base + WPW * wave + 16 * n + lr;
+    if (col >= g.N) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rl = 16 * m + 4 * lg + i;
-      if (rl >= nrows) continue;
-      const long off = (long)(r0 + rl) * g.ldc + col;
-      const float v = acc[m][i];
-      if (EPI == EPI_STORE_BF16) {
-        reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(v);
-      } else if (EPI == EPI_STORE_F32) {
-        reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = v;
-      } else {
-        reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(gelu_tanh(v) * u[i]);
+    for (int m = 0; m < NAF; ++m) {
+      floatx4 u = {0.f, 0.f, 0.f, 0.f};
+      if (GEGLU) u = reinterpret_cast<floatx4*>(S0)[((wave * NAF + m) * NBF + n) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 16 * m + 4 * lg + i;
+        if (rl >= nrows) continue;
+        const long off = (long)(r0 + rl) * g.ldc + col;
+        const float v = acc[m][n][i];
+        if (EPI == EPI_STORE_BF16) {
+          reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(v);
+        } else if (EPI == EPI_STORE_F32) {
+          reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = v;
+        } else {
+          reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(gelu_tanh(v) * u[i]);
+        }
       }
     }
   }
 }
 
-template <int EPI, bool ITEMS, int AR, int NS>
+template <int EPI, bool ITEMS, int AR, int BW, int NS>
 static hipError_t launch_v(GemmArgs a, hipStream_t s) {
-  constexpr int NCOL = (EPI == EPI_GEGLU_BF16) ? 32 : 64;
+  constexpr int NCOL = (EPI == EPI_GEGLU_BF16) ? BW / 2 : BW;
   if (!ITEMS) a.items_max = (a.M + AR - 1) / AR;
   const int ntiles = (a.N + NCOL - 1) / NCOL;
   const long total = (long)a.items_max * ntiles * a.k_split;
   if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<EPI, ITEMS, AR, NS>), dim3(xcd_grid(total)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<EPI, ITEMS, AR, BW, NS>), dim3(xcd_grid(total)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// variant (activation rows, ring depth) chosen by the caller: a.tile_rows, a.ring
+// variant chosen by the caller: a.tile_rows (activation rows), a.tile_cols
+// (weight rows), a.ring (LDS ring depth)
 template <int EPI, bool ITEMS>
 static hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  // measured on the 2816-wide model: tile rows and ring depth barely move the
-  // weight stream (the activation tile's L2 traffic and the MFMA/LDS work bound
-  // it); the grouped expert products run a 5-deep ring, dense ones 4
   if (a.tile_rows != 64) return hipErrorInvalidValue;
-  switch (a.ring) {
-    case 4: return launch_v<EPI, ITEMS, 64, 4>(a, s);
-    case 5: return launch_v<EPI, ITEMS, 64, 5>(a, s);
+  const int v = a.tile_cols * 10 + a.ring;
+  switch (v) {
+    case 644: return launch_v<EPI, ITEMS, 64, 64, 4>(a, s);
+    case 645: return launch_v<EPI, ITEMS, 64, 64, 5>(a, s);
+    case 1283: return launch_v<EPI, ITEMS, 64, 128, 3>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
