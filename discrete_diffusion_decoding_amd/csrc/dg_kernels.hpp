@@ -34,7 +34,7 @@ struct GemmArgs {
   int k_split;
   int tile_rows;   // 64-row kernel: activation rows per tile (64; also the work-list chunk size),
   int tile_cols;   // weight rows per tile (64 | 128)
-  int ring;        // and its LDS ring depth (64 wide: 4 | 5; 128 wide: 3)
+  int ring;        // and its LDS ring depth (64 wide: 4 | 5; 128 wide: 2 | 3)
   void* C;
   long ldc;
   long c_kstride;

@@ -60,6 +60,9 @@ struct dg_model {
   bool use_graphs = true;
   // 64-row GEMM kernel variants: grouped expert products (tile rows, ring) and dense (ring)
   int x_rows = 64, x_cols = 64, x_ring = 5, d_ring = 4;
+  // expert down projection: 128 weight rows per tile (22 tiles of d), double
+  // buffered so three workgroups share a CU (its K is only 11 stages long)
+  int xd_cols = 128, xd_ring = 2;
   // second stream (default priority) for the shared FFN, which runs beside the
   // routed path; created on first use, with its fork / join events
   hipStream_t side = nullptr;
@@ -562,7 +565,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g = gargs();
       g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
       g.N = D; g.k_chunk = fe; g.items = items; g.n_items = nitems; g.items_max = items_max;
-      g.tile_rows = m->x_rows; g.tile_cols = 128; g.ring = 3;   // 128 weight rows per tile: 22 tiles of d
+      g.tile_rows = m->x_rows; g.tile_cols = m->xd_cols; g.ring = m->xd_ring;
       g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_F32, g, st));

@@ -81,24 +81,28 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   // staging values stay in registers
   static_assert(KPT <= 2 && VPT <= 2, "tile staging assumes hd <= 256");
   uint4 ka0, ka1, va0, va1, kb0, kb1, vb0, vb1;   // two staging sets: tiles t+1 and t+2 in flight
-#define DG_K_SRC(C)                                                                                \
-  ({                                                                                               \
-    const int kc_ = min(kt_ + min((C) / (HD / 8), 31), nk - 1);                                    \
-    (kc_ < a.n1 ? K1 + (long)kc_ * HD : K2 + (long)(kc_ - a.n1) * HD) + ((C) % (HD / 8)) * 8;      \
-  })
-#define DG_V_SRC(C)                                                                                \
-  ({                                                                                               \
-    const int c_ = min((C), VCH - 1);                                                              \
-    (kt_ < a.n1 ? V1 + (long)(c_ >> 2) * a.v1_pitch + kt_ : V2 + (long)(c_ >> 2) * a.v2_pitch + (kt_ - a.n1)) \
-        + (c_ & 3) * 8;                                                                            \
-  })
+  // Every key count here is a multiple of 32 (prefix lengths, canvases and
+  // prefill chunks are), so a 32-key tile lies wholly in one source and needs
+  // no clamping: its address is a wave-uniform base plus a per-thread offset
+  // fixed for the whole loop.
+  long koff[2], voff1[2], voff2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = tid + 512 * j;
+    const int kc = min(c, KCH - 1), vc = min(c, VCH - 1);
+    koff[j] = (long)(kc / (HD / 8)) * HD + (kc % (HD / 8)) * 8;
+    voff1[j] = (long)(vc >> 2) * a.v1_pitch + (vc & 3) * 8;
+    voff2[j] = (long)(vc >> 2) * a.v2_pitch + (vc & 3) * 8;
+  }
+#define DG_K_SRC(J) (kt_ < a.n1 ? K1 + (long)kt_ * HD : K2 + (long)(kt_ - a.n1) * HD) + koff[J]
+#define DG_V_SRC(J) (kt_ < a.n1 ? V1 + kt_ + voff1[J] : V2 + (kt_ - a.n1) + voff2[J])
 #define DG_ATTN_ISSUE(KT, K0, K1_, V0, V1_)                                                        \
   do {                                                                                             \
     const int kt_ = (KT);                                                                          \
-    K0 = *reinterpret_cast<const uint4*>(DG_K_SRC(tid));                                           \
-    if (KPT > 1) K1_ = *reinterpret_cast<const uint4*>(DG_K_SRC(tid + 512));                       \
-    V0 = *reinterpret_cast<const uint4*>(DG_V_SRC(tid));                                           \
-    if (VPT > 1) V1_ = *reinterpret_cast<const uint4*>(DG_V_SRC(tid + 512));                       \
+    K0 = *reinterpret_cast<const uint4*>(DG_K_SRC(0));                                             \
+    if (KPT > 1) K1_ = *reinterpret_cast<const uint4*>(DG_K_SRC(1));                               \
+    V0 = *reinterpret_cast<const uint4*>(DG_V_SRC(0));                                             \
+    if (VPT > 1) V1_ = *reinterpret_cast<const uint4*>(DG_V_SRC(1));                               \
   } while (0)
 #define DG_K_PUT(BUF, C, V)                                                                        \
   do {                                                                                             \
@@ -107,18 +111,8 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   } while (0)
 #define DG_V_PUT(BUF, KT, C, VV)                                                                   \
   do {                                                                                             \
-    if (VCH % 512 == 0 || (C) < VCH) {                                                             \
-      uint4 v = (VV);                                                                              \
-      const int k0 = (KT) + ((C) & 3) * 8; /* zero the values of keys beyond the valid range */    \
-      if (k0 + 8 > nk) {                                                                           \
-        const int nv = max(0, nk - k0);                                                            \
-        v.x = nv >= 2 ? v.x : (nv == 1 ? (v.x & 0x0000FFFFu) : 0u);                                 \
-        v.y = nv >= 4 ? v.y : (nv == 3 ? (v.y & 0x0000FFFFu) : 0u);                                 \
-        v.z = nv >= 6 ? v.z : (nv == 5 ? (v.z & 0x0000FFFFu) : 0u);                                 \
-        v.w = nv >= 8 ? v.w : (nv == 7 ? (v.w & 0x0000FFFFu) : 0u);                                 \
-      }                                                                                            \
-      *reinterpret_cast<uint4*>(&Vs[BUF][((C) >> 2) * VP + ((C) & 3) * 8]) = v;                    \
-    }                                                                                              \
+    if (VCH % 512 == 0 || (C) < VCH)                                                               \
+      *reinterpret_cast<uint4*>(&Vs[BUF][((C) >> 2) * VP + ((C) & 3) * 8]) = (VV);                  \
   } while (0)
 #define DG_ATTN_STORE(BUF, KT, K0, K1_, V0, V1_)                                                   \
   do {                                                                                             \
@@ -135,9 +129,10 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   const float sl2 = a.scale * 1.4426950408889634f;
 
   // Tile t sits in LDS buffer t & 1; the loads of tiles t+1 and t+2 are in
-  // flight in the two staging sets.  Issues are unconditional with the tile
-  // start clamped to the last tile, so the compiler's wait before each store
-  // only covers the older set.
+  // flight in the two staging sets.  Issues and stores are unconditional (tile
+  // start clamped to the last tile; a store past the end fills a buffer that
+  // is not read again), so the compiler's wait before each store only covers
+  // the older set and nothing waits at the top of the loop.
   const int klast = kbeg + 32 * max(ntile - 1, 0);
 #define DG_ATTN_TILE(BUF, KT)                                                                      \
   do {                                                                                             \
@@ -198,6 +193,10 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
     }                                                                                              \
   } while (0)
 
+  // the Q fragments are complete before the loop, so the compiler's waits
+  // inside it only concern tile loads (otherwise every iteration re-waits on
+  // the Q loads and drains the tile prefetch with them)
+  __builtin_amdgcn_s_waitcnt(0);
   if (ntile > 0) {
     DG_ATTN_ISSUE(kbeg, ka0, ka1, va0, va1);
     DG_ATTN_ISSUE(min(kbeg + 32, klast), kb0, kb1, vb0, vb1);
@@ -209,13 +208,13 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
     // even tile t: buffer 0; set b holds tile t+1; set a takes tile t+2
     DG_ATTN_ISSUE(min(kt + 64, klast), ka0, ka1, va0, va1);
     DG_ATTN_TILE(0, kt);
-    if (t + 1 < ntile) DG_ATTN_STORE(1, kt + 32, kb0, kb1, vb0, vb1);
+    DG_ATTN_STORE(1, kt + 32, kb0, kb1, vb0, vb1);   // past the last tile: a clamped copy nobody reads
     __syncthreads();
     if (t + 1 >= ntile) break;
     // odd tile t+1: buffer 1; set a holds tile t+2; set b takes tile t+3
     DG_ATTN_ISSUE(min(kt + 96, klast), kb0, kb1, vb0, vb1);
     DG_ATTN_TILE(1, kt + 32);
-    if (t + 2 < ntile) DG_ATTN_STORE(0, kt + 64, ka0, ka1, va0, va1);
+    DG_ATTN_STORE(0, kt + 64, ka0, ka1, va0, va1);
     __syncthreads();
   }
 
@@ -246,7 +245,7 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
 hipError_t attention(const AttnArgs& a, hipStream_t s) {
   const int GQ = a.H / a.Hkv;
   if (a.H % a.Hkv != 0 || (GQ != 1 && GQ != 2 && GQ != 4)) return hipErrorInvalidValue;
-  if (a.split_len % 32 != 0 || a.rows_per_batch <= 0 || (a.n2 > 0 && a.n1 % 32 != 0)) return hipErrorInvalidValue;
+  if (a.split_len % 32 != 0 || a.rows_per_batch <= 0 || a.n1 % 32 != 0 || a.n2 % 32 != 0) return hipErrorInvalidValue;
   const int qpw = 128 / GQ;
   const long total = (long)((a.rows_per_batch + qpw - 1) / qpw) * a.Hkv * a.splits * a.B;
   if (total <= 0) return hipSuccess;

@@ -39,10 +39,10 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >
 // activation tile is re-read from L2 for every weight tile, so a wider BW
 // spends fewer DMA and LDS cycles per weight byte.
 template <int EPI, bool ITEMS, int AR, int BW, int NS>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256, NS == 2 ? 3 : 2) void gemm_kernel(GemmArgs g) {
   static_assert(AR == 32 || AR == 64, "activation tile of 32 or 64 rows");
   static_assert(BW == 64 || BW == 128, "weight tile of 64 or 128 rows");
-  static_assert(NS >= 3 && NS <= 6, "ring of 3..6 stages");
+  static_assert(NS >= 2 && NS <= 6, "ring of 2..6 stages");
   constexpr int SE = (AR + BW) * 64;         // stage: AR activation rows then BW weight rows, 64 bf16 each
   constexpr int NG = (AR + BW) / 8;          // 8-row groups per stage (one 1 KB DMA each)
   constexpr int GPW = NG / 4;                // groups per wave
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
   constexpr int WPW = BW / 4;                // weight rows per wave
   constexpr int NBF = WPW / 16;              // weight fragments per wave
   static_assert(NG % 4 == 0, "groups split evenly over 4 waves");
-  static_assert(NS * SE * 2 <= 80 * 1024, "two workgroups per CU");
+  static_assert(NS * SE * 2 <= (NS == 2 ? 53 : 80) * 1024, "two (double-buffered: three) workgroups per CU");
   __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
   __shared__ __attribute__((aligned(1024))) bf16_t S1[SE];
   __shared__ __attribute__((aligned(1024))) bf16_t S2[SE];
@@ -184,12 +184,17 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g) {
 
   if (nst > 0) {
     DG_ISSUE(S0, 0);
-    DG_ISSUE(S1, min(1, nst - 1));
+    if (NS > 2) DG_ISSUE(S1, min(1, nst - 1));
     if (NS > 3) DG_ISSUE(S2, min(2, nst - 1));
     if (NS > 4) DG_ISSUE(S3, min(3, nst - 1));
     if (NS > 5) DG_ISSUE(S4, min(4, nst - 1));
     int s = 0;
-    if (NS == 3) {
+    if (NS == 2) {
+      for (; s + 2 <= nst; s += 2) {
+        DG_ITER(s, S0, S1); DG_ITER(s + 1, S1, S0);
+      }
+      if (s < nst) DG_TAIL(S0);
+    } else if (NS == 3) {
       for (; s + 3 <= nst; s += 3) {
         DG_ITER(s, S0, S2); DG_ITER(s + 1, S1, S0); DG_ITER(s + 2, S2, S1);
       }
@@ -293,6 +298,7 @@ static hipError_t launch(const GemmArgs& a, hipStream_t s) {
     case 644: return launch_v<EPI, ITEMS, 64, 64, 4>(a, s);
     case 645: return launch_v<EPI, ITEMS, 64, 64, 5>(a, s);
     case 1283: return launch_v<EPI, ITEMS, 64, 128, 3>(a, s);
+    case 1282: return launch_v<EPI, ITEMS, 64, 128, 2>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
