@@ -90,11 +90,18 @@ struct AttnArgs {
   const bf16_t* k2; const bf16_t* vt2; long k2_bstride, k2_hstride, v2_bstride, v2_hstride, v2_pitch; int n2;
   int causal; int qpos0;            // causal: query row r (within batch) sits at qpos0 + r
   int splits; int split_len;        // key splits (split_len multiple of 32)
-  float* opart; float* mlpart;      // [splits][B*rows][H][hd], [splits][B*rows][H][2]
+  bf16_t* out;                      // one split: O [B*rows][H][hd] (bf16, normalised)
+  bf16_t* opart; float* mlpart;     // more: per split normalised O [splits][B*rows][H][hd] (bf16)
+                                    // and (running max in log2 units, sum) [splits][B*rows][H][2]
   const int32_t* flag;
 };
 hipError_t attention(const AttnArgs& a, hipStream_t s);
-hipError_t attention_merge(const float* opart, const float* mlpart, int splits, int rows, int H, int hd,
+// attention workgroup shape: attn_waves(hd) waves of attn_frags(hd) row
+// fragments (16 rows) each, i.e. 16 * waves * frags (query, head) rows
+constexpr int attn_waves(int hd) { return hd >= 256 ? 8 : 4; }
+constexpr int attn_frags(int hd) { return hd >= 256 ? 1 : hd >= 128 ? 2 : 4; }
+constexpr int attn_rows_per_wg(int hd) { return 16 * attn_waves(hd) * attn_frags(hd); }
+hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits, int rows, int H, int hd,
                            bf16_t* out, const int32_t* flag, hipStream_t s);
 
 // router logits = sum over split-K partials of the hi rows [0, rows) and lo rows [rows, 2 rows)

@@ -283,7 +283,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.kc = take(R * Hkv * hd * 2);
   p.vc = take(R * Hkv * hd * 2);
   p.rope = take(R * (hd / 2) * 8);
-  p.opart = take((size_t)kMaxSplits * R * H * hd * 4);
+  p.opart = take((size_t)kMaxSplits * R * H * hd * 2);
   p.ml = take((size_t)kMaxSplits * R * H * 2 * 4);
   p.o = take(R * H * hd * 2);
   p.dpart = take((size_t)kMaxDenseSplit * R * D * 4);
@@ -413,7 +413,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   // attention split choice: about one workgroup per CU
   const int GQ = H / Hkv;
   const int nkeys = ps.prefill ? ps.q0 + R : ps.P + ps.per_batch;
-  const int base_wg = cdiv(ps.per_batch, 128 / GQ) * Hkv * ps.B;   // attention workgroups per key split
+  const int base_wg = cdiv(ps.per_batch, attn_rows_per_wg(hd) / GQ) * Hkv * ps.B;   // per key split
   int splits = std::max(1, std::min(p.splits_max, cdiv(256, base_wg)));
   const int split_len = cdiv(cdiv(nkeys, splits), 32) * 32;
   splits = cdiv(nkeys, split_len);
@@ -463,7 +463,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       a.q = q; a.H = H; a.Hkv = Hkv; a.hd = hd; a.scale = 1.0f / sqrtf((float)hd);
       a.rows_per_batch = ps.per_batch; a.B = ps.B;
       a.splits = splits; a.split_len = split_len;
-      a.opart = at<float>(ws, p.opart); a.mlpart = at<float>(ws, p.ml); a.flag = ps.flag;
+      a.out = o; a.opart = at<bf16_t>(ws, p.opart); a.mlpart = at<float>(ws, p.ml); a.flag = ps.flag;
       if (ps.prefill) {
         a.k1 = Kc; a.vt1 = Vc; a.k1_bstride = 0; a.k1_hstride = (long)ps.P_max * hd;
         a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max; a.n1 = ps.q0 + R; a.nb1 = 1;
@@ -484,7 +484,8 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       }
       ProfScope ps_(m, DG_PROF_ATTN, st);
       DG_CK(attention(a, st));
-      DG_CK(attention_merge(at<float>(ws, p.opart), at<float>(ws, p.ml), splits, R, H, hd, o, ps.flag, st));
+      if (splits > 1)
+        DG_CK(attention_merge(at<bf16_t>(ws, p.opart), at<float>(ws, p.ml), splits, R, H, hd, o, ps.flag, st));
     }
     // O projection: split-K partials, summed into the residual by the next norm
     Partials opp{at<float>(ws, p.dpart), 1, (long)R * D};

@@ -5,42 +5,57 @@
 // every canvas key of their own canvas; prefix queries (prefill) see keys at
 // positions <= their own.  Query head h reads key/value head h / (H / Hkv).
 //
-// A workgroup (8 waves) owns 8 row fragments of 16 (query, head) rows that share
-// one key/value head: 16 * 8 / GQ queries times the GQ query heads of that kv
-// head.  Key/value tiles of 32 keys are loaded cooperatively (16-byte loads,
-// clamped and branch-free) into double-buffered LDS; the next tile's loads are
-// in flight while the current one is multiplied.  K rows are padded by 16 bytes
-// and V^T rows (values are cached transposed, [head][dim][position]) by 16 bytes
-// so the MFMA operand reads hit distinct banks.
+// Work split.  A workgroup of NW waves owns 16 NW NF (query, head) rows that
+// share one key/value head: 16 NW NF / GQ queries times the GQ query heads of
+// that kv head, as NW NF row fragments of 16.  Each wave holds NF fragments, so
+// every key / value fragment it reads from LDS feeds NF MFMAs (shapes per
+// head_dim: attn_waves / attn_frags).  Workgroups also split the keys; a merge
+// combines the splits.
 //
-// Each wave computes S^T = K Q^T with keys as the MFMA M dimension, so every
-// lane holds 8 probabilities of ONE query row (keys 4*(l/16)+i and 16+4*(l/16)+i);
-// those 8 values are the A operand of P V when the B operand (from V^T) uses
-// the same 32-key order.  Scores are kept in log2 units.  Each key split writes
-// unnormalised O with its running max / sum; attention_merge combines them.
+// Key / value tiles (32 keys) stream through a 4-deep LDS ring by direct
+// global->LDS DMA: K rows [32][hd] and V^T rows [hd][32 keys], 16-byte slots
+// XOR-swizzled (K: slot ^ (key mod 16); V^T: slot ^ ((dim / 4) mod 4)) so the
+// MFMA operand reads are free of bank conflicts.
+//
+// Each fragment computes S^T = K Q^T with keys as the MFMA M dimension, so a
+// lane holds 8 scores of ONE query row (keys 4*(l/16)+i and 16+4*(l/16)+i);
+// as probabilities those 8 values are the A operand of P V when the B operand
+// (from V^T) uses the same key order.  Scores are in log2 units.  The running
+// max is raised lazily: the accumulator is rescaled only when a row's max
+// grows by more than 8 (probabilities then stay below 2^8), which happens on
+// the first tiles and rarely after.  Outputs: the normalised O of each split
+// in bf16 plus (max, sum) per row, or the final O when there is one split.
 #include <math.h>
 
 #include "dg_kernels.hpp"
 
 namespace dg {
 
-template <int HD>
-__global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
-  constexpr int KP = HD + 8;   // K tile pitch (elements)
-  constexpr int VP = 40;       // V^T tile pitch (elements): 32 keys + pad
-  constexpr int KCH = 32 * HD / 8;   // 16-byte chunks of a K tile
-  constexpr int VCH = HD * 4;        // 16-byte chunks of a V^T tile
-  constexpr int KPT = (KCH + 511) / 512, VPT = (VCH + 511) / 512;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][32 * KP];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][HD * VP];
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int waitcnt_vm_attn(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+template <int HD, int GQ, int NW, int NF>
+__global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
+  constexpr int KS = HD / 32;          // 32-wide contraction steps of S over hd
+  constexpr int NFD = HD / 16;         // 16-wide blocks of O over hd
+  constexpr int CK = HD / 8;           // 16-byte slots per K row
+  constexpr int SWM = CK < 16 ? CK - 1 : 15;
+  constexpr int SE = 64 * HD;          // stage: K [32][HD] then V^T [HD][32], bf16 elements
+  constexpr int IPW = HD / 8 / NW;     // 1 KB DMA instructions per wave per stage
+  constexpr int KI = HD / 16 / NW;     // of which the first KI move K rows
+  static_assert(KI >= 1 && IPW == 2 * KI, "K and V^T tiles split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S2[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S3[SE];
   if (a.flag && *a.flag) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int GQ = a.H / a.Hkv;
-  const int qpw = 128 / GQ;                      // queries per workgroup
+  constexpr int QPW = 16 * NW * NF / GQ;   // queries per workgroup
   const int R = a.rows_per_batch;
-  const int nqb = (R + qpw - 1) / qpw;
+  const int nqb = (R + QPW - 1) / QPW;
   // query blocks fastest: the blocks that read one (kv head, key split) share an XCD
   const long lb = xcd_logical_block((long)nqb * a.Hkv * a.splits * a.B);
   if (lb < 0) return;
@@ -48,16 +63,13 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   const int gy = (int)((lb / nqb) % (a.Hkv * a.splits));
   const int b = (int)(lb / ((long)nqb * a.Hkv * a.splits));
   const int g = gy % a.Hkv, split = gy / a.Hkv;
-  const int q0wg = qb * qpw;
-  const int hq = wave % GQ, qf = wave / GQ;      // this wave's head and query fragment
-  const int h = g * GQ + hq;
-  const int qrow0 = q0wg + qf * 16;
+  const int q0wg = qb * QPW;
   const int lr = lane & 15, lg = lane >> 4;
 
   const int nk = a.n1 + a.n2;
   const int kbeg = split * a.split_len;
   int kend = min(nk, kbeg + a.split_len);
-  if (a.causal) kend = min(kend, a.qpos0 + min(q0wg + qpw, R));
+  if (a.causal) kend = min(kend, a.qpos0 + min(q0wg + QPW, R));
   const int ntile = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
 
   const int b1 = (a.nb1 == 1) ? 0 : b;
@@ -66,194 +78,228 @@ __global__ __launch_bounds__(512, 1) void attn_kernel(AttnArgs a) {
   const bf16_t* K2 = a.k2 ? a.k2 + b * a.k2_bstride + g * a.k2_hstride : K1;
   const bf16_t* V2 = a.vt2 ? a.vt2 + b * a.v2_bstride + g * a.v2_hstride : V1;
 
-  // Q fragments: B operand of S^T (row = lr, hd slots 32 ks + 8 lg)
-  const int myq = min(qrow0 + lr, R - 1);
-  const bf16_t* qp = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
-  constexpr int KS = HD / 32;
-  bf16x8 qfr[KS];
+  // ---- fragments of this wave: f = 4 wave + j -> head g*GQ + f%GQ, queries q0wg + 16 (f/GQ) + lr
+  bf16x8 qfr[NF][KS];
+  int qrow[NF], qpos[NF];
+  bool live[NF];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qfr[ks] = load_bf16x8(qp + 32 * ks);
-  const int qpos = a.qpos0 + myq;
-  const bool wave_live = qrow0 < R;
-
-  // cooperative tile loads (registers -> LDS); at most two 16-byte chunks of
-  // K and two of V^T per thread (hd <= 256), written out slot by slot so the
-  // staging values stay in registers
-  static_assert(KPT <= 2 && VPT <= 2, "tile staging assumes hd <= 256");
-  uint4 ka0, ka1, va0, va1, kb0, kb1, vb0, vb1;   // two staging sets: tiles t+1 and t+2 in flight
-  // Every key count here is a multiple of 32 (prefix lengths, canvases and
-  // prefill chunks are), so a 32-key tile lies wholly in one source and needs
-  // no clamping: its address is a wave-uniform base plus a per-thread offset
-  // fixed for the whole loop.
-  long koff[2], voff1[2], voff2[2];
+  for (int j = 0; j < NF; ++j) {
+    const int f = NF * wave + j;
+    const int h = g * GQ + f % GQ;
+    const int qr0 = q0wg + 16 * (f / GQ);
+    live[j] = qr0 < R;
+    qrow[j] = qr0;
+    const int myq = min(qr0 + lr, R - 1);
+    qpos[j] = a.qpos0 + myq;
+    const bf16_t* qp = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = tid + 512 * j;
-    const int kc = min(c, KCH - 1), vc = min(c, VCH - 1);
-    koff[j] = (long)(kc / (HD / 8)) * HD + (kc % (HD / 8)) * 8;
-    voff1[j] = (long)(vc >> 2) * a.v1_pitch + (vc & 3) * 8;
-    voff2[j] = (long)(vc >> 2) * a.v2_pitch + (vc & 3) * 8;
+    for (int ks = 0; ks < KS; ++ks) qfr[j][ks] = load_bf16x8(qp + 32 * ks);
   }
-#define DG_K_SRC(J) (kt_ < a.n1 ? K1 + (long)kt_ * HD : K2 + (long)(kt_ - a.n1) * HD) + koff[J]
-#define DG_V_SRC(J) (kt_ < a.n1 ? V1 + kt_ + voff1[J] : V2 + (kt_ - a.n1) + voff2[J])
-#define DG_ATTN_ISSUE(KT, K0, K1_, V0, V1_)                                                        \
+
+  // ---- DMA sources: every key count is a multiple of 32, so a tile lies in one
+  // source; per-lane element offsets are fixed for the whole loop
+  // (source 2 differs only in the V^T pitch: dsoff holds the difference, kept
+  // as a value so that choosing the source is a select, not an indexed array)
+  int soff[IPW], dsoff[IPW];
+#pragma unroll
+  for (int j = 0; j < IPW; ++j) {
+    if (j < KI) {
+      constexpr int KPI = 512 / HD;                     // keys per instruction
+      const int key = (wave + NW * j) * KPI + lane / CK;
+      const int c = (lane % CK) ^ (key & SWM);
+      soff[j] = key * HD + c * 8;
+      dsoff[j] = 0;
+    } else {
+      const int row = (wave + NW * (j - KI)) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      soff[j] = row * (int)a.v1_pitch + c * 8;    // < 2^31: pitches are key capacities
+      dsoff[j] = row * (int)(a.v2_pitch - a.v1_pitch);
+    }
+  }
+#define DG_AISSUE(S, KT)                                                                           \
   do {                                                                                             \
     const int kt_ = (KT);                                                                          \
-    K0 = *reinterpret_cast<const uint4*>(DG_K_SRC(0));                                             \
-    if (KPT > 1) K1_ = *reinterpret_cast<const uint4*>(DG_K_SRC(1));                               \
-    V0 = *reinterpret_cast<const uint4*>(DG_V_SRC(0));                                             \
-    if (VPT > 1) V1_ = *reinterpret_cast<const uint4*>(DG_V_SRC(1));                               \
-  } while (0)
-#define DG_K_PUT(BUF, C, V)                                                                        \
-  do {                                                                                             \
-    if (KCH % 512 == 0 || (C) < KCH)                                                               \
-      *reinterpret_cast<uint4*>(&Ks[BUF][((C) / (HD / 8)) * KP + ((C) % (HD / 8)) * 8]) = (V);     \
-  } while (0)
-#define DG_V_PUT(BUF, KT, C, VV)                                                                   \
-  do {                                                                                             \
-    if (VCH % 512 == 0 || (C) < VCH)                                                               \
-      *reinterpret_cast<uint4*>(&Vs[BUF][((C) >> 2) * VP + ((C) & 3) * 8]) = (VV);                  \
-  } while (0)
-#define DG_ATTN_STORE(BUF, KT, K0, K1_, V0, V1_)                                                   \
-  do {                                                                                             \
-    DG_K_PUT(BUF, tid, K0);                                                                        \
-    if (KPT > 1) DG_K_PUT(BUF, tid + 512, K1_);                                                    \
-    DG_V_PUT(BUF, KT, tid, V0);                                                                    \
-    if (VPT > 1) DG_V_PUT(BUF, KT, tid + 512, V1_);                                                \
+    const bool one_ = kt_ < a.n1;                                                                  \
+    const bf16_t* kb_ = one_ ? K1 + (long)kt_ * HD : K2 + (long)(kt_ - a.n1) * HD;                 \
+    const bf16_t* vb_ = one_ ? V1 + kt_ : V2 + (kt_ - a.n1);                                       \
+    _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                              \
+      const bf16_t* src_ = (j < KI ? kb_ : vb_) + (soff[j] + (one_ ? 0 : dsoff[j]));              \
+      const int dst_ = (j < KI ? (wave + NW * j) : 32 * HD / 512 + (wave + NW * (j - KI))) * 512;  \
+      __builtin_amdgcn_global_load_lds((const void*)src_, (lds_void_t*)&S[dst_], 16, 0, 0);        \
+    }                                                                                              \
   } while (0)
 
-  floatx4 O[HD / 16];
+  // LDS read offsets: K fragment (keys kf*16 + lr, slots 4 ks + lg), V^T fragment
+  const int kro = lr * HD;                       // + kf * 16 * HD
+  const int swk = lr & SWM;
+  const int vsw = (lr >> 2) & 3;
+  const int vro0 = 32 * HD + lr * 32 + (((lg >> 1) ^ vsw) << 3) + (lg & 1) * 4;
+  const int vro1 = 32 * HD + lr * 32 + (((2 + (lg >> 1)) ^ vsw) << 3) + (lg & 1) * 4;
+
+  floatx4 O[NF][NFD];
 #pragma unroll
-  for (int nf = 0; nf < HD / 16; ++nf) O[nf] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int j = 0; j < NF; ++j)
+#pragma unroll
+    for (int nf = 0; nf < NFD; ++nf) O[j][nf] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NF], l_run[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
   const float sl2 = a.scale * 1.4426950408889634f;
 
-  // Tile t sits in LDS buffer t & 1; the loads of tiles t+1 and t+2 are in
-  // flight in the two staging sets.  Issues and stores are unconditional (tile
-  // start clamped to the last tile; a store past the end fills a buffer that
-  // is not read again), so the compiler's wait before each store only covers
-  // the older set and nothing waits at the top of the loop.
-  const int klast = kbeg + 32 * max(ntile - 1, 0);
-#define DG_ATTN_TILE(BUF, KT)                                                                      \
+#define DG_ATILE(S, KT)                                                                            \
   do {                                                                                             \
-    const int kt_t_ = (KT);                                                                           \
-    if (wave_live) {                                                                               \
-      floatx4 s[2];                                                                                \
-      _Pragma("unroll") for (int kf = 0; kf < 2; ++kf) {                                           \
-        const bf16_t* kp = &Ks[BUF][(kf * 16 + lr) * KP + lg * 8];                                 \
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};                                                        \
-        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(load_bf16x8(kp + 32 * ks), qfr[ks], acc); \
-        s[kf] = acc;                                                                               \
+    const int kt = (KT);                                                                           \
+    floatx4 s[NF][2];                                                                              \
+    _Pragma("unroll") for (int j = 0; j < NF; ++j) s[j][0] = s[j][1] = floatx4{0.f, 0.f, 0.f, 0.f}; \
+    _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                               \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                          \
+        const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&S[kf * 16 * HD + kro + (((4 * ks + lg) ^ swk) << 3)]); \
+        _Pragma("unroll") for (int j = 0; j < NF; ++j)                                             \
+          s[j][kf] = mfma16x16x32(kfr, qfr[j][ks], s[j][kf]);                                      \
       }                                                                                            \
+    bf16x8 pf[NF];                                                                                 \
+    _Pragma("unroll") for (int j = 0; j < NF; ++j) {                                               \
       float p[8];                                                                                  \
       float mx = -INFINITY;                                                                        \
       _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                             \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-          const int key = kt_t_ + kf * 16 + lg * 4 + i;                                               \
-          const bool ok = key < kend && (!a.causal || key <= qpos);                                \
-          const float v = ok ? s[kf][i] * sl2 : -INFINITY;                                         \
+          const int key = kt + kf * 16 + lg * 4 + i;                                               \
+          const bool ok = key < kend && (!a.causal || key <= qpos[j]);                             \
+          const float v = ok ? s[j][kf][i] * sl2 : -INFINITY;                                      \
           p[kf * 4 + i] = v;                                                                       \
           mx = fmaxf(mx, v);                                                                       \
         }                                                                                          \
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));                                                      \
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                      \
-      const float m_new = fmaxf(m_run, mx);                                                        \
-      const bool live = m_new != -INFINITY;                                                        \
-      const float alpha = live ? exp2f(m_run - m_new) : 1.0f;                                      \
+      /* raise the running max only when it grows by more than 8 (log2 units) */                   \
+      const bool up = mx > m_run[j] + 8.0f;                                                        \
+      if (__builtin_amdgcn_ballot_w64(up)) {                                                       \
+        const float m_new = fmaxf(m_run[j], mx);                                                   \
+        const float alpha = (m_run[j] == -INFINITY) ? 0.f : exp2f(m_run[j] - m_new);               \
+        l_run[j] *= alpha;                                                                         \
+        m_run[j] = m_new;                                                                          \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
+          const float ai = __shfl(alpha, lg * 4 + i, 64);                                          \
+          _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) O[j][nf][i] *= ai;                    \
+        }                                                                                          \
+      }                                                                                            \
+      const bool any_ = m_run[j] != -INFINITY;                                                     \
       float ps = 0.f;                                                                              \
       _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                              \
-        p[e] = live ? exp2f(p[e] - m_new) : 0.f;                                                   \
+        p[e] = any_ ? exp2f(p[e] - m_run[j]) : 0.f;                                                \
         ps += p[e];                                                                                \
       }                                                                                            \
       ps += __shfl_xor(ps, 16, 64);                                                                \
       ps += __shfl_xor(ps, 32, 64);                                                                \
-      l_run = l_run * alpha + ps;                                                                  \
-      m_run = m_new;                                                                               \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                              \
-        const float ai = __shfl(alpha, lg * 4 + i, 64);                                            \
-        _Pragma("unroll") for (int nf = 0; nf < HD / 16; ++nf) O[nf][i] *= ai;                     \
-      }                                                                                            \
-      bf16x8 pf;                                                                                   \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];                          \
-      _Pragma("unroll") for (int nf = 0; nf < HD / 16; ++nf) {                                     \
-        const bf16_t* vp = &Vs[BUF][(nf * 16 + lr) * VP + lg * 4];                                 \
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);                                      \
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);                                 \
-        bf16x8 vb;                                                                                 \
-        vb[0] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x & 0xFFFF));                             \
-        vb[1] = __builtin_bit_cast(__bf16, (uint16_t)(lo.x >> 16));                                \
-        vb[2] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y & 0xFFFF));                             \
-        vb[3] = __builtin_bit_cast(__bf16, (uint16_t)(lo.y >> 16));                                \
-        vb[4] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x & 0xFFFF));                             \
-        vb[5] = __builtin_bit_cast(__bf16, (uint16_t)(hi.x >> 16));                                \
-        vb[6] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y & 0xFFFF));                             \
-        vb[7] = __builtin_bit_cast(__bf16, (uint16_t)(hi.y >> 16));                                \
-        O[nf] = mfma16x16x32(pf, vb, O[nf]);                                                       \
-      }                                                                                            \
+      l_run[j] += ps;                                                                              \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[j][e] = (__bf16)p[e];                       \
+    }                                                                                              \
+    _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) {                                           \
+      const uint2 lo_ = *reinterpret_cast<const uint2*>(&S[vro0 + nf * 16 * 32]);                  \
+      const uint2 hi_ = *reinterpret_cast<const uint2*>(&S[vro1 + nf * 16 * 32]);                  \
+      const uint4 w_ = make_uint4(lo_.x, lo_.y, hi_.x, hi_.y);                                     \
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, w_);                                            \
+      _Pragma("unroll") for (int j = 0; j < NF; ++j) O[j][nf] = mfma16x16x32(pf[j], vb, O[j][nf]); \
     }                                                                                              \
   } while (0)
 
-  // the Q fragments are complete before the loop, so the compiler's waits
-  // inside it only concern tile loads (otherwise every iteration re-waits on
-  // the Q loads and drains the tile prefetch with them)
-  __builtin_amdgcn_s_waitcnt(0);
-  if (ntile > 0) {
-    DG_ATTN_ISSUE(kbeg, ka0, ka1, va0, va1);
-    DG_ATTN_ISSUE(min(kbeg + 32, klast), kb0, kb1, vb0, vb1);
-    DG_ATTN_STORE(0, kbeg, ka0, ka1, va0, va1);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntile; t += 2) {
-    const int kt = kbeg + 32 * t;
-    // even tile t: buffer 0; set b holds tile t+1; set a takes tile t+2
-    DG_ATTN_ISSUE(min(kt + 64, klast), ka0, ka1, va0, va1);
-    DG_ATTN_TILE(0, kt);
-    DG_ATTN_STORE(1, kt + 32, kb0, kb1, vb0, vb1);   // past the last tile: a clamped copy nobody reads
-    __syncthreads();
-    if (t + 1 >= ntile) break;
-    // odd tile t+1: buffer 1; set a holds tile t+2; set b takes tile t+3
-    DG_ATTN_ISSUE(min(kt + 96, klast), kb0, kb1, vb0, vb1);
-    DG_ATTN_TILE(1, kt + 32);
-    DG_ATTN_STORE(0, kt + 64, ka0, ka1, va0, va1);
-    __syncthreads();
-  }
+  // Ring of 4: when tile t is read, tiles t+1 and t+2 may still be in flight.
+  // All LDS reads of tile t precede the DMA of tile t+3 (start clamped to the
+  // last tile, so every iteration issues the same count), which goes to the
+  // buffer of tile t-1, free once every wave passed this iteration's barrier;
+  // with the reads first the compiler adds no wait of its own.
+#define DG_AITER(T, CUR, NXT)                                                                      \
+  do {                                                                                             \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_attn(2 * IPW));                                          \
+    __builtin_amdgcn_s_barrier();                                                                  \
+    DG_ATILE(CUR, kbeg + 32 * (T));                                                                \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
+    DG_AISSUE(NXT, kbeg + 32 * min((T) + 3, ntile - 1));                                           \
+    __builtin_amdgcn_sched_barrier(0);                                                             \
+  } while (0)
 
-#undef DG_ATTN_ISSUE
-#undef DG_ATTN_TILE
-#undef DG_ATTN_STORE
-#undef DG_K_SRC
-#undef DG_V_SRC
-#undef DG_K_PUT
-#undef DG_V_PUT
-  if (!wave_live) return;
+  __builtin_amdgcn_s_waitcnt(0);   // Q fragments in registers before the ring starts
+  if (ntile > 0) {
+    DG_AISSUE(S0, kbeg);
+    DG_AISSUE(S1, kbeg + 32 * min(1, ntile - 1));
+    DG_AISSUE(S2, kbeg + 32 * min(2, ntile - 1));
+    for (int t = 0; t < ntile; t += 4) {
+      DG_AITER(t, S0, S3);
+      if (t + 1 >= ntile) break;
+      DG_AITER(t + 1, S1, S0);
+      if (t + 2 >= ntile) break;
+      DG_AITER(t + 2, S2, S1);
+      if (t + 3 >= ntile) break;
+      DG_AITER(t + 3, S3, S2);
+    }
+  }
+#undef DG_AITER
+#undef DG_ATILE
+#undef DG_AISSUE
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- outputs: normalised O (bf16) of this split, and (max, sum) per row
   const long BR = (long)a.B * R;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = qrow0 + lg * 4 + i;
-    if (row >= R) continue;
-    float* op = a.opart + (((long)split * BR + (long)b * R + row) * a.H + h) * HD;
+  for (int j = 0; j < NF; ++j) {
+    if (!live[j]) continue;
+    const int h = g * GQ + (NF * wave + j) % GQ;
+    const float inv = l_run[j] > 0.f ? 1.0f / l_run[j] : 0.f;
 #pragma unroll
-    for (int nf = 0; nf < HD / 16; ++nf) op[nf * 16 + lr] = O[nf][i];
+    for (int i = 0; i < 4; ++i) {
+      const int row = qrow[j] + lg * 4 + i;
+      const float iv = __shfl(inv, lg * 4 + i, 64);
+      if (row >= R) continue;
+      bf16_t* op = (a.splits == 1 ? a.out + ((long)b * R + row) * a.H * HD
+                                  : a.opart + (((long)split * BR + (long)b * R + row) * a.H) * HD) + (long)h * HD;
+#pragma unroll
+      for (int nf = 0; nf < NFD; ++nf) op[nf * 16 + lr] = f2bf(O[j][nf][i] * iv);
+    }
+    if (a.splits > 1 && lg == 0 && qrow[j] + lr < R) {
+      float* mp = a.mlpart + (((long)split * BR + (long)b * R + qrow[j] + lr) * a.H + h) * 2;
+      mp[0] = m_run[j];
+      mp[1] = l_run[j];
+    }
   }
-  if (lg == 0 && qrow0 + lr < R) {
-    float* mp = a.mlpart + (((long)split * BR + (long)b * R + qrow0 + lr) * a.H + h) * 2;
-    mp[0] = m_run;
-    mp[1] = l_run;
-  }
+}
+
+template <int HD, int GQ, int NW, int NF>
+static void attn_launch(const AttnArgs& a, hipStream_t s) {
+  const long total = (long)((a.rows_per_batch + 16 * NW * NF / GQ - 1) / (16 * NW * NF / GQ)) * a.Hkv * a.splits * a.B;
+  if (total <= 0) return;
+  hipLaunchKernelGGL((attn_kernel<HD, GQ, NW, NF>), dim3(xcd_grid(total)), dim3(64 * NW), 0, s, a);
+}
+
+// Workgroup shapes (waves x fragments per wave), measured on the 2816-wide
+// model: at head_dim 256 eight waves of one fragment (two waves per SIMD, so
+// one wave's softmax overlaps the other's MFMAs) beat four waves of two, whose
+// halved LDS traffic does not pay for the lost overlap; smaller heads fit
+// four fragments per wave.
+template <int HD, int GQ>
+static void attn_shape(const AttnArgs& a, hipStream_t s) {
+  constexpr int NW = attn_waves(HD), NF = attn_frags(HD);
+  attn_launch<HD, GQ, NW, NF>(a, s);
 }
 
 hipError_t attention(const AttnArgs& a, hipStream_t s) {
   const int GQ = a.H / a.Hkv;
   if (a.H % a.Hkv != 0 || (GQ != 1 && GQ != 2 && GQ != 4)) return hipErrorInvalidValue;
   if (a.split_len % 32 != 0 || a.rows_per_batch <= 0 || a.n1 % 32 != 0 || a.n2 % 32 != 0) return hipErrorInvalidValue;
-  const int qpw = 128 / GQ;
-  const long total = (long)((a.rows_per_batch + qpw - 1) / qpw) * a.Hkv * a.splits * a.B;
-  if (total <= 0) return hipSuccess;
-  const dim3 grid(xcd_grid(total));
-  switch (a.hd) {
-    case 64: hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(512), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(512), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(attn_kernel<256>, grid, dim3(512), 0, s, a); break;
+  if (a.splits < 1 || (a.splits == 1 && !a.out) || (a.splits > 1 && (!a.opart || !a.mlpart)))
+    return hipErrorInvalidValue;
+  switch (a.hd * 10 + GQ) {
+    case 641: attn_shape<64, 1>(a, s); break;
+    case 642: attn_shape<64, 2>(a, s); break;
+    case 644: attn_shape<64, 4>(a, s); break;
+    case 1281: attn_shape<128, 1>(a, s); break;
+    case 1282: attn_shape<128, 2>(a, s); break;
+    case 1284: attn_shape<128, 4>(a, s); break;
+    case 2561: attn_shape<256, 1>(a, s); break;
+    case 2562: attn_shape<256, 2>(a, s); break;
+    case 2564: attn_shape<256, 4>(a, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

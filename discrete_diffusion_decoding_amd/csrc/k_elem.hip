@@ -263,7 +263,7 @@ hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
 // the split weights 2^(m_s - M) / L of every head are formed once in LDS, then
 // each thread sums its float4 columns over the splits.
 template <int NSP>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const float* ml, int rows, int H, int hd,
+__global__ __launch_bounds__(256) void attn_merge_kernel(const bf16_t* op, const float* ml, int rows, int H, int hd,
                                                          bf16_t* out, const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ float wts[64 * NSP];
@@ -279,11 +279,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const 
       lv[s] = ml[(s * srow + base) * 2 + 1];
       M = fmaxf(M, mv[s]);
     }
+    // split s holds O_s / l_s; its weight in the merged softmax is l_s 2^(m_s - M) / L
     float L = 0.f;
 #pragma unroll
     for (int s = 0; s < NSP; ++s) {
-      mv[s] = (mv[s] == -INFINITY) ? 0.f : exp2f(mv[s] - M);
-      L += mv[s] * lv[s];
+      mv[s] = (mv[s] == -INFINITY) ? 0.f : exp2f(mv[s] - M) * lv[s];
+      L += mv[s];
     }
     const float il = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const 
     const int h = (4 * i4) / hd;
     float4 vals[NSP];
 #pragma unroll
-    for (int s = 0; s < NSP; ++s) vals[s] = reinterpret_cast<const float4*>(op + s * sstride + rowoff)[i4];
+    for (int s = 0; s < NSP; ++s) vals[s] = load_bf16x4(op + s * sstride + rowoff + 4 * i4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int s = 0; s < NSP; ++s) acc = f4fma(wts[h * NSP + s], vals[s], acc);
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* op, const 
   }
 }
 
-hipError_t attention_merge(const float* opart, const float* mlpart, int splits, int rows, int H, int hd,
+hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits, int rows, int H, int hd,
                            bf16_t* out, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (H > 64 || hd % 4) return hipErrorInvalidValue;
