@@ -14,17 +14,21 @@
 //
 // Key / value tiles (32 keys) stream through a 4-deep LDS ring by direct
 // global->LDS DMA: K rows [32][hd] and V^T rows [hd][32 keys], 16-byte slots
-// XOR-swizzled (K: slot ^ (key mod 16); V^T: slot ^ ((dim / 4) mod 4)) so the
-// MFMA operand reads are free of bank conflicts.
+// XOR-swizzled (K: slot ^ kswz(key), V^T: slot ^ vswz(dim)) so that every 8
+// and every 16 lanes of an MFMA operand read hit distinct banks.
 //
-// Each fragment computes S^T = K Q^T with keys as the MFMA M dimension, so a
-// lane holds 8 scores of ONE query row (keys 4*(l/16)+i and 16+4*(l/16)+i);
-// as probabilities those 8 values are the A operand of P V when the B operand
-// (from V^T) uses the same key order.  Scores are in log2 units.  The running
-// max is raised lazily: the accumulator is rescaled only when a row's max
-// grows by more than 8 (probabilities then stay below 2^8), which happens on
-// the first tiles and rarely after.  Outputs: the normalised O of each split
-// in bf16 plus (max, sum) per row, or the final O when there is one split.
+// Each fragment computes S^T = K Q^T with keys as the MFMA M dimension.  The
+// K fragment of block kf reads key row 8 (r / 4) + 4 kf + r % 4 for MFMA row
+// r, so a lane ends up with the 8 consecutive keys 8 (l / 16) .. + 7 of ONE
+// query row: as bf16 probabilities they are the A operand of P V, and the B
+// operand is one 16-byte read of a V^T row.  Scores are scaled to log2 units
+// inside the exponent.  The running max is raised lazily: the accumulator is
+// rescaled only when a row's max grows by more than 8 (probabilities then stay
+// below 2^8), which happens on the first tiles and rarely after.  Only tiles
+// that cross the causal diagonal or the end of the keys are masked.  Each lane
+// keeps a partial row sum of its own keys; the four partials of a row are
+// added once at the end.  Outputs: the normalised O of each split in bf16
+// plus (max, sum) per row, or the final O when there is one split.
 #include <math.h>
 
 #include "dg_kernels.hpp"
@@ -35,12 +39,31 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int waitcnt_vm_attn(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
+// slot swizzles: K row `key` (0..31 in the tile) of a head_dim with ck 16-byte
+// slots, and V^T row `dim`
+__device__ __forceinline__ int kswz(int key, int ck) { return ((key & 3) | ((key >> 1) & 12)) & (ck - 1); }
+__device__ __forceinline__ int vswz(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
+
+// sum / max over the four lanes l % 16 + 16 i of a wave (gfx950 row swaps)
+__device__ __forceinline__ float xrow_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 template <int HD, int GQ, int NW, int NF>
 __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
   constexpr int KS = HD / 32;          // 32-wide contraction steps of S over hd
   constexpr int NFD = HD / 16;         // 16-wide blocks of O over hd
   constexpr int CK = HD / 8;           // 16-byte slots per K row
-  constexpr int SWM = CK < 16 ? CK - 1 : 15;
+  constexpr int KSB = KS < 4 ? KS : 4;  // distinct K read offsets per block (swizzle period 16 slots)
   constexpr int SE = 64 * HD;          // stage: K [32][HD] then V^T [HD][32], bf16 elements
   constexpr int IPW = HD / 8 / NW;     // 1 KB DMA instructions per wave per stage
   constexpr int KI = HD / 16 / NW;     // of which the first KI move K rows
@@ -106,12 +129,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     if (j < KI) {
       constexpr int KPI = 512 / HD;                     // keys per instruction
       const int key = (wave + NW * j) * KPI + lane / CK;
-      const int c = (lane % CK) ^ (key & SWM);
+      const int c = (lane % CK) ^ kswz(key, CK);
       soff[j] = key * HD + c * 8;
       dsoff[j] = 0;
     } else {
       const int row = (wave + NW * (j - KI)) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int c = (lane & 3) ^ vswz(row);
       soff[j] = row * (int)a.v1_pitch + c * 8;    // < 2^31: pitches are key capacities
       dsoff[j] = row * (int)(a.v2_pitch - a.v1_pitch);
     }
@@ -129,25 +152,35 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     }                                                                                              \
   } while (0)
 
-  // LDS read offsets: K fragment (keys kf*16 + lr, slots 4 ks + lg), V^T fragment
-  const int kro = lr * HD;                       // + kf * 16 * HD
-  const int swk = lr & SWM;
-  const int vsw = (lr >> 2) & 3;
-  const int vro0 = 32 * HD + lr * 32 + (((lg >> 1) ^ vsw) << 3) + (lg & 1) * 4;
-  const int vro1 = 32 * HD + lr * 32 + (((2 + (lg >> 1)) ^ vsw) << 3) + (lg & 1) * 4;
+  // LDS read offsets.  K block kf, step ks: key row kr = 8 (lr / 4) + 4 kf +
+  // lr % 4, global slot 4 ks + lg at LDS slot (4 ks + lg) ^ kswz(kr), i.e.
+  // koff[kf][ks % 4] + 128 (ks / 4) elements.  V^T block nf: row 16 nf + lr,
+  // slot lg, i.e. voff[nf % 2] + 512 nf.
+  int koff[2][KSB];
+#pragma unroll
+  for (int kf = 0; kf < 2; ++kf) {
+    const int kr = 8 * (lr >> 2) + 4 * kf + (lr & 3);
+#pragma unroll
+    for (int q = 0; q < KSB; ++q) koff[kf][q] = kr * HD + (((4 * q + lg) ^ kswz(kr, CK)) << 3);
+  }
+  int voff[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) voff[e] = 32 * HD + lr * 32 + ((lg ^ vswz(16 * e + lr)) << 3);
 
   floatx4 O[NF][NFD];
 #pragma unroll
   for (int j = 0; j < NF; ++j)
 #pragma unroll
     for (int nf = 0; nf < NFD; ++nf) O[j][nf] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[NF], l_run[NF];
+  float m_run[NF], l_run[NF];   // l_run: this lane's partial sum until the end
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     m_run[j] = -INFINITY;
     l_run[j] = 0.f;
   }
   const float sl2 = a.scale * 1.4426950408889634f;
+  // keys below this bound are visible to every query of the workgroup
+  const int kfull = a.causal ? min(kend, a.qpos0 + q0wg + 1) : kend;
 
 #define DG_ATILE(S, KT)                                                                            \
   do {                                                                                             \
@@ -156,29 +189,28 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     _Pragma("unroll") for (int j = 0; j < NF; ++j) s[j][0] = s[j][1] = floatx4{0.f, 0.f, 0.f, 0.f}; \
     _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                               \
       _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                          \
-        const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&S[kf * 16 * HD + kro + (((4 * ks + lg) ^ swk) << 3)]); \
+        const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&S[koff[kf][ks % KSB] + 128 * (ks / KSB)]); \
         _Pragma("unroll") for (int j = 0; j < NF; ++j)                                             \
           s[j][kf] = mfma16x16x32(kfr, qfr[j][ks], s[j][kf]);                                      \
       }                                                                                            \
+    const bool masked_ = kt + 32 > kfull;                                                          \
     bf16x8 pf[NF];                                                                                 \
     _Pragma("unroll") for (int j = 0; j < NF; ++j) {                                               \
       float p[8];                                                                                  \
-      float mx = -INFINITY;                                                                        \
-      _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                             \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
-          const int key = kt + kf * 16 + lg * 4 + i;                                               \
-          const bool ok = key < kend && (!a.causal || key <= qpos[j]);                             \
-          const float v = ok ? s[j][kf][i] * sl2 : -INFINITY;                                      \
-          p[kf * 4 + i] = v;                                                                       \
-          mx = fmaxf(mx, v);                                                                       \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) p[e] = s[j][e >> 2][e & 3];                    \
+      if (masked_) {                                                                               \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                            \
+          const int key = kt + 8 * lg + e;                                                         \
+          if (!(key < kend && (!a.causal || key <= qpos[j]))) p[e] = -INFINITY;                    \
         }                                                                                          \
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));                                                      \
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));                                                      \
+      }                                                                                            \
+      float mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7]))); \
+      mx = xrow_max(mx) * sl2;                                                                     \
       /* raise the running max only when it grows by more than 8 (log2 units) */                   \
       const bool up = mx > m_run[j] + 8.0f;                                                        \
       if (__builtin_amdgcn_ballot_w64(up)) {                                                       \
         const float m_new = fmaxf(m_run[j], mx);                                                   \
-        const float alpha = (m_run[j] == -INFINITY) ? 0.f : exp2f(m_run[j] - m_new);               \
+        const float alpha = (m_run[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[j] - m_new); \
         l_run[j] *= alpha;                                                                         \
         m_run[j] = m_new;                                                                          \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                            \
@@ -186,22 +218,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
           _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) O[j][nf][i] *= ai;                    \
         }                                                                                          \
       }                                                                                            \
-      const bool any_ = m_run[j] != -INFINITY;                                                     \
-      float ps = 0.f;                                                                              \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                              \
-        p[e] = any_ ? exp2f(p[e] - m_run[j]) : 0.f;                                                \
-        ps += p[e];                                                                                \
+      const float nm_ = -m_run[j];                                                                 \
+      if (masked_) {                                                                               \
+        const bool any_ = m_run[j] != -INFINITY;                                                   \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e)                                              \
+          p[e] = any_ ? __builtin_amdgcn_exp2f(fmaf(p[e], sl2, nm_)) : 0.f;                        \
+      } else {                                                                                     \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(p[e], sl2, nm_)); \
       }                                                                                            \
-      ps += __shfl_xor(ps, 16, 64);                                                                \
-      ps += __shfl_xor(ps, 32, 64);                                                                \
-      l_run[j] += ps;                                                                              \
+      l_run[j] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));               \
       _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[j][e] = (__bf16)p[e];                       \
     }                                                                                              \
     _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) {                                           \
-      const uint2 lo_ = *reinterpret_cast<const uint2*>(&S[vro0 + nf * 16 * 32]);                  \
-      const uint2 hi_ = *reinterpret_cast<const uint2*>(&S[vro1 + nf * 16 * 32]);                  \
-      const uint4 w_ = make_uint4(lo_.x, lo_.y, hi_.x, hi_.y);                                     \
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, w_);                                            \
+      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&S[voff[nf & 1] + 512 * nf]);             \
       _Pragma("unroll") for (int j = 0; j < NF; ++j) O[j][nf] = mfma16x16x32(pf[j], vb, O[j][nf]); \
     }                                                                                              \
   } while (0)
@@ -243,6 +272,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
 
   // ---- outputs: normalised O (bf16) of this split, and (max, sum) per row
   const long BR = (long)a.B * R;
+#pragma unroll
+  for (int j = 0; j < NF; ++j) l_run[j] = xrow_sum(l_run[j]);
 #pragma unroll
   for (int j = 0; j < NF; ++j) {
     if (!live[j]) continue;

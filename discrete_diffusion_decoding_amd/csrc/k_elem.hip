@@ -162,11 +162,9 @@ hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta,
 // e +- hd/2, i.e. slot j +- hd/128 of the same lane when hd >= 128, or lane
 // l ^ (hd/2) when hd == 64.
 template <int HD>
-__global__ __launch_bounds__(256) void qk_rope_kernel(QkRopeArgs a) {
-  if (a.flag && *a.flag) return;
+__device__ __forceinline__ void qk_rope_row(const QkRopeArgs& a, int r) {
   constexpr int HALF = HD / 2;
   constexpr int NS = HD / 64;
-  const int r = blockIdx.x;
   const int tloc = r % a.per_batch, bidx = r / a.per_batch;
   const float2* tab = a.rope + (long)tloc * HALF;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -210,11 +208,8 @@ __global__ __launch_bounds__(256) void qk_rope_kernel(QkRopeArgs a) {
 // LDS so that every row of V^T (one dimension, 32 consecutive positions) is
 // written as one contiguous 64-byte run.
 template <int HD>
-__global__ __launch_bounds__(256) void vt_scatter_kernel(QkRopeArgs a) {
-  if (a.flag && *a.flag) return;
-  __shared__ bf16_t tile[32][HD + 2];
-  const int g = blockIdx.y;
-  const int t0 = blockIdx.x * 32;               // first row of the tile (rows of one batch element)
+__device__ __forceinline__ void vt_scatter_tile(const QkRopeArgs& a, int g, int t0, bf16_t (*tile)[HD + 2]) {
+  // t0: first row of the tile (rows of one batch element)
   const int qkvd = (a.H + 2 * a.Hkv) * HD;
   for (int i = threadIdx.x; i < 32 * HD; i += 256) {
     const int tr = i / HD, e = i % HD;
@@ -236,23 +231,30 @@ __global__ __launch_bounds__(256) void vt_scatter_kernel(QkRopeArgs a) {
   }
 }
 
+// one launch: blocks [0, rows) normalise and rotate the q / k heads of a row,
+// the blocks after them scatter V^T tiles of 32 rows x one kv head
+template <int HD>
+__global__ __launch_bounds__(256) void qk_rope_kernel(QkRopeArgs a) {
+  if (a.flag && *a.flag) return;
+  __shared__ bf16_t tile[32][HD + 2];
+  const int bx = blockIdx.x;
+  if (bx < a.rows) {
+    qk_rope_row<HD>(a, bx);
+  } else {
+    const int nt = (a.rows + 31) / 32;
+    const int v = bx - a.rows;
+    vt_scatter_tile<HD>(a, v / nt, (v % nt) * 32, tile);
+  }
+}
+
 hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.per_batch % 32 != 0 && a.per_batch != a.rows) return hipErrorInvalidValue;
-  dim3 vg((a.rows + 31) / 32, a.Hkv);
+  const dim3 grid(a.rows + ((a.rows + 31) / 32) * a.Hkv);
   switch (a.hd) {
-    case 64:
-      hipLaunchKernelGGL(qk_rope_kernel<64>, dim3(a.rows), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(vt_scatter_kernel<64>, vg, dim3(256), 0, s, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(qk_rope_kernel<128>, dim3(a.rows), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(vt_scatter_kernel<128>, vg, dim3(256), 0, s, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL(qk_rope_kernel<256>, dim3(a.rows), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(vt_scatter_kernel<256>, vg, dim3(256), 0, s, a);
-      break;
+    case 64: hipLaunchKernelGGL(qk_rope_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(qk_rope_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(qk_rope_kernel<256>, grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -325,81 +327,99 @@ hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits,
 }
 
 // ---------------------------------------------------------------------------
-// Router: logits = hi-part + lo-part products (an fp32-accurate product from two
-// bf16 MFMA passes) summed over split-K partials; top-k by rank: the rank of
-// expert e is the number of experts that order before it (larger logit, or an
-// equal logit and a lower index), so the k experts of rank < k are the top-k in
-// the order of repeated argmax with ties to the lower index.  Gates = softmax
-// over the k selected logits.  One wave per token row; every lane ranks its
-// experts against all logits of the row, read back from LDS as broadcasts.
+// Router top-k: logits = hi-part + lo-part products (an fp32-accurate product
+// from two bf16 MFMA passes) summed over the split-K partials, the k largest (ties to the lower expert index, as a stable sort of the
+// negated logits), gates = softmax over the k selected logits.  One wave per
+// token row: each lane holds experts lane + 64 j as 64-bit keys (order-
+// preserving bits of the logit, then the complemented index), and k rounds of
+// a wave-wide maximum pick the experts in order.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFF - e);
+}
+__device__ __forceinline__ float topk_key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t umax64_dpp(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint32_t lo2 = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xF, 0xF, false);
+  const uint32_t hi2 = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xF, 0xF, false);
+  const uint64_t y = ((uint64_t)hi2 << 32) | lo2;
+  return x > y ? x : y;
+}
+template <bool W32>
+__device__ __forceinline__ uint64_t umax64_swap(uint64_t x) {
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  auto l = W32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false) : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto h = W32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false) : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  const uint64_t a = ((uint64_t)h[0] << 32) | l[0], b = ((uint64_t)h[1] << 32) | l[1];
+  return a > b ? a : b;
+}
+// maximum over the wave, in every lane: lane pairs (xor 1, xor 2), mirrored
+// halves of 8 and 16 lanes, then the row swaps of 16 and 32 lanes
+__device__ __forceinline__ uint64_t wave_umax64(uint64_t x) {
+  x = umax64_dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  x = umax64_dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  x = umax64_dpp<0x141>(x);   // row_half_mirror
+  x = umax64_dpp<0x140>(x);   // row_mirror
+  x = umax64_swap<false>(x);
+  return umax64_swap<true>(x);
+}
+
 template <int NS, int NK>
-__global__ __launch_bounds__(256) void topk_kernel(Partials rl, int rows, int E, int32_t* idx, float* gate,
-                                                   int32_t* idx_dump, float* gate_dump, const int32_t* flag) {
+__global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, int32_t* idx, float* gate,
+                                                  int32_t* idx_dump, float* gate_dump, const int32_t* flag) {
   if (flag && *flag) return;
-  __shared__ __attribute__((aligned(16))) float lv_s[4][256];
-  __shared__ float sel_v[4][NK];
-  __shared__ int sel_i[4][NK];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r = min((int)blockIdx.x * 4 + w, rows - 1);   // surplus waves redo the last row, store nothing
-  const bool store = (int)blockIdx.x * 4 + w < rows;
-  float hv[4][NS], lo[4][NS];
+  const int lane = threadIdx.x;
+  const int r = blockIdx.x;
+  uint64_t key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int e = min(lane + 64 * j, E - 1);
+    key[j] = 0;
+    if (64 * j < E) {   // uniform over the wave
+      const int e = lane + 64 * j;
+      if (e < E) {
+        float h = 0.f, l = 0.f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      hv[j][s] = rl.p[s * rl.stride + (long)r * E + e];
-      lo[j][s] = rl.p[s * rl.stride + (long)(rows + r) * E + e];
-    }
-  }
-  float v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float h = 0.f, l = 0.f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      h += hv[j][s];
-      l += lo[j][s];
-    }
-    v[j] = h + l;
-    lv_s[w][lane + 64 * j] = (lane + 64 * j < E) ? v[j] : -INFINITY;
-  }
-  __syncthreads();
-  int rank[4] = {0, 0, 0, 0};
-  const float4* row4 = reinterpret_cast<const float4*>(lv_s[w]);
-  const int E4 = (E + 3) >> 2;
-  for (int q = 0; q < E4; ++q) {
-    const float4 o = row4[q];
-    const float ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int eo = 4 * q + t;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        rank[j] += (ov[t] > v[j] || (ov[t] == v[j] && eo < e)) ? 1 : 0;
+        for (int s = 0; s < NS; ++s) {
+          h += rl.p[s * rl.stride + (long)r * E + e];
+          l += rl.p[s * rl.stride + (long)(rows + r) * E + e];
+        }
+        key[j] = topk_key(h + l, e);
       }
     }
   }
+  float mine_v = 0.f, top_v = 0.f;
+  int mine_e = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = lane + 64 * j;
-    if (e < E && rank[j] < NK) {
-      sel_v[w][rank[j]] = v[j];
-      sel_i[w][rank[j]] = e;
+  for (int t = 0; t < NK; ++t) {
+    const uint64_t best = wave_umax64(max(max(key[0], key[1]), max(key[2], key[3])));
+    const int e = 0xFFFF - (int)(best & 0xFFFF);
+    const float v = topk_key_value(best);
+    if (t == 0) top_v = v;
+    if (lane == t) {
+      mine_v = v;
+      mine_e = e;
+    }
+    if ((e & 63) == lane) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if ((e >> 6) == j) key[j] = 0;
     }
   }
-  __syncthreads();
-  if (lane < NK && store) {
-    const float m = sel_v[w][0];
-    float den = 0.f;
+  // softmax over the selected logits (lane t holds selection t)
+  float ex = lane < NK ? expf(mine_v - top_v) : 0.f;
+  float den = ex;
 #pragma unroll
-    for (int t = 0; t < NK; ++t) den += expf(sel_v[w][t] - m);
-    const float gt = expf(sel_v[w][lane] - m) / den;
-    const int e = sel_i[w][lane];
-    idx[(long)r * NK + lane] = e;
+  for (int o = 1; o < NK; o <<= 1) den += __shfl_xor(den, o, 64);
+  if (lane < NK) {
+    const float gt = ex / den;
+    idx[(long)r * NK + lane] = mine_e;
     gate[(long)r * NK + lane] = gt;
-    if (idx_dump) idx_dump[(long)r * NK + lane] = e;
+    if (idx_dump) idx_dump[(long)r * NK + lane] = mine_e;
     if (gate_dump) gate_dump[(long)r * NK + lane] = gt;
   }
 }
@@ -408,7 +428,7 @@ hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, floa
                        float* gate_dump, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (E > 256 || k > E || rlog.n < 1 || rlog.n > 8) return hipErrorInvalidValue;
-  const dim3 grid((rows + 3) / 4), block(256);
+  const dim3 grid(rows), block(64);
 #define DG_TOPK_NS(NK)                                                                                   \
   switch (rlog.n) {                                                                                      \
     case 1: hipLaunchKernelGGL((topk_kernel<1, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \

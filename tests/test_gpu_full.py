@@ -30,11 +30,11 @@ SEED = 2024
 FULL = WORKLOADS["full_step"].model
 CHECK_LAYERS = (0, 1, FULL.n_layers // 2, FULL.n_layers - 1)
 # Near-tie margin for expert selection.  Router logits (std ~1 in this model)
-# inherit the relative error of the layer's hidden state, held to 1e-2, so two
-# experts whose logits the oracle separates by less than 1e-2 may swap.  Deep
-# layers and the 32768-key attention reach that level; the single-layer tests
-# keep the tighter 1e-3.
-ROUTER_MARGIN = 1e-2
+# inherit the relative error of the layer's hidden state, held to 1e-2, so each
+# logit may move by up to ~1e-2 and two experts whose logits the oracle
+# separates by less than twice that may swap.  Deep layers and the 32768-key
+# attention reach that level; the single-layer tests keep the tighter 1e-3.
+ROUTER_MARGIN = 2e-2
 
 
 @pytest.fixture(scope="module")
