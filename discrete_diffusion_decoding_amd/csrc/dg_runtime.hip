@@ -433,6 +433,9 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.ring = m->d_ring;
       g.A = xn; g.lda = D; g.W = lw(m, l, m->lay.w_qkv); g.ldw = D; g.K = D; g.N = qkvd; g.k_chunk = D;
       dense_rows(g, R); g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
+      // 128-wide weight tiles: without a k split there are enough of them, and
+      // each activation byte fetched then feeds twice the weight rows
+      g.tile_cols = 128; g.ring = 3;
       ProfScope ps_(m, DG_PROF_DENSE, st);
       DG_CK(gemm(EPI_STORE_BF16, g, st));
     }
@@ -494,7 +497,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.ring = m->d_ring;
       g.A = o; g.lda = H * hd; g.W = lw(m, l, m->lay.w_o); g.ldw = H * hd; g.K = H * hd; g.N = D;
       dense_rows(g, R);
-      g.k_split = choose_ksplit((long)g.items_max * cdiv(D, 64), H * hd, kMaxDenseSplit, &g.k_chunk);
+      g.k_split = choose_ksplit((long)g.items_max * cdiv(D, g.tile_cols), H * hd, kMaxDenseSplit, &g.k_chunk);
       opp.n = g.k_split;
       g.C = at<float>(ws, p.dpart); g.ldc = D; g.c_kstride = (long)R * D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_DENSE, st);
@@ -527,7 +530,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g2.ring = m->d_ring;
       g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
       dense_rows(g2, R);
-      g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, 64), fs, kMaxDenseSplit, &g2.k_chunk);
+      g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, g2.tile_cols), fs, kMaxDenseSplit, &g2.k_chunk);
       ysp.n = g2.k_split;
       g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
       DG_CK(gemm(EPI_STORE_F32, g2, ss));

@@ -63,12 +63,29 @@ __global__ __launch_bounds__(256, NS == 2 ? 3 : 2) void gemm_kernel(GemmArgs g) 
   constexpr bool GEGLU = EPI == EPI_GEGLU_BF16;
   constexpr int NCOL = GEGLU ? BW / 2 : BW;   // output columns per tile
   const int ntiles = (g.N + NCOL - 1) / NCOL;
-  const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
-  if (bidx < 0) return;
-  const int item = (int)(bidx % g.items_max);
-  const long rest = bidx / g.items_max;
-  const int tile = (int)(rest % ntiles);
-  const int zk = (int)(rest / ntiles);
+  int item, tile, zk;
+  if (ITEMS) {
+    // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the actual work
+    // list, tile-major within an item, so the gathered activation rows of an
+    // item are fetched into one XCD's L2 only
+    const int ni = *g.n_items;
+    const int x = blockIdx.x & 7;
+    const long w = blockIdx.x >> 3;
+    const int lo = (int)(((long)x * ni) >> 3), hi = (int)(((long)(x + 1) * ni) >> 3);
+    const long per = (long)ntiles * g.k_split;
+    if (w >= (long)(hi - lo) * per) return;
+    item = lo + (int)(w / per);
+    const long rest = w % per;
+    tile = (int)(rest % ntiles);
+    zk = (int)(rest / ntiles);
+  } else {
+    const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
+    if (bidx < 0) return;
+    item = (int)(bidx % g.items_max);
+    const long rest = bidx / g.items_max;
+    tile = (int)(rest % ntiles);
+    zk = (int)(rest / ntiles);
+  }
 
   int grp, r0, nrows;
   if (ITEMS) {
@@ -282,7 +299,8 @@ static hipError_t launch_v(GemmArgs a, hipStream_t s) {
   constexpr int NCOL = (EPI == EPI_GEGLU_BF16) ? BW / 2 : BW;
   if (!ITEMS) a.items_max = (a.M + AR - 1) / AR;
   const int ntiles = (a.N + NCOL - 1) / NCOL;
-  const long total = (long)a.items_max * ntiles * a.k_split;
+  // work lists: every XCD gets room for an eighth of items_max (rounded up)
+  const long total = (ITEMS ? 8L * ((a.items_max + 7) / 8) : (long)a.items_max) * ntiles * a.k_split;
   if (total <= 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_kernel<EPI, ITEMS, AR, BW, NS>), dim3(xcd_grid(total)), dim3(256), 0, s, a);
   return hipGetLastError();
