@@ -44,6 +44,29 @@ __device__ __forceinline__ int row_step(const SampleArgs& a, int b) {
   return a.step_arg >= 0 ? a.step_arg : a.steps[b];
 }
 
+// Gumbel noise through the hardware log2: over all 2^23 uniforms that
+// dg_uniform_open01 can produce it differs from dg_gumbel by at most 1.6e-6
+// (measured exhaustively on gfx950), so kGumbelScreen bounds the difference.
+// It screens candidates; decisions are taken on dg_gumbel only.
+constexpr float kGumbelScreen = 4e-6f;
+__device__ __forceinline__ float gumbel_screen(float u) {
+  const float LN2 = 0.693147180559945f;
+  return -LN2 * __builtin_amdgcn_logf(-LN2 * __builtin_amdgcn_logf(u));
+}
+// scaled logit and score: separate IEEE operations (no contraction), shared by
+// the screen and the exact score so that they differ only through the noise
+__device__ __forceinline__ float scale_logit(float l, float inv_tau) {
+#pragma clang fp contract(off)
+  return l * inv_tau;
+}
+__device__ __forceinline__ float add_noise(float scaled, float g) {
+#pragma clang fp contract(off)
+  return scaled + g;
+}
+__device__ __forceinline__ float gumbel_score(float scaled, uint32_t w) {
+  return add_noise(scaled, dg_gumbel(dg_uniform_open01(w)));
+}
+
 __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   if (a.flag && *a.flag) return;
   __shared__ Stat red[4][4];
@@ -60,14 +83,31 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   const int v0 = sl * per, v1 = min(a.V, v0 + per);
   const float* l0 = a.logits + (long)(b * a.T + pg * 4) * a.ldl;
 
+  // Per row j: softmax statistics and argmax as the logits stream by; for the
+  // Gumbel maximum the screened score keeps this thread's best two, and only
+  // the best one is scored exactly.  If the runner-up is within twice the
+  // screening error of the best, the thread rescores all its entries of that
+  // row exactly (rare), so the result is the exact maximum in every case.
   Stat st[4];
+  float b1[4], b2[4], bl[4];   // best / runner-up screened score, best's scaled logit
+  uint32_t bw[4];
+  int bv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) st[j] = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
-  for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+  for (int j = 0; j < 4; ++j) {
+    st[j] = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
+    b1[j] = b2[j] = -INFINITY;
+    bl[j] = 0.f;
+    bw[j] = 0u;
+    bv[j] = 0x7FFFFFFF;
+  }
+  // entries v and v + 256 alternate between two register sets: the loads of
+  // the next entry are in flight while one is processed (indices clamped to
+  // the slice, so every load is issued)
+  const auto proc = [&](int v, const float* lv) {
     const dg_u32x4 w = dg_philox4x32_10((uint32_t)v, (uint32_t)pg, (uint32_t)s, 0u, k0, k1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float l = l0[(long)j * a.ldl + v];
+      const float l = lv[j];
       Stat& t = st[j];
       if (l > t.m) {
         if (t.m == -INFINITY) {
@@ -84,13 +124,52 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
         t.A += e * (l - t.m);
       }
       if (l > t.av) { t.av = l; t.ai = v; }   // v increasing per thread: ties keep the lower index
-      float sc;
-      {
-#pragma clang fp contract(off)
-        const float scaled = l * inv_tau;
-        sc = scaled + dg_gumbel(dg_uniform_open01(w.x[j]));
+      const float scaled = scale_logit(l, inv_tau);
+      const float sc = add_noise(scaled, gumbel_screen(dg_uniform_open01(w.x[j])));
+      if (sc > b1[j]) {
+        b2[j] = b1[j];
+        b1[j] = sc;
+        bl[j] = scaled;
+        bw[j] = w.x[j];
+        bv[j] = v;
+      } else {
+        b2[j] = fmaxf(b2[j], sc);
       }
-      if (sc > t.gv) { t.gv = sc; t.gi = v; }
+    }
+  };
+  const int vlast = v1 - 1;
+  float la[4], lb[4];
+  const int vs = v0 + (int)threadIdx.x;
+  if (vs < v1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) la[j] = l0[(long)j * a.ldl + vs];
+  }
+  for (int v = vs; v < v1; v += 512) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lb[j] = l0[(long)j * a.ldl + min(v + 256, vlast)];
+    proc(v, la);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) la[j] = l0[(long)j * a.ldl + min(v + 512, vlast)];
+    if (v + 256 < v1) proc(v + 256, lb);
+  }
+  unsigned slow = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (bv[j] == 0x7FFFFFFF) continue;   // no entries
+    const float tol = kGumbelScreen + fmaxf(fabsf(b1[j]), fabsf(b2[j])) * 2.5e-7f;
+    if (b2[j] >= b1[j] - 2.f * tol) slow |= 1u << j;
+    st[j].gv = gumbel_score(bl[j], bw[j]);
+    st[j].gi = bv[j];
+  }
+  if (slow) {
+    for (int v = v0 + threadIdx.x; v < v1; v += 256) {
+      const dg_u32x4 w = dg_philox4x32_10((uint32_t)v, (uint32_t)pg, (uint32_t)s, 0u, k0, k1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!((slow >> j) & 1u)) continue;
+        const float sc = gumbel_score(scale_logit(l0[(long)j * a.ldl + v], inv_tau), w.x[j]);
+        if (sc > st[j].gv || (sc == st[j].gv && v < st[j].gi)) { st[j].gv = sc; st[j].gi = v; }
+      }
     }
   }
   // wavefront reduction

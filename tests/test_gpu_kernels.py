@@ -52,8 +52,9 @@ def _canvas(B, T, V):
     return st
 
 
-def _run_sampler_case(B, T, V, scale, peaked, steps, sp, seed=5):
-    logits = synth.logits(seed, f"lg{B}x{T}x{V}", (B, T, V), scale=scale, peaked=peaked)
+def _run_sampler_case(B, T, V, scale, peaked, steps, sp, seed=5, logits=None):
+    if logits is None:
+        logits = synth.logits(seed, f"lg{B}x{T}x{V}", (B, T, V), scale=scale, peaked=peaked)
     seeds = synth.row_seeds(seed, B)
     L = dev(logits)
     st = _canvas(B, T, V)
@@ -107,6 +108,35 @@ def test_sampler_full_vocab_one_canvas_bit_exact():
 
 def test_sampler_full_vocab_four_canvases_bit_exact():
     _run_sampler_case(4, 256, 262144, 1.06, 20.0, [3], SamplerParams(), seed=11)
+
+
+def test_sampler_near_tie_gumbel_winners_bit_exact():
+    """Each row holds three entries whose Gumbel-max scores agree to within a
+    few ulps (logits built from the oracle's own noise at this step, all others
+    far below; two of them 256 apart, so one GPU thread reads both), so the
+    winner is decided by the last bits of the exact scores and, on equality,
+    by the lower index."""
+    from oracle import rng as orng
+    B, T, V, step, seed = 1, 32, 2048, 2, 21
+    sp = SamplerParams()
+    seeds = synth.row_seeds(seed, B)
+    _, inv_tau = osmp.temperature(step, sp.tau_start, sp.tau_end, sp.max_steps)
+    k0, k1 = orng.seed_key(int(seeds[0]))
+    v = np.arange(V, dtype=np.uint64)
+    logits = np.full((B, T, V), -30.0, np.float32)
+    for g in range(T // 4):
+        words = orng.philox4x32(v, g, step, 0, k0, k1)
+        for j in range(4):
+            i = 4 * g + j
+            noise = orng.gumbel_f32(orng.uniform_open01(words[j]))
+            v1, v2 = (7 * i + 3) % V, (13 * i + 1000) % V
+            v3 = v1 + 256 if v1 % 1024 < 768 else v1 - 256   # read by the same thread as v1
+            for vv, off in ((v1, 0), (v2, (i % 5) - 2), (v3, (i % 3) - 1)):
+                lv = np.float32((np.float32(10.0) - noise[vv]) / inv_tau)
+                for _ in range(abs(off)):
+                    lv = np.nextafter(lv, np.float32(np.inf if off > 0 else -np.inf), dtype=np.float32)
+                logits[0, i, vv] = lv
+    _run_sampler_case(B, T, V, 0.0, 0.0, [step], sp, seed=seed, logits=logits)
 
 
 def test_init_canvas_bit_exact():
