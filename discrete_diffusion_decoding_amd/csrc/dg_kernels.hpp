@@ -45,10 +45,14 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
 // 256 activation rows x 128 weight rows per workgroup; dense rows only (items_max =
 // ceil(M / 256)); epilogues EPI_STORE_F32 (split-K partials) and EPI_STORE_BF16
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s);
+hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s);
 constexpr int kFatRowChunk = 256;
 // the 256-row kernel addresses a tile with 32-bit byte offsets from its first row
 inline bool gemm_fat_pitch_ok(long lda, long ldw) {
   return (long)kFatRowChunk * lda * 2 < 0x7FFFFFFFL && 128L * ldw * 2 < 0x7FFFFFFFL;
+}
+inline bool gemm_fat2_pitch_ok(long lda, long ldw) {
+  return (long)kFatRowChunk * lda * 2 < 0x7FFFFFFFL && 256L * ldw * 2 < 0x7FFFFFFFL;
 }
 constexpr int kGemmRowChunk = 64;
 

@@ -229,9 +229,10 @@ static int choose_ksplit(long tiles_times_items, int K, int max_split, int* k_ch
   return cdiv(K, kc);
 }
 
-// Products with at least this many rows run on the 256-row tile kernel: every
-// weight byte then enters one workgroup only, where the 64-row kernel fetches
-// it once per 64-row chunk.
+// Products with at least this many rows run on the 256 x 256 tile kernel:
+// every weight byte then enters one workgroup only (the 64-row kernel fetches
+// it once per 64-row chunk), and every activation byte fetched feeds 256
+// weight rows.
 static const int kFatMinRows = 192;
 static bool fat_rows(int rows) { return rows >= kFatMinRows; }
 
@@ -239,8 +240,9 @@ static bool fat_rows(int rows) { return rows >= kFatMinRows; }
 // per CU) or ~1024 (64-row tiles) workgroups share the contraction.
 static void soft_split(const dg_model_desc& d, int rows, int* ksplit, int* kchunk) {
   const bool fat = fat_rows(rows);
-  const int items = fat ? cdiv(d.d_model, 128) * cdiv(rows, kFatRowChunk) : cdiv(d.d_model, 64) * cdiv(rows, 64);
-  int ks = std::max(1, std::min(32, cdiv(fat ? 352 : 1024, items)));
+  const int items = fat ? cdiv(d.d_model, 256) * cdiv(rows, kFatRowChunk) : cdiv(d.d_model, 64) * cdiv(rows, 64);
+  // 256 x 256 tiles run one workgroup per CU: at most one round of 256
+  int ks = std::max(1, std::min(32, fat ? 256 / items : cdiv(1024, items)));
   int kc = cdiv(cdiv(d.vocab, ks), 64) * 64;
   *kchunk = kc;
   *ksplit = cdiv(d.vocab, kc);
@@ -254,6 +256,7 @@ static hipError_t dense_gemm(int epi, GemmArgs g, int M, hipStream_t st) {
   if (fat_rows(M) && (epi == EPI_STORE_F32 || epi == EPI_STORE_BF16) && !g.a_rows &&
       gemm_fat_pitch_ok(g.lda, g.ldw)) {
     g.items_max = cdiv(M, kFatRowChunk);
+    if (gemm_fat2_pitch_ok(g.lda, g.ldw)) return gemm_fat2(epi, g, st);
     return gemm_fat(epi, g, st);
   }
   g.items_max = cdiv(M, kGemmRowChunk);

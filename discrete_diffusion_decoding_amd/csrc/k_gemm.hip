@@ -484,6 +484,153 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Square variant for the widest products (LM head, soft-prediction embedding):
+// 256 activation rows x 256 weight rows per workgroup of 8 waves, so every
+// activation byte fetched feeds 256 weight rows (two request bytes per weight
+// byte instead of three).  Stages of 64 columns (A 32 KB + B 32 KB) in a ring
+// of two: stage s+1 streams while stage s is multiplied, and the DMA of stage
+// s+2 reuses stage s's buffer once every wave has read it.  Wave w multiplies
+// activation rows 128 (w / 4) .. +127 by weight rows 64 (w % 4) .. +63.
+constexpr int kFat2A = 256 * 64, kFat2Stage = 512 * 64;
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[kFat2Stage];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[kFat2Stage];
+  if (g.flag && *g.flag) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntiles = (g.N + 255) / 256;
+  const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
+  if (bidx < 0) return;
+  const int item = (int)(bidx % g.items_max);
+  const long rest = bidx / g.items_max;
+  const int tile = (int)(rest % ntiles);
+  const int zk = (int)(rest / ntiles);
+  const int r0 = item * 256;
+  const int nrows = min(256, g.M - r0);
+  if (nrows <= 0) return;
+  const int n_base = tile * 256;
+  const int kb = zk * g.k_chunk;
+  const int ke = min(g.K, kb + g.k_chunk);
+  const int nst = (ke - kb) >> 6;
+  if (nst <= 0) return;
+
+  // DMA: wave w moves A row groups 4w..4w+3 and B row groups 4w..4w+3 (8 rows
+  // each); wave-uniform bases advance per stage, per-lane byte offsets are fixed.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int part = lslot ^ lrow;
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * wave + j) * 8 + lrow;   // 0..255
+    aoff[j] = (int)(((long)min(row, nrows - 1) * g.lda + part * 8) * 2);
+    boff[j] = (int)(((long)(min(n_base + row, g.N - 1) - n_base) * g.ldw + part * 8) * 2);
+  }
+  const char* abase = reinterpret_cast<const char*>(g.A + (long)r0 * g.lda + kb);
+  const char* bbase = reinterpret_cast<const char*>(g.W + (long)n_base * g.ldw + kb);
+  const int dst_a = (4 * wave) * 512, dst_b = kFat2A + (4 * wave) * 512;
+#define DG_F2ISSUE(S, ST)                                                                                  \
+  do {                                                                                                     \
+    const char* ab_ = abase + ((long)(ST) << 7);                                                           \
+    const char* bb_ = bbase + ((long)(ST) << 7);                                                           \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
+      __builtin_amdgcn_global_load_lds((const void*)(ab_ + aoff[j]), (lds_void_t*)&S[dst_a + 512 * j], 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
+      __builtin_amdgcn_global_load_lds((const void*)(bb_ + boff[j]), (lds_void_t*)&S[dst_b + 512 * j], 16, 0, 0); \
+  } while (0)
+
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wn = wave & 3, wm = wave >> 2;
+  int boffr[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) boffr[n] = kFat2A + (64 * wn + 16 * n + lr) * 64;
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 af[8], bfr[4];
+#define DG_F2HALF(S, J)                                                                                    \
+  do {                                                                                                     \
+    const int p_ = 4 * (J) + lg;                                                                           \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                                        \
+      const int arow = 128 * wm + 16 * m + lr;                                                             \
+      af[m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);                  \
+    }                                                                                                      \
+    _Pragma("unroll") for (int n = 0; n < 4; ++n)                                                          \
+      bfr[n] = *reinterpret_cast<const bf16x8*>(&S[boffr[n] + ((p_ ^ (lr & 7)) << 3)]);                    \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m)                                                          \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bfr[n], acc[m][n]);    \
+  } while (0)
+  // stage s is read when at most stage s+1 (8 loads per lane) is pending; its
+  // buffer is refilled (stage s+2, clamped to the last stage, so every
+  // iteration issues the same count) after every wave has read it
+#define DG_F2ITER(SI, CUR)                                                                                 \
+  do {                                                                                                     \
+    const int s_ = (SI);                                                                                   \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                                                             \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    DG_F2HALF(CUR, 0);                                                                                     \
+    DG_F2HALF(CUR, 1);                                                                                     \
+    __builtin_amdgcn_s_waitcnt(0xC07F);   /* lgkmcnt(0): this wave's reads of CUR are done */              \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+    DG_F2ISSUE(CUR, min(s_ + 2, nst - 1));                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+  } while (0)
+
+  DG_F2ISSUE(S0, 0);
+  DG_F2ISSUE(S1, min(1, nst - 1));
+  int s = 0;
+  for (; s + 2 <= nst; s += 2) {
+    DG_F2ITER(s, S0);
+    DG_F2ITER(s + 1, S1);
+  }
+  if (s < nst) {   // odd count: the last stage sits in S0; drain the ring
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    DG_F2HALF(S0, 0);
+    DG_F2HALF(S0, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the loop
+#undef DG_F2ISSUE
+#undef DG_F2HALF
+#undef DG_F2ITER
+
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = n_base + 64 * wn + 16 * n + lr;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 128 * wm + 16 * m + 4 * lg + i;
+        if (rl >= nrows) continue;
+        const long off = (long)(r0 + rl) * g.ldc + col;
+        if (EPI == EPI_STORE_BF16) reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(acc[m][n][i]);
+        else reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = acc[m][n][i];
+      }
+    }
+  }
+}
+
+hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
+  if (a.lda % 8 != 0 || a.ldw % 8 != 0 || a.items || a.a_rows) return hipErrorInvalidValue;
+  if (!gemm_fat2_pitch_ok(a.lda, a.ldw)) return hipErrorInvalidValue;   // 32-bit per-lane offsets
+  const long total = (long)a.items_max * ((a.N + 255) / 256) * a.k_split;
+  if (total <= 0) return hipSuccess;
+  switch (epi) {
+    case EPI_STORE_F32: hipLaunchKernelGGL(gemm_fat2_kernel<EPI_STORE_F32>, dim3(xcd_grid(total)), dim3(512), 0, s, a); break;
+    case EPI_STORE_BF16: hipLaunchKernelGGL(gemm_fat2_kernel<EPI_STORE_BF16>, dim3(xcd_grid(total)), dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
   if (a.lda % 8 != 0 || a.ldw % 8 != 0 || a.items || a.a_rows) return hipErrorInvalidValue;

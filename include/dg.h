@@ -216,7 +216,7 @@ dg_status dg_init_canvas(const dg_model* m, dg_canvas* canvas, int32_t B, int32_
 
 /* C fp32 [M][N] (row pitch ldc) = A [M][K] (bf16, pitch lda) times W^T, W bf16
  * [N][K] (pitch ldw): the MFMA weight-streaming GEMM every projection of the
- * step uses, exposed on its own (M >= 192 runs on the 256-row tile kernel,
+ * step uses, exposed on its own (M >= 192 runs on the 256 x 256 tile kernel,
  * smaller M on the 64-row one).  K a multiple of 64; lda and ldw multiples of
  * 8 (16-byte aligned rows), else DG_ERR_SHAPE before any device work. */
 dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t M, int32_t N, int32_t K,
