@@ -156,101 +156,137 @@ hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta,
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup per token row.  Waves take heads round-robin: q heads, then k
-// heads: RMSNorm over head_dim, then rotate-half RoPE from the table.  Lane l
-// holds elements l + 64 j of a head; the rotary partner of element e is
-// e +- hd/2, i.e. slot j +- hd/128 of the same lane when hd >= 128, or lane
-// l ^ (hd/2) when hd == 64.
+// sum over the wave, in every lane: lane pairs (xor 1, xor 2), mirrored
+// halves of 8 and 16 lanes, then the gfx950 row swaps of 16 and 32 lanes
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x140, 0xF, 0xF, false));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// One wave per (token row, head): q heads, then k heads.  RMSNorm over
+// head_dim, then rotate-half RoPE from the table.  Lane l holds the EPL =
+// hd/64 consecutive elements EPL*l ..; the rotary partner of element e is
+// e +- hd/2, held by lane l ^ 32 in the same position.
 template <int HD>
-__device__ __forceinline__ void qk_rope_row(const QkRopeArgs& a, int r) {
+__device__ __forceinline__ void qk_rope_head(const QkRopeArgs& a, int r, int hh) {
   constexpr int HALF = HD / 2;
-  constexpr int NS = HD / 64;
+  constexpr int EPL = HD / 64;
   const int tloc = r % a.per_batch, bidx = r / a.per_batch;
-  const float2* tab = a.rope + (long)tloc * HALF;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int e0 = EPL * lane;
   const int qkvd = (a.H + 2 * a.Hkv) * HD;
-  const bf16_t* src = a.qkv + (long)r * qkvd;
-  for (int hh = wave; hh < a.H + a.Hkv; hh += 4) {
-    const bf16_t* xs = src + hh * HD;
-    const bool isq = hh < a.H;
-    const bf16_t* nw = isq ? a.qnorm : a.knorm;
-    float x[NS];
-    float ss = 0.f;
+  const bool isq = hh < a.H;
+  const bf16_t* xs = a.qkv + (long)r * qkvd + hh * HD + e0;
+  const bf16_t* nw = (isq ? a.qnorm : a.knorm) + e0;
+  const float2* tab = a.rope + (long)tloc * HALF + (e0 < HALF ? e0 : e0 - HALF);
+  float x[EPL], w[EPL];
+  float2 cs[EPL];
+  static_assert(EPL == 1 || EPL == 2 || EPL == 4, "head_dim 64, 128 or 256");
+  if constexpr (EPL == 4) {   // 8-byte element loads, 16-byte table loads
+    const uint2 xv = *reinterpret_cast<const uint2*>(xs);
+    const uint2 wv = *reinterpret_cast<const uint2*>(nw);
+    const float4 t0 = *reinterpret_cast<const float4*>(tab);
+    const float4 t1 = *reinterpret_cast<const float4*>(tab + 2);
+    x[0] = bf2f(xv.x & 0xFFFF); x[1] = bf2f(xv.x >> 16); x[2] = bf2f(xv.y & 0xFFFF); x[3] = bf2f(xv.y >> 16);
+    w[0] = bf2f(wv.x & 0xFFFF); w[1] = bf2f(wv.x >> 16); w[2] = bf2f(wv.y & 0xFFFF); w[3] = bf2f(wv.y >> 16);
+    cs[0] = make_float2(t0.x, t0.y); cs[1] = make_float2(t0.z, t0.w);
+    cs[2] = make_float2(t1.x, t1.y); cs[3] = make_float2(t1.z, t1.w);
+  } else {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      x[j] = bf2f(xs[lane + 64 * j]);
-      ss += x[j] * x[j];
+    for (int j = 0; j < EPL; ++j) {
+      x[j] = bf2f(xs[j]);
+      w[j] = bf2f(nw[j]);
+      cs[j] = tab[j];
     }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
+  }
+  float ss = 0.f;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) x[j] = x[j] * inv * bf2f(nw[lane + 64 * j]);
-    float y[NS];
+  for (int j = 0; j < EPL; ++j) ss += x[j] * x[j];
+  ss = wave_sum_dpp(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)HD + a.eps);
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int e = lane + 64 * j;
-      const float partner = (HD >= 128) ? x[(j + HALF / 64) % NS] : __shfl_xor(x[j], HALF, 64);
-      const float2 cs = tab[e < HALF ? e : e - HALF];
-      y[j] = (e < HALF) ? x[j] * cs.x - partner * cs.y : x[j] * cs.x + partner * cs.y;
-    }
-    bf16_t* dst;
-    if (isq) {
-      dst = a.q + ((long)r * a.H + hh) * HD;
-    } else {
-      dst = a.kdst + bidx * a.k_bstride + (hh - a.H) * a.k_hstride + (long)(a.t_offset + tloc) * HD;
-    }
+  for (int j = 0; j < EPL; ++j) x[j] = x[j] * inv * w[j];
+  const float sgn = e0 < HALF ? -1.f : 1.f;
+  bf16_t* dst = isq ? a.q + ((long)r * a.H + hh) * HD + e0
+                    : a.kdst + bidx * a.k_bstride + (hh - a.H) * a.k_hstride + (long)(a.t_offset + tloc) * HD + e0;
+  uint16_t y[EPL];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) dst[lane + 64 * j] = f2bf(y[j]);
+  for (int j = 0; j < EPL; ++j) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[j]), __float_as_uint(x[j]), false, false);
+    // lanes < 32 get the partner from swap output 1, lanes >= 32 from output 0
+    const float partner = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
+    y[j] = f2bf(x[j] * cs[j].x + sgn * partner * cs[j].y);
+  }
+  if constexpr (EPL == 4) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2((uint32_t)y[0] | ((uint32_t)y[1] << 16), (uint32_t)y[2] | ((uint32_t)y[3] << 16));
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) dst[j] = y[j];
   }
 }
 
-// V^T scatter: a workgroup moves 32 tokens x hd values of one kv head through
-// LDS so that every row of V^T (one dimension, 32 consecutive positions) is
-// written as one contiguous 64-byte run.
+// V^T scatter: a workgroup moves 32 positions x 64 dims of one kv head through
+// LDS (one 16-byte load per thread), then each thread writes 8 positions of
+// one dim as a 16-byte store, so every V^T row gets one 64-byte run.  The LDS
+// row pitch of 66 values staggers the banks of the 8-row steps read together.
+constexpr int kVtPitch = 66;
 template <int HD>
-__device__ __forceinline__ void vt_scatter_tile(const QkRopeArgs& a, int g, int t0, bf16_t (*tile)[HD + 2]) {
-  // t0: first row of the tile (rows of one batch element)
+__device__ __forceinline__ void vt_scatter_block(const QkRopeArgs& a, int g, int t0, int d0, bf16_t* tile) {
+  const int tid = threadIdx.x;
   const int qkvd = (a.H + 2 * a.Hkv) * HD;
-  for (int i = threadIdx.x; i < 32 * HD; i += 256) {
-    const int tr = i / HD, e = i % HD;
+  {
+    const int tr = tid >> 3, c = (tid & 7) * 8;
     const int r = min(t0 + tr, a.rows - 1);
-    tile[tr][e] = a.qkv[(long)r * qkvd + (a.H + a.Hkv + g) * HD + e];
+    const uint4 v = *reinterpret_cast<const uint4*>(a.qkv + (long)r * qkvd + (a.H + a.Hkv + g) * HD + d0 + c);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(tile + tr * kVtPitch + c);   // 4-byte aligned (even pitch)
+    dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
   }
   __syncthreads();
-  const int bidx = t0 / a.per_batch, tloc0 = t0 % a.per_batch;
-  bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (a.t_offset + tloc0);
+  const int bidx = t0 / a.per_batch, p0 = a.t_offset + t0 % a.per_batch;
+  const int dim = tid >> 2, pg = (tid & 3) * 8;
   const int nval = min(32, a.rows - t0);
-  for (int i = threadIdx.x; i < HD * 16; i += 256) {     // HD rows x 16 pairs of positions
-    const int e = i >> 4, p = (i & 15) * 2;
-    if (p + 1 < nval) {
-      const uint32_t w = (uint32_t)tile[p][e] | ((uint32_t)tile[p + 1][e] << 16);
-      *reinterpret_cast<uint32_t*>(vt + (long)e * a.v_pitch + p) = w;
-    } else if (p < nval) {
-      vt[(long)e * a.v_pitch + p] = tile[p][e];
-    }
+  bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (long)(d0 + dim) * a.v_pitch + p0 + pg;
+  uint16_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = tile[(pg + i) * kVtPitch + dim];
+  if (pg + 8 <= nval && ((a.v_pitch | p0) & 7) == 0) {
+    *reinterpret_cast<uint4*>(vt) = make_uint4((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                                               (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16));
+  } else {
+    for (int i = 0; i < 8 && pg + i < nval; ++i) vt[i] = v[i];
   }
 }
 
-// one launch: blocks [0, rows) normalise and rotate the q / k heads of a row,
-// the blocks after them scatter V^T tiles of 32 rows x one kv head
+// one launch of 4-wave blocks: V^T blocks (32 positions x 64 dims of one kv
+// head) first, then blocks of 4 waves, each wave the norm + RoPE of one
+// (row, q / k head)
 template <int HD>
 __global__ __launch_bounds__(256) void qk_rope_kernel(QkRopeArgs a) {
   if (a.flag && *a.flag) return;
-  __shared__ bf16_t tile[32][HD + 2];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[32 * kVtPitch];
+  const int nh = a.H + a.Hkv;
+  const int nt = (a.rows + 31) / 32, nd = HD / 64;
+  const int nvt = nt * nd * a.Hkv;
   const int bx = blockIdx.x;
-  if (bx < a.rows) {
-    qk_rope_row<HD>(a, bx);
+  if (bx < nvt) {
+    vt_scatter_block<HD>(a, bx / (nt * nd), ((bx / nd) % nt) * 32, (bx % nd) * 64, tile);
   } else {
-    const int nt = (a.rows + 31) / 32;
-    const int v = bx - a.rows;
-    vt_scatter_tile<HD>(a, v / nt, (v % nt) * 32, tile);
+    const int u = (bx - nvt) * 4 + (int)(threadIdx.x >> 6);
+    if (u < a.rows * nh) qk_rope_head<HD>(a, u / nh, u % nh);
   }
 }
 
 hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.per_batch % 32 != 0 && a.per_batch != a.rows) return hipErrorInvalidValue;
-  const dim3 grid(a.rows + ((a.rows + 31) / 32) * a.Hkv);
+  const long nvt = (long)((a.rows + 31) / 32) * (a.hd / 64) * a.Hkv;
+  const dim3 grid((unsigned)(nvt + ((long)a.rows * (a.H + a.Hkv) + 3) / 4));
   switch (a.hd) {
     case 64: hipLaunchKernelGGL(qk_rope_kernel<64>, grid, dim3(256), 0, s, a); break;
     case 128: hipLaunchKernelGGL(qk_rope_kernel<128>, grid, dim3(256), 0, s, a); break;
