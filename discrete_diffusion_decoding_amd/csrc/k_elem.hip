@@ -489,52 +489,25 @@ hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, floa
 
 // ---------------------------------------------------------------------------
 // Expert permutation in one workgroup of 1024 threads (16 waves).
-// Assignment a = row * k + j goes to slot offsets[e] + (number of earlier
-// assignments to the same expert e), so every expert's rows stay in token
-// order (deterministic).  Within a wave, lanes with equal experts are found
-// with 8 ballots (one per bit of e); per-wave counts are scanned across the
-// 16 waves of a tile and across tiles.
+// Assignment a = row * k + j takes position p in its expert e from an LDS
+// counter (atomic add; the order of rows within an expert is arbitrary and
+// changes no result: every row of an expert GEMM depends on its own
+// activation row only, and the combine reads the k slots of a row in j
+// order), then goes to slot offsets[e] + p.  p is parked in slot_of[a] (this
+// thread's own write) until the offsets are known.
 __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int na, int k, int E, int32_t* counts,
                                                        int32_t* offsets, int32_t* slot_of, int32_t* slot_row,
                                                        int4* items, int32_t* n_items, int chunk,
                                                        const int32_t* flag) {
   if (flag && *flag) return;
-  __shared__ int wcnt[16][256];
   __shared__ int cnt[256];
   __shared__ int off[257];
   __shared__ int ibase[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < 256; e += 1024) cnt[e] = 0;
-  for (int base = 0; base < na; base += 1024) {
-    for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-    const int a = base + tid;
-    const bool valid = a < na;
-    const int e = valid ? idx[a] : 255;
-    unsigned long long mask = __ballot(valid);
-    if (!valid) mask = ~mask;
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const bool on = (e >> bit) & 1;
-      const unsigned long long bb = __ballot(on);
-      mask &= on ? bb : ~bb;
-    }
-    const int rank = __popcll(mask & ((1ull << lane) - 1ull));
-    if (valid && rank == 0) wcnt[wave][e] = __popcll(mask);
-    __syncthreads();
-    if (tid < E) {
-      int run = cnt[tid];
-      for (int w = 0; w < 16; ++w) {
-        const int c = wcnt[w][tid];
-        wcnt[w][tid] = run;
-        run += c;
-      }
-      cnt[tid] = run;
-    }
-    __syncthreads();
-    if (valid) slot_of[a] = wcnt[wave][e] + rank;
-    __syncthreads();
-  }
+  if (tid < 256) cnt[tid] = 0;
+  __syncthreads();
+  for (int a = tid; a < na; a += 1024) slot_of[a] = atomicAdd(&cnt[idx[a]], 1);
+  __syncthreads();
   // exclusive scans over the experts of the row counts and of the item counts:
   // waves 0-3 scan 64 experts each (shuffle scan), then add the wave totals
   __shared__ int wtot[4][2];
