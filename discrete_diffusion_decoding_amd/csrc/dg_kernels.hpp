@@ -117,7 +117,7 @@ hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* coun
                        int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
                        const int32_t* flag, hipStream_t s);
 // h[r] += sum_s ys_s[r] + sum_j gate[r,j] * Y[slot_of[r,j]]; then optional next RMSNorm -> xn, dump of h
-hipError_t moe_combine(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate,
+hipError_t moe_combine(float* h, Partials ys, const bf16_t* Y, const int32_t* slot_of, const float* gate,
                        int rows, int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump,
                        const int32_t* flag, hipStream_t s);
 

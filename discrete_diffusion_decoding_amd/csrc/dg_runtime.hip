@@ -302,7 +302,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.items = take((E + (R * k + 31) / 32) * 16);   // work list for chunks of >= 32 rows
   p.nitems = take(16);
   p.hbuf = take(R * k * d.d_expert * 2);
-  p.ybuf = take(R * k * D * 4);
+  p.ybuf = take(R * k * D * 2);
   p.hs = take(R * std::max(d.d_shared, 1) * 2);
   p.ys = take(d.d_shared ? (size_t)kMaxDenseSplit * R * D * 4 : 0);
   if (V) {
@@ -409,7 +409,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   int32_t* nitems = at<int32_t>(ws, p.nitems);
   const int items_max = E + cdiv((long)R * k, m->x_rows);
   bf16_t* hbuf = at<bf16_t>(ws, p.hbuf);
-  float* ybuf = at<float>(ws, p.ybuf);
+  bf16_t* ybuf = at<bf16_t>(ws, p.ybuf);
   bf16_t* hs = at<bf16_t>(ws, p.hs);
   float* ys = fs ? at<float>(ws, p.ys) : nullptr;
 
@@ -575,7 +575,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.tile_rows = m->x_rows; g.tile_cols = m->xd_cols; g.ring = m->xd_ring;
       g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
-      DG_CK(gemm(EPI_STORE_F32, g, st));
+      DG_CK(gemm(EPI_STORE_BF16, g, st));
     }
     if (forked) DG_CK(hipStreamWaitEvent(st, m->ev_join, 0));
     const bf16_t* nw = nullptr;

@@ -574,9 +574,10 @@ hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* coun
 }
 
 // ---------------------------------------------------------------------------
-// h[r] += sum_s ys_s[r] + sum_j gate[r,j] * Y[slot[r,j]], then the next RMSNorm.
+// h[r] += sum_s ys_s[r] + sum_j gate[r,j] * Y[slot[r,j]] (expert outputs Y in bf16,
+// as stored by the down projection), then the next RMSNorm.
 template <int NS, int NK>
-__global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, const float* Y,
+__global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, const bf16_t* Y,
                                                       const int32_t* slot_of, const float* gate, int d,
                                                       const bf16_t* nw, float eps, bf16_t* xn, float* dump,
                                                       const int32_t* flag) {
@@ -600,7 +601,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, con
     if (c4 < d4) {
       float4 yv[NK], pv[NS > 0 ? NS : 1];
 #pragma unroll
-      for (int j = 0; j < NK; ++j) yv[j] = reinterpret_cast<const float4*>(Y + (long)sl[j] * d)[c4];
+      for (int j = 0; j < NK; ++j) yv[j] = load_bf16x4(Y + (long)sl[j] * d + 4 * c4);
 #pragma unroll
       for (int s = 0; s < NS; ++s) pv[s] = reinterpret_cast<const float4*>(ys.p + s * ys.stride + (long)r * d)[c4];
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -631,7 +632,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, con
 }
 
 template <int NK>
-static hipError_t combine_k(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate,
+static hipError_t combine_k(float* h, Partials ys, const bf16_t* Y, const int32_t* slot_of, const float* gate,
                             int rows, int d, const bf16_t* nw, float eps, bf16_t* xn, float* dump,
                             const int32_t* flag, hipStream_t s) {
 #define DG_COMB_CASE(N)                                                                                   \
@@ -648,7 +649,7 @@ static hipError_t combine_k(float* h, Partials ys, const float* Y, const int32_t
   return hipGetLastError();
 }
 
-hipError_t moe_combine(float* h, Partials ys, const float* Y, const int32_t* slot_of, const float* gate, int rows,
+hipError_t moe_combine(float* h, Partials ys, const bf16_t* Y, const int32_t* slot_of, const float* gate, int rows,
                        int d, int k, const bf16_t* next_w, float eps, bf16_t* xn, float* dump, const int32_t* flag,
                        hipStream_t s) {
   if (rows <= 0) return hipSuccess;
