@@ -218,15 +218,30 @@ static const int kMaxSplits = 16;
 static const int kMaxDenseSplit = 8;    // split-K slices of a dense projection
 static const int kMaxRouterSplit = 8;   // split-K slices of the router logits
 
-// Split the contraction of a dense product when its output tiles alone would
-// leave the GPU short of ~512 workgroups (2 per CU): returns the slice count and
-// sets the 64-aligned slice length.
+// Split-K slices for the 64-row kernel (two workgroups per CU); returns the
+// slice count and sets the 64-aligned slice length: the count that minimises the modelled time, workgroup length (its 64-column stages plus
+// a fixed cost of 4 for fill and epilogue) times the rounds the grid needs on
+// 256 CUs (a full round of 512 takes two lengths; a remainder of up to 256
+// takes one); ties go to fewer slices (fewer partial sums).
 static int choose_ksplit(long tiles_times_items, int K, int max_split, int* k_chunk) {
-  int ks = (int)std::max(1L, std::min((long)max_split, (512 + tiles_times_items - 1) / tiles_times_items));
-  ks = std::min(ks, std::max(1, K / 128));
-  int kc = cdiv(cdiv(K, ks), 64) * 64;
-  *k_chunk = kc;
-  return cdiv(K, kc);
+  const long t = std::max(1L, tiles_times_items);
+  int best_ks = 1, best_kc = cdiv(K, 64) * 64;
+  long best_time = -1;
+  const int top = std::max(1, std::min(max_split, K / 128));
+  for (int want = 1; want <= top; ++want) {
+    const int kc = cdiv(cdiv(K, want), 64) * 64;
+    const int ks = cdiv(K, kc);
+    const long n = t * ks, w = kc / 64 + 4;
+    const long full = n / 512, rem = n % 512;
+    const long time = w * (2 * full + (rem + 255) / 256);
+    if (best_time < 0 || time < best_time) {
+      best_time = time;
+      best_ks = ks;
+      best_kc = kc;
+    }
+  }
+  *k_chunk = best_kc;
+  return best_ks;
 }
 
 // Products with at least this many rows run on the 256 x 256 tile kernel:
