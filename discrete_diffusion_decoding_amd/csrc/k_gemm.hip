@@ -65,17 +65,19 @@ __global__ __launch_bounds__(256, NS == 2 ? 3 : 2) void gemm_kernel(GemmArgs g) 
   const int ntiles = (g.N + NCOL - 1) / NCOL;
   int item, tile, zk;
   if (ITEMS) {
-    // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the actual work
-    // list, tile-major within an item, so the gathered activation rows of an
-    // item are fetched into one XCD's L2 only
-    const int ni = *g.n_items;
+    // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the actual
+    // (item, tile) units, tile-major within an item, so the gathered
+    // activation rows of an item are fetched into one (at most two) XCD's L2
+    // and every XCD gets the same number of units (to one)
+    const long per = (long)ntiles * g.k_split;
+    const long nu = (long)(*g.n_items) * per;
     const int x = blockIdx.x & 7;
     const long w = blockIdx.x >> 3;
-    const int lo = (int)(((long)x * ni) >> 3), hi = (int)(((long)(x + 1) * ni) >> 3);
-    const long per = (long)ntiles * g.k_split;
-    if (w >= (long)(hi - lo) * per) return;
-    item = lo + (int)(w / per);
-    const long rest = w % per;
+    const long lo = (x * nu) >> 3, hi = ((x + 1) * nu) >> 3;
+    if (w >= hi - lo) return;
+    const long u = lo + w;
+    item = (int)(u / per);
+    const long rest = u % per;
     tile = (int)(rest % ntiles);
     zk = (int)(rest / ntiles);
   } else {
