@@ -111,8 +111,9 @@ hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits,
 // router logits = sum over split-K partials of the hi rows [0, rows) and lo rows [rows, 2 rows)
 hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
                        float* gate_dump, const int32_t* flag, hipStream_t s);
-// also emits the GEMM work list: int4 {expert, first slot, rows, 0} per chunk of
-// <= chunk rows of every touched expert, and its length in *n_items
+// also emits the GEMM work list: int4 {expert, first slot, rows, chunk index << 16 |
+// chunks of the expert} per chunk of <= chunk rows of every touched expert, and
+// its length in *n_items
 hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* counts, int32_t* offsets,
                        int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
                        const int32_t* flag, hipStream_t s);

@@ -552,7 +552,9 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
     if (e < E) {
       counts[e] = cnt[e];
       int i = ibase[e];
-      for (int r = 0; r < cnt[e]; r += chunk, ++i) items[i] = make_int4(e, off[e] + r, min(chunk, cnt[e] - r), 0);
+      const int nc = (cnt[e] + chunk - 1) / chunk;
+      for (int r = 0, c = 0; r < cnt[e]; r += chunk, ++i, ++c)
+        items[i] = make_int4(e, off[e] + r, min(chunk, cnt[e] - r), (c << 16) | nc);
     }
   }
   for (int a = tid; a < na; a += 1024) {

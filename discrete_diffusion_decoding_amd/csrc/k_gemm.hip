@@ -77,7 +77,19 @@ __global__ __launch_bounds__(256, NS == 2 ? 3 : 2) void gemm_kernel(GemmArgs g) 
     if (w >= hi - lo) return;
     const long u = lo + w;
     item = (int)(u / per);
-    const long rest = u % per;
+    long rest = u % per;
+    {
+      // an expert of several 64-row chunks (items.w = chunk index << 16 |
+      // chunk count): its units run chunk-fastest, so consecutive workgroups
+      // of one XCD share each weight tile
+      const int wv = g.items[item].w;
+      const int ci = wv >> 16, ce = wv & 0xFFFF;
+      if (ce > 1) {
+        const long p = (long)ci * per + rest;
+        item = item - ci + (int)(p % ce);
+        rest = p / ce;
+      }
+    }
     tile = (int)(rest % ntiles);
     zk = (int)(rest / ntiles);
   } else {
