@@ -103,6 +103,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
 
   // ---- fragments of this wave: f = 4 wave + j -> head g*GQ + f%GQ, queries q0wg + 16 (f/GQ) + lr
   bf16x8 qfr[NF][KS];
+  const bf16_t* qptr[NF];
   int qrow[NF], qpos[NF];
   bool live[NF];
 #pragma unroll
@@ -114,9 +115,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     qrow[j] = qr0;
     const int myq = min(qr0 + lr, R - 1);
     qpos[j] = a.qpos0 + myq;
-    const bf16_t* qp = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qfr[j][ks] = load_bf16x8(qp + 32 * ks);
+    qptr[j] = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
   }
 
   // ---- DMA sources: every key count is a multiple of 32, so a tile lies in one
@@ -250,20 +249,29 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_barrier(0);                                                             \
   } while (0)
 
-  __builtin_amdgcn_s_waitcnt(0);   // Q fragments in registers before the ring starts
   if (ntile > 0) {
+    // the Q fragments load ahead of the first three tiles; they retire first,
+    // so waiting for them leaves the tiles in flight
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qfr[j][ks] = load_bf16x8(qptr[j] + 32 * ks);
+    __builtin_amdgcn_sched_barrier(0);
     DG_AISSUE(S0, kbeg);
     DG_AISSUE(S1, kbeg + 32 * min(1, ntile - 1));
     DG_AISSUE(S2, kbeg + 32 * min(2, ntile - 1));
-    for (int t = 0; t < ntile; t += 4) {
+    // full rounds of four, then the last 0-3 tiles: a loop without early
+    // exits keeps the compiler from draining the ring at its head
+    int t = 0;
+    for (; t + 4 <= ntile; t += 4) {
       DG_AITER(t, S0, S3);
-      if (t + 1 >= ntile) break;
       DG_AITER(t + 1, S1, S0);
-      if (t + 2 >= ntile) break;
       DG_AITER(t + 2, S2, S1);
-      if (t + 3 >= ntile) break;
       DG_AITER(t + 3, S3, S2);
     }
+    if (t < ntile) DG_AITER(t, S0, S3);
+    if (t + 1 < ntile) DG_AITER(t + 1, S1, S0);
+    if (t + 2 < ntile) DG_AITER(t + 2, S2, S1);
   }
 #undef DG_AITER
 #undef DG_ATILE
