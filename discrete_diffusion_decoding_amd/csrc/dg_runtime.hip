@@ -640,27 +640,30 @@ extern "C" dg_status dg_forward_hidden(dg_model* m, const void* kv, int32_t Bp, 
   return DG_OK;
 }
 
-static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* hidden, int Bp, int P, int P_max,
-                              void* kv, void* ws, size_t ws_bytes, hipStream_t st) {
+// causal encoding of positions P0 .. P0+n-1 of each of Bp prompts (inputs
+// [Bp][n]), against the cached K/V of positions 0 .. P0-1
+static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* hidden, int Bp, int P0, int n,
+                              int P_max, void* kv, void* ws, size_t ws_bytes, hipStream_t st) {
   if (!m || !kv || !ws || (!tokens && !hidden)) return DG_ERR_ARG;
-  if (Bp < 1 || P < 1 || P_max < P) return DG_ERR_ARG;
-  if (P % 32 || P_max % 32) return DG_ERR_SHAPE;
+  if (Bp < 1 || n < 1 || P0 < 0 || P_max < P0 + n) return DG_ERR_ARG;
+  if (P0 % 32 || n % 32 || P_max % 32) return DG_ERR_SHAPE;
   if (tokens && m->d.vocab == 0) return DG_ERR_ARG;
+  const int P = P0 + n;
   // largest chunk (multiple of 32 rows) whose workspace fits
   int chunk = 0;
-  for (int c = std::min(P, 4096); c >= 32; c -= 32)
+  for (int c = std::min(n, 4096); c >= 32; c -= 32)
     if (make_plan(m->d, c, P).total <= ws_bytes) { chunk = c; break; }
   if (chunk == 0) return DG_ERR_WORKSPACE;
   const Plan p = make_plan(m->d, chunk, P);
   const dg_model_desc& d = m->d;
   for (int bp = 0; bp < Bp; ++bp) {
-    for (int q0 = 0; q0 < P; q0 += chunk) {
+    for (int q0 = P0; q0 < P; q0 += chunk) {
       const int R = std::min(chunk, P - q0);
       if (tokens) {
-        DG_CK(embed_rows(tokens + (size_t)bp * P + q0, (const bf16_t*)m->w.embed, R, d.d_model,
+        DG_CK(embed_rows(tokens + (size_t)bp * n + (q0 - P0), (const bf16_t*)m->w.embed, R, d.d_model,
                          at<float>(ws, p.h), nullptr, st));
       } else {
-        DG_CK(hipMemcpyAsync(at<float>(ws, p.h), hidden + ((size_t)bp * P + q0) * d.d_model,
+        DG_CK(hipMemcpyAsync(at<float>(ws, p.h), hidden + ((size_t)bp * n + (q0 - P0)) * d.d_model,
                              (size_t)R * d.d_model * 4, hipMemcpyDeviceToDevice, st));
       }
       DG_CK(rmsnorm_rows(at<float>(ws, p.h), m->layers[0] + m->lay.attn_norm, R, d.d_model, d.rms_eps,
@@ -679,13 +682,19 @@ static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* h
 extern "C" dg_status dg_prefill_prefix(dg_model* m, const int32_t* prefix, int32_t Bp, int32_t P, int32_t P_max,
                                        void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
   if (!prefix) return DG_ERR_ARG;
-  return prefill_impl(m, prefix, nullptr, Bp, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
+  return prefill_impl(m, prefix, nullptr, Bp, 0, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
+}
+
+extern "C" dg_status dg_prefill_append(dg_model* m, const int32_t* tokens, int32_t Bp, int32_t P0, int32_t n,
+                                       int32_t P_max, void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
+  if (!tokens) return DG_ERR_ARG;
+  return prefill_impl(m, tokens, nullptr, Bp, P0, n, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
 }
 
 extern "C" dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, int32_t Bp, int32_t P,
                                        int32_t P_max, void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
   if (!prefix_hidden) return DG_ERR_ARG;
-  return prefill_impl(m, nullptr, prefix_hidden, Bp, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
+  return prefill_impl(m, nullptr, prefix_hidden, Bp, 0, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -74,6 +74,7 @@ def lib():
             "dg_kv_bytes": (sz, [vp, i32, i32]),
             "dg_workspace_bytes": (sz, [vp, i32, i32]),
             "dg_prefill_prefix": (st, [vp, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "dg_prefill_append": (st, [vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
             "dg_prefill_hidden": (st, [vp, vp, i32, i32, i32, vp, vp, sz, vp]),
             "dg_forward_hidden": (st, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dg_denoise_step": (st, [vp, vp, i32, i32, i32, i32, i32, C.POINTER(Canvas), i32,
@@ -157,6 +158,11 @@ def dg_workspace_bytes(h, rows, keys):
 def dg_prefill_prefix(h, prefix, Bp, P, P_max, kv, ws, stream=None):
     _ck(lib().dg_prefill_prefix(h, _ptr(prefix), Bp, P, P_max, _ptr(kv), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "dg_prefill_prefix")
+
+
+def dg_prefill_append(h, tokens, Bp, P0, n, P_max, kv, ws, stream=None):
+    _ck(lib().dg_prefill_append(h, _ptr(tokens), Bp, P0, n, P_max, _ptr(kv), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "dg_prefill_append")
 
 
 def dg_prefill_hidden(h, prefix_hidden, Bp, P, P_max, kv, ws, stream=None):

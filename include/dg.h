@@ -177,6 +177,15 @@ dg_status dg_prefill_prefix(dg_model* m, const int32_t* prefix, int32_t Bp, int3
 dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, int32_t Bp, int32_t P, int32_t P_max,
                             void* kv, void* ws, size_t ws_bytes, dg_stream_t stream);
 
+/* Block continuation (the finished block joins the causally encoded prompt,
+ * article section 2 and section 5): encodes tokens int32 [Bp][n] at positions
+ * P0 .. P0+n-1 of each prompt, attending causally to the K/V of positions
+ * 0 .. P0-1 already in kv and to each other, and writes their K and V into kv.
+ * dg_prefill_prefix is the case P0 = 0.  P0 and n multiples of 32, n >= 32,
+ * P0 + n <= P_max; else DG_ERR_SHAPE / DG_ERR_ARG before any device work. */
+dg_status dg_prefill_append(dg_model* m, const int32_t* tokens, int32_t Bp, int32_t P0, int32_t n, int32_t P_max,
+                            void* kv, void* ws, size_t ws_bytes, dg_stream_t stream);
+
 /* Layer stack on canvas hidden states: hidden fp32 [B][T][d] in/out (input of
  * layer 0 in, output of the last layer out), bidirectional over the canvas and
  * attending all P prefix keys of prefix (Bp == 1 ? 0 : b).  Dumps as in

@@ -22,6 +22,19 @@ def host(t):
     return t.detach().cpu().numpy()
 
 
+def kv_layer(kv, m, Bp, P_max, l, bp, P):
+    """(K, V) of prefix bp at layer l as float64 [P][Hkv][hd]; the cache holds
+    per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][hd][P_max]."""
+    from discrete_diffusion_decoding_amd import synth
+    n = Bp * m.n_kv_heads * P_max * m.head_dim
+    x = kv.view(torch.int16)[2 * n * l: 2 * n * (l + 1)]
+    K = x[:n].view(Bp, m.n_kv_heads, P_max, m.head_dim)[bp, :, :P, :]
+    Vt = x[n:].view(Bp, m.n_kv_heads, m.head_dim, P_max)[bp, :, :, :P]
+    K = synth.bf16_bits_to_f32(K.permute(1, 0, 2).contiguous().cpu().numpy().view(np.uint16))
+    V = synth.bf16_bits_to_f32(Vt.permute(2, 0, 1).contiguous().cpu().numpy().view(np.uint16))
+    return K.astype(np.float64), V.astype(np.float64)
+
+
 def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

@@ -112,6 +112,24 @@ def test_step_rejects_bad_arguments_before_any_device_work():
     dg.dg_model_destroy(h)
 
 
+def test_prefill_append_rejects_bad_arguments_before_any_device_work():
+    w, keep = _fake_weights(TINY)
+    h = dg.dg_model_create(TINY, w)
+    L = dg.lib()
+    kv, ws, tok = C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000)
+    big = 1 << 30
+    # P0 or n not a multiple of 32
+    assert L.dg_prefill_append(h, tok, 1, 48, 32, 128, kv, ws, big, None) == dg.DG_ERR_SHAPE
+    assert L.dg_prefill_append(h, tok, 1, 64, 40, 128, kv, ws, big, None) == dg.DG_ERR_SHAPE
+    # P0 + n beyond the cache capacity; no tokens; n < 1
+    assert L.dg_prefill_append(h, tok, 1, 96, 64, 128, kv, ws, big, None) == dg.DG_ERR_ARG
+    assert L.dg_prefill_append(h, None, 1, 64, 32, 128, kv, ws, big, None) == dg.DG_ERR_ARG
+    assert L.dg_prefill_append(h, tok, 1, 64, 0, 128, kv, ws, big, None) == dg.DG_ERR_ARG
+    # workspace too small
+    assert L.dg_prefill_append(h, tok, 1, 64, 32, 128, kv, ws, 1024, None) == dg.DG_ERR_WORKSPACE
+    dg.dg_model_destroy(h)
+
+
 def test_gemm_rejects_bad_shapes_before_any_device_work():
     L = dg.lib()
     p = C.c_void_p(0x4000)

@@ -23,7 +23,7 @@ from discrete_diffusion_decoding_amd.configs import WORKLOADS, SamplerParams
 from discrete_diffusion_decoding_amd.device import DeviceModel
 from oracle import model as om
 from oracle import sampler as osmp
-from tests.gpu_util import announce, check_experts, dev, host, rel_l2
+from tests.gpu_util import announce, check_experts, dev, host, kv_layer, rel_l2
 
 pytestmark = pytest.mark.gpu
 SEED = 2024
@@ -51,22 +51,10 @@ def full():
     torch.cuda.empty_cache()
 
 
-def _kv_layer(kv, m, Bp, P_max, l, bp, P):
-    """(K, V) of prefix bp at layer l as float64 [P][Hkv][hd]; the cache holds
-    per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][hd][P_max]."""
-    n = Bp * m.n_kv_heads * P_max * m.head_dim
-    x = kv.view(torch.int16)[2 * n * l: 2 * n * (l + 1)]
-    K = x[:n].view(Bp, m.n_kv_heads, P_max, m.head_dim)[bp, :, :P, :]
-    Vt = x[n:].view(Bp, m.n_kv_heads, m.head_dim, P_max)[bp, :, :, :P]
-    K = synth.bf16_bits_to_f32(K.permute(1, 0, 2).contiguous().cpu().numpy().view(np.uint16))
-    V = synth.bf16_bits_to_f32(Vt.permute(2, 0, 1).contiguous().cpu().numpy().view(np.uint16))
-    return K.astype(np.float64), V.astype(np.float64)
-
-
 def _check_prefix_layer0(M, kv, Bp, P_max, prefix, positions):
     lw = M.layer_dense(0)
     for bp in range(Bp):
-        K, V = _kv_layer(kv, FULL, Bp, P_max, 0, bp, prefix.shape[1])
+        K, V = kv_layer(kv, FULL, Bp, P_max, 0, bp, prefix.shape[1])
         _, k, v = M.qkv(M.embed(prefix[bp][positions]), lw, positions)
         assert rel_l2(K[positions], k) <= 1e-2
         assert rel_l2(V[positions], v) <= 1e-2
@@ -108,7 +96,7 @@ def _check_layers(M, got, kv, Bp, P_max, P, T, rows_by_canvas):
             r0 = b * T
             h_in = hd[l][r0:r0 + T].astype(np.float64)
             q, k, v = M.qkv(h_in, lw, pos)
-            Kp, Vp = _kv_layer(kv, FULL, Bp, P_max, l, 0 if Bp == 1 else b, P)
+            Kp, Vp = kv_layer(kv, FULL, Bp, P_max, l, 0 if Bp == 1 else b, P)
             kk = np.concatenate([Kp, k], axis=0)
             vv = np.concatenate([Vp, v], axis=0)
             o = om.attention(q[rows], kk, vv, np.ones((len(rows), P + T), dtype=bool))

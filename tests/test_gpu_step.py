@@ -22,7 +22,7 @@ from discrete_diffusion_decoding_amd.configs import WORKLOADS, SamplerParams
 from discrete_diffusion_decoding_amd.device import DeviceModel
 from oracle import model as om
 from oracle import sampler as osmp
-from tests.gpu_util import announce, check_experts, dev, host, rel_l2
+from tests.gpu_util import announce, check_experts, dev, host, kv_layer, rel_l2
 
 pytestmark = pytest.mark.gpu
 SEED = 1234
@@ -159,6 +159,47 @@ def test_layer_step_matches_oracle():
     assert rel_l2(hdump[1], h_o) <= 1e-2
     # the layer's own contribution (h_out - h_in) is also matched
     assert rel_l2(out - hc, h_o - hc) <= 2e-2
+
+
+def test_block_append_extends_prefix_cache():
+    """A finished block appended with dg_prefill_append leaves the cache as a
+    prefill of the whole sequence would: K/V of the new positions match the
+    oracle in every layer, the cached prefix and the unused tail are untouched,
+    and a denoising step over the longer prefix matches the oracle's."""
+    wl = WORKLOADS["tiny_step"]
+    m = wl.model
+    P0, n, T = wl.prefix_len, 32, wl.canvas_len
+    P, P_max = P0 + n, P0 + n + 32
+    announce(f"block append: upload (P0={P0}, n={n}, P_max={P_max})")
+    dm = DeviceModel(m, SEED)
+    prefix = synth.tokens(SEED, "prefix", (1, P0), m.vocab)
+    block = synth.tokens(SEED, "block", (1, n), m.vocab)
+    canvas_tok = synth.tokens(SEED, "canvas", (1, T), m.vocab)
+    kv = dm.kv_cache(1, P_max)
+    ws = dm.workspace(T, P + T)
+    dg.dg_prefill_prefix(dm.handle, dev(prefix), 1, P0, P_max, kv, ws)
+    before = kv.clone()
+    announce("block append: dg_prefill_append")
+    dg.dg_prefill_append(dm.handle, dev(block), 1, P0, n, P_max, kv, ws)
+    st = dm.canvas_state(1, T, tokens=canvas_tok, dumps=True)
+    sampler, keep = dg.make_sampler(SamplerParams(), synth.row_seeds(SEED, 1))
+    announce("block append: denoise step over the extended prefix")
+    dg.dg_denoise_step(dm.handle, kv, 1, P, P_max, 1, T, dg.make_canvas(st), 0, sampler, ws)
+    got = {k: host(v) for k, v in st.items()}
+    announce("block append: oracle")
+    M = om.Model(m, synth.SynthWeights(m, SEED, cache_layers=True))
+    kv_o, _ = M.prefill_tokens(np.concatenate([prefix[0], block[0]]))
+    for l in range(m.n_layers):
+        K, V = kv_layer(kv, m, 1, P_max, l, 0, P_max)
+        K0, V0 = kv_layer(before, m, 1, P_max, l, 0, P0)
+        assert np.array_equal(K[:P0], K0) and np.array_equal(V[:P0], V0), l
+        assert not K[P:].any() and not V[P:].any(), l
+        assert rel_l2(K[P0:P], kv_o[l][0][P0:P]) <= 1e-2, l
+        assert rel_l2(V[P0:P], kv_o[l][1][P0:P]) <= 1e-2, l
+    h, recs = M.canvas_hidden(M.canvas_input(canvas_tok[0], None), kv_o, P)
+    assert rel_l2(got["hidden_dump"][m.n_layers], h) <= 1e-2
+    assert rel_l2(got["logits_dump"][0], M.head(h)) <= 1e-2
+    dm.close()
 
 
 def test_tiny_block_equals_repeated_steps():
