@@ -134,6 +134,43 @@ def cpu_baseline(m_full, seed):
     }
 
 
+def multi_block(dg, synth, dm, prefix, B, T, P, nb, sp, seed, stream):
+    """Generation as the pages time it: the prompt is prefilled once, then nb
+    blocks are denoised one after another; each finished block is encoded onto
+    the cache (dg_prefill_append) so the next block sees it as prefix."""
+    import torch
+    P_max = P + nb * T
+    kv = dm.kv_cache(B, P_max)
+    ws = dm.workspace(B * T, P_max + T)
+    st = dm.canvas_state(B, T)
+    canvas = dg.make_canvas(st)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * nb)]
+    ev[0].record()
+    dg.dg_prefill_prefix(dm.handle, prefix, B, P, P_max, kv, ws, stream=stream)
+    ev[1].record()
+    steps, Pc = [], P
+    for k in range(nb):
+        seeds = synth.row_seeds(seed + 1 + k, B)
+        sampler, keep = dg.make_sampler(sp, seeds)
+        dg.dg_init_canvas(dm.handle, canvas, B, T, seeds, stream=stream)
+        dg.dg_generate_block(dm.handle, kv, B, Pc, P_max, B, T, canvas, sampler, ws, poll_every=8, stream=stream)
+        ev[2 + 2 * k].record()
+        dg.dg_prefill_append(dm.handle, st["tokens"], B, Pc, T, P_max, kv, ws, stream=stream)
+        ev[3 + 2 * k].record()
+        Pc += T
+        torch.cuda.synchronize()
+        steps.append(st["steps"].cpu().numpy().tolist())
+    torch.cuda.synchronize()
+    e2e = ev[0].elapsed_time(ev[-1])
+    blocks_ms = ev[1].elapsed_time(ev[-1])
+    append = [ev[2 + 2 * k].elapsed_time(ev[3 + 2 * k]) for k in range(nb)]
+    del kv, ws
+    return {"blocks": nb, "tokens": nb * B * T, "prompt": P, "prompt_prefill_ms": round(ev[0].elapsed_time(ev[1]), 2),
+            "e2e_ms": round(e2e, 2), "tok_s_e2e": round(nb * B * T / (e2e / 1e3), 2),
+            "tok_s_blocks": round(nb * B * T / (blocks_ms / 1e3), 2),
+            "append_ms": [round(x, 2) for x in append], "steps_taken": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +181,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--blocks", type=int, default=2,
+                    help="blocks generated one after another over a growing cache, each appended to it when "
+                         "finished (end-to-end leg, prompt prefill included; 0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one elementwise copy of 256 MiB fp32 first (reads and writes 256 MiB each): "
                          "the reference dispatch that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -250,6 +290,10 @@ def main():
         block_ms = e0.elapsed_time(e1)
         steps_taken = st["steps"].cpu().numpy().tolist()
         log(f"block: steps taken {steps_taken}, {block_ms:.1f} ms")
+    multi = None
+    if args.blocks > 0 and Bp == B:
+        multi = multi_block(dg, synth, dm, prefix, B, T, P, args.blocks, sp, args.seed, stream)
+        log(f"{args.blocks} blocks end to end: {multi['e2e_ms']:.1f} ms, {multi['tok_s_e2e']:.1f} tok/s")
     spb = max(steps_taken) if steps_taken else sp.max_steps
     tok_s = B * T / (spb * ms_per_step / 1e3)
 
@@ -286,6 +330,7 @@ def main():
                           "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms_per_step, 4)},
         "touched_experts_per_layer": float(np.mean(touched)),
         "kernel_ms": kernel_ms, "prefill_ms": round(prefill_ms, 2), "setup_s": round(setup_s, 1),
+        "multi_block": multi,
     }
     dm.close()
     if not args.no_cpu_baseline:
