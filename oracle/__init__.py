@@ -17,8 +17,10 @@ listed in each module's docstring.
 
 Modules
   rng      Philox4x32-10 (SC'11 definition), uniform mapping, own fp32 ln, Gumbel
-  model    forward pass: prefix prefill (causal), canvas step (bidirectional)
-  sampler  entropy, Gumbel-max sample, lock / re-randomise / stop, block loop
+  model    forward pass: prefix prefill (causal), canvas step (bidirectional),
+           one-token autoregressive decode against the cache
+  sampler  entropy, Gumbel-max sample, lock / re-randomise / stop, block loop,
+           the autoregressive next-token sample
 
 Parity unpinned: the whole-step output against the real DiffusionGemma (no
 trained weights or reference implementation are available); every function

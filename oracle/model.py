@@ -206,6 +206,27 @@ class Model:
             h = h + gate * (np.asarray(s_prev, dtype=F) @ g["self_cond_w"].T)
         return h
 
+    # -- autoregressive decoding (one token against the cache) ----------------
+    def decode_token(self, token, kv, P):
+        """One token at position P decoded against the cached K/V of positions
+        0..P-1 (the model also generates autoregressively: arXiv abstract page;
+        the per-step comparison of article section 5 is against this step).
+        The token's query sees every cached key and its own.  Returns the final
+        hidden [1, d] and per layer the token's own (K, V) [1, Hkv, hd]."""
+        h = self.embed([token])
+        pos = np.array([P])
+        new = []
+        for l in range(self.m.n_layers):
+            lw = self.layer_dense(l)
+            q, k, v = self.qkv(h, lw, pos)
+            kp, vp = kv[l]
+            kk = np.concatenate([kp[:P], k], axis=0)
+            vv = np.concatenate([vp[:P], v], axis=0)
+            o = attention(q, kk, vv, np.ones((1, P + 1), dtype=bool))
+            h, _ = self.post_attention(h, o, lw)
+            new.append((k, v))
+        return h, new
+
     def head(self, h):
         """Final RMSNorm and tied LM head: logits [T, V]."""
         g = self.glob()

@@ -22,6 +22,9 @@ step budget.  Random numbers are Philox4x32-10 words keyed by the row seed:
   Gumbel of (position i, vocab v) at step s: counter (v, i >> 2, s, 0), word i & 3
   re-randomised token of position i:         counter (i, 0, s, 1), word 0
   initial canvas token of position i:        counter (i, 0, 2^32 - 1, 1), word 0
+  autoregressive token at position p, vocab v: counter (v >> 2, p, 0, 2), word v & 3
+(the last is for the one-token AR step that the pages compare against, article
+section 5; the next token is a Gumbel-max sample of softmax(l / tau)).
 """
 from __future__ import annotations
 
@@ -187,3 +190,25 @@ def generate_block(model, kv, P, tokens0, seeds, sp, logits_fn=None, record=Fals
         if record:
             hist.append({"tokens": tokens.copy(), **info})
     return tokens, steps, hist
+
+
+def ar_inv_tau(tau) -> np.float32:
+    """fp32(1 / tau) of the fp32 temperature, the quotient taken in float64."""
+    return np.float32(1.0 / float(np.float32(tau)))
+
+
+def ar_sample(logits_f32, tau, seed, pos: int):
+    """Next token of an autoregressive step at decode position pos: argmax_v
+    fp32(l_v * inv_tau) + G_v, ties to the lowest v, with G_v the Gumbel noise
+    of Philox block (v >> 2, pos, 0, 2), word v & 3.  Returns (token, argmax of
+    the logits, entropy in nats, gap between the best two scores)."""
+    l = np.asarray(logits_f32, dtype=np.float32)
+    V = l.shape[0]
+    k0, k1 = seed_key(seed)
+    blocks = philox4x32(np.arange((V + 3) // 4, dtype=np.uint64), pos & 0xFFFFFFFF, 0, 2, k0, k1)
+    words = np.stack(blocks, axis=1).reshape(-1)[:V]
+    score = (l * ar_inv_tau(tau)).astype(np.float32) + gumbel_f32(uniform_open01(words))
+    tok = int(np.argmax(score))
+    rest = score.copy()
+    rest[tok] = -np.inf
+    return tok, int(np.argmax(l)), float(entropy(l)), float(score[tok] - np.max(rest))

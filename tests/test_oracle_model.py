@@ -195,6 +195,28 @@ def test_prefix_blind_to_canvas_and_canvas_fully_coupled(tiny_model):
         assert np.all(diff > 1e-9), (j, diff)           # every canvas row sees token j
 
 
+def test_decode_token_equals_prefill_of_the_longer_sequence(tiny_model):
+    """Decoding one token against the cache (one query row whose keys are the
+    cached positions and itself) equals the last row of a causal prefill of
+    the sequence extended by that token: final hidden state, and the token's
+    K and V in every layer.  Cache rows at or beyond P are not read."""
+    M = tiny_model
+    P = 20
+    tp = synth.tokens(3, "p", (P + 1,), TINY.vocab)
+    kv, _ = M.prefill_tokens(tp[:P])
+    junk = [(np.concatenate([k, np.full((5,) + k.shape[1:], 1e3)]),
+             np.concatenate([v, np.full((5,) + v.shape[1:], -1e3)])) for k, v in kv]
+    h, new = M.decode_token(tp[P], junk, P)
+    kv2, h2 = M.prefill_tokens(tp)
+    assert np.allclose(h, h2[P:], rtol=1e-11, atol=1e-12)
+    for l in range(TINY.n_layers):
+        assert np.allclose(new[l][0], kv2[l][0][P:], rtol=1e-11, atol=1e-12)
+        assert np.allclose(new[l][1], kv2[l][1][P:], rtol=1e-11, atol=1e-12)
+    # a token at position 0 attends to itself only
+    h0, _ = M.decode_token(tp[0], [(k[:0], v[:0]) for k, v in kv], 0)
+    assert np.allclose(h0, M.prefill_tokens(tp[:1])[1], rtol=1e-11, atol=1e-12)
+
+
 def test_entropy_bounds_and_special_cases():
     V = 2048
     assert np.isclose(entropy(np.zeros(V)), np.log(V), rtol=0, atol=1e-12)

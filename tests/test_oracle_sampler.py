@@ -141,3 +141,28 @@ def test_init_canvas_reproducible_uniform():
     assert np.array_equal(a, osmp.init_canvas(77, 256, 262144))
     assert a.min() >= 0 and a.max() < 262144 and len(set(a.tolist())) > 250
     assert not np.array_equal(a, osmp.init_canvas(78, 256, 262144))
+
+
+def test_ar_sample_is_a_softmax_sample_at_its_temperature():
+    """The autoregressive next token is a Gumbel-max draw, so over seeds (and
+    over decode positions) it is distributed as softmax(l / tau); a tiny tau
+    gives the argmax; the entropy and argmax outputs are those of the logits."""
+    l = np.array([1.0, 0.0, -0.5, 2.0, 0.3, -1.0, 0.8, 0.1, 0.4, -0.2], np.float32)
+    tau = 0.7
+    z = np.exp((l.astype(np.float64) - l.max()) / tau)
+    p = z / z.sum()
+    n = 4000
+    by_seed = np.bincount([osmp.ar_sample(l, tau, 1000 + s, 5)[0] for s in range(n)], minlength=l.size)
+    by_pos = np.bincount([osmp.ar_sample(l, tau, 77, 100 + q)[0] for q in range(n)], minlength=l.size)
+    assert stats.chisquare(by_seed, n * p).pvalue > 1e-4
+    assert stats.chisquare(by_pos, n * p).pvalue > 1e-4
+    # draws at different positions are independent: they agree about sum p^2 of the time
+    a = np.array([osmp.ar_sample(l, tau, 5 + s, 9)[0] for s in range(n)])
+    b = np.array([osmp.ar_sample(l, tau, 5 + s, 10)[0] for s in range(n)])
+    agree = float(np.mean(a == b))
+    assert abs(agree - float(np.sum(p * p))) < 4 * np.sqrt(agree * (1 - agree) / n)
+    for s in range(20):
+        tok, amax, H, gap = osmp.ar_sample(l, 1e-4, s, 3)
+        assert tok == 3 and amax == 3 and gap > 0
+    assert np.isclose(osmp.ar_sample(l, 1.0, 0, 0)[2], osmp.entropy(l), rtol=0, atol=1e-12)
+    assert osmp.ar_inv_tau(0.8) == np.float32(1.25)
