@@ -136,6 +136,17 @@ struct SampleArgs {
   int32_t* stopped; int32_t* steps; int32_t* all_stopped;
   const int32_t* flag;
 };
+// autoregressive next-token sample: B rows of V logits (row pitch ldl), one
+// decode position; V and ldl multiples of 4
+struct ArSampleArgs {
+  const float* logits; int B, V; long ldl;
+  float inv_tau; int pos;
+  uint64_t seeds[16];
+  int vsplit;                       // vocab slices per row
+  float* part;                      // [B][vsplit][8]
+  int32_t* next; int32_t* argmax; float* entropy;   // [B]; argmax / entropy may be null
+};
+hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s);
 hipError_t sample_partial(const SampleArgs& a, hipStream_t s);
 hipError_t sample_finish(const SampleArgs& a, hipStream_t s);
 hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,

@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "dg.h"
@@ -487,7 +488,10 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       a.out = o; a.opart = at<bf16_t>(ws, p.opart); a.mlpart = at<float>(ws, p.ml); a.flag = ps.flag;
       if (ps.prefill) {
         a.k1 = Kc; a.vt1 = Vc; a.k1_bstride = 0; a.k1_hstride = (long)ps.P_max * hd;
-        a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max; a.n1 = ps.q0 + R; a.nb1 = 1;
+        // keys up to the last row's position, in whole 32-key tiles: the causal
+        // mask hides the tail, so a pass may start and end anywhere
+        a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max;
+        a.n1 = cdiv(ps.q0 + R, 32) * 32; a.nb1 = 1;
         a.n2 = 0; a.causal = 1; a.qpos0 = ps.q0;
       } else {
         const int T = ps.per_batch;
@@ -646,12 +650,12 @@ static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* h
                               int P_max, void* kv, void* ws, size_t ws_bytes, hipStream_t st) {
   if (!m || !kv || !ws || (!tokens && !hidden)) return DG_ERR_ARG;
   if (Bp < 1 || n < 1 || P0 < 0 || P_max < P0 + n) return DG_ERR_ARG;
-  if (P0 % 32 || n % 32 || P_max % 32) return DG_ERR_SHAPE;
+  if (P_max % 32) return DG_ERR_SHAPE;
   if (tokens && m->d.vocab == 0) return DG_ERR_ARG;
   const int P = P0 + n;
-  // largest chunk (multiple of 32 rows) whose workspace fits
+  // largest chunk whose workspace fits: all n rows (at most 4096), else a multiple of 32
   int chunk = 0;
-  for (int c = std::min(n, 4096); c >= 32; c -= 32)
+  for (int c = std::min(n, 4096); c >= 1; c = c > 32 ? (c - 1) / 32 * 32 : 0)
     if (make_plan(m->d, c, P).total <= ws_bytes) { chunk = c; break; }
   if (chunk == 0) return DG_ERR_WORKSPACE;
   const Plan p = make_plan(m->d, chunk, P);
@@ -682,6 +686,7 @@ static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* h
 extern "C" dg_status dg_prefill_prefix(dg_model* m, const int32_t* prefix, int32_t Bp, int32_t P, int32_t P_max,
                                        void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
   if (!prefix) return DG_ERR_ARG;
+  if (P % 32) return DG_ERR_SHAPE;
   return prefill_impl(m, prefix, nullptr, Bp, 0, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
 }
 
@@ -694,7 +699,57 @@ extern "C" dg_status dg_prefill_append(dg_model* m, const int32_t* tokens, int32
 extern "C" dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, int32_t Bp, int32_t P,
                                        int32_t P_max, void* kv, void* ws, size_t ws_bytes, dg_stream_t stream) {
   if (!prefix_hidden) return DG_ERR_ARG;
+  if (P % 32) return DG_ERR_SHAPE;
   return prefill_impl(m, nullptr, prefix_hidden, Bp, 0, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// One autoregressive step per sequence: the token at position P is encoded
+// against the cached positions 0..P-1 (its K/V written at P), then the final
+// norm, the LM head and the next-token sample.  Sequences run one after
+// another, each a one-row pass over the layers.
+extern "C" dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int32_t P_max, const int32_t* token,
+                                float tau, const uint64_t* row_seeds, int32_t* next, int32_t* argmax,
+                                float* entropy, float* logits_dump, void* ws, size_t ws_bytes,
+                                dg_stream_t stream) {
+  if (!m || !kv || !token || !next || !row_seeds || !ws) return DG_ERR_ARG;
+  if (m->d.vocab == 0) return DG_ERR_UNSUPPORTED;
+  if (B < 1 || B > 16 || P < 0 || P_max < P + 1 || !(tau > 0.f) || !std::isfinite(tau)) return DG_ERR_ARG;
+  if (P_max % 32 || m->d.vocab % 4) return DG_ERR_SHAPE;
+  const Plan p = make_plan(m->d, 1, P + 1);
+  if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
+  const dg_model_desc& d = m->d;
+  const int V = d.vocab, D = d.d_model;
+  hipStream_t st = (hipStream_t)stream;
+  const float inv_tau = (float)(1.0 / (double)tau);
+  float* h = at<float>(ws, p.h);
+  bf16_t* xn = at<bf16_t>(ws, p.xn);
+  for (int b = 0; b < B; ++b) {
+    DG_CK(embed_rows(token + b, (const bf16_t*)m->w.embed, 1, D, h, nullptr, st));
+    DG_CK(rmsnorm_rows(h, m->layers[0] + m->lay.attn_norm, 1, D, d.rms_eps, xn, nullptr, nullptr,
+                       Partials{nullptr, 0, 0}, nullptr, nullptr, st));
+    Pass ps{};
+    ps.rows = 1; ps.B = 1; ps.per_batch = 1; ps.pos0 = P; ps.prefill = true; ps.bp = b; ps.q0 = P;
+    ps.kv = (const bf16_t*)kv; ps.kv_Bp = B; ps.Bp = 1; ps.P = 0; ps.P_max = P_max;
+    ps.final_norm = true; ps.flag = nullptr;
+    dg_status s = run_layers(m, p, ws, ps, st);
+    if (s != DG_OK) return s;
+    float* logits = logits_dump ? logits_dump + (size_t)b * V : at<float>(ws, p.logits);
+    {
+      GemmArgs g = gargs();
+      g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D;
+      g.C = logits; g.ldc = V;
+      ProfScope ps_(m, DG_PROF_LMHEAD, st);
+      DG_CK(dense_gemm(EPI_STORE_F32, g, 1, st));
+    }
+    ArSampleArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    sa.logits = logits; sa.B = 1; sa.V = V; sa.ldl = V; sa.inv_tau = inv_tau; sa.pos = P;
+    sa.seeds[0] = row_seeds[b]; sa.vsplit = p.vsplit; sa.part = at<float>(ws, p.spart);
+    sa.next = next + b; sa.argmax = argmax ? argmax + b : nullptr; sa.entropy = entropy ? entropy + b : nullptr;
+    ProfScope ps_(m, DG_PROF_SAMPLER, st);
+    DG_CK(ar_sample(sa, st));
+  }
+  return DG_OK;
 }
 
 // ---------------------------------------------------------------------------

@@ -67,6 +67,64 @@ __device__ __forceinline__ float gumbel_score(float scaled, uint32_t w) {
   return add_noise(scaled, dg_gumbel(dg_uniform_open01(w)));
 }
 
+// one logit into a thread's online (max, Z, A) triple and argmax; entries
+// arrive in increasing vocab order, so ties keep the lower index
+__device__ __forceinline__ void stat_push(Stat& t, float l, int v) {
+  if (l > t.m) {
+    if (t.m == -INFINITY) {
+      t.Z = 1.f; t.A = 0.f;
+    } else {
+      const float f = __expf(t.m - l);
+      t.A = f * (t.A + (t.m - l) * t.Z);
+      t.Z = f * t.Z + 1.f;
+    }
+    t.m = l;
+  } else {
+    const float e = __expf(l - t.m);
+    t.Z += e;
+    t.A += e * (l - t.m);
+  }
+  if (l > t.av) { t.av = l; t.ai = v; }
+}
+
+// screened Gumbel score of one entry into the best / runner-up pair
+struct Screen {
+  float b1, b2, bl;   // best / runner-up screened score, best's scaled logit
+  uint32_t bw;        // best's Philox word
+  int bv;             // best's vocab index
+};
+__device__ __forceinline__ void screen_init(Screen& c) {
+  c.b1 = c.b2 = -INFINITY; c.bl = 0.f; c.bw = 0u; c.bv = 0x7FFFFFFF;
+}
+__device__ __forceinline__ void screen_push(Screen& c, float l, float inv_tau, uint32_t w, int v) {
+  const float scaled = scale_logit(l, inv_tau);
+  const float sc = add_noise(scaled, gumbel_screen(dg_uniform_open01(w)));
+  if (sc > c.b1) {
+    c.b2 = c.b1; c.b1 = sc; c.bl = scaled; c.bw = w; c.bv = v;
+  } else {
+    c.b2 = fmaxf(c.b2, sc);
+  }
+}
+// the exact score of the screened best; true when the runner-up is within
+// twice the screening error, so the entries must be rescored exactly
+__device__ __forceinline__ bool screen_close(const Screen& c, Stat& t) {
+  if (c.bv == 0x7FFFFFFF) return false;   // no entries
+  const float tol = kGumbelScreen + fmaxf(fabsf(c.b1), fabsf(c.b2)) * 2.5e-7f;
+  t.gv = gumbel_score(c.bl, c.bw);
+  t.gi = c.bv;
+  return c.b2 >= c.b1 - 2.f * tol;
+}
+__device__ __forceinline__ void stat_wave_merge(Stat& t) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Stat y;
+    y.m = __shfl_xor(t.m, o, 64); y.Z = __shfl_xor(t.Z, o, 64); y.A = __shfl_xor(t.A, o, 64);
+    y.av = __shfl_xor(t.av, o, 64); y.ai = __shfl_xor(t.ai, o, 64);
+    y.gv = __shfl_xor(t.gv, o, 64); y.gi = __shfl_xor(t.gi, o, 64);
+    stat_merge(t, y);
+  }
+}
+
 __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   if (a.flag && *a.flag) return;
   __shared__ Stat red[4][4];
@@ -89,16 +147,11 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   // screening error of the best, the thread rescores all its entries of that
   // row exactly (rare), so the result is the exact maximum in every case.
   Stat st[4];
-  float b1[4], b2[4], bl[4];   // best / runner-up screened score, best's scaled logit
-  uint32_t bw[4];
-  int bv[4];
+  Screen sc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     st[j] = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
-    b1[j] = b2[j] = -INFINITY;
-    bl[j] = 0.f;
-    bw[j] = 0u;
-    bv[j] = 0x7FFFFFFF;
+    screen_init(sc[j]);
   }
   // entries v and v + 256 alternate between two register sets: the loads of
   // the next entry are in flight while one is processed (indices clamped to
@@ -107,34 +160,8 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
     const dg_u32x4 w = dg_philox4x32_10((uint32_t)v, (uint32_t)pg, (uint32_t)s, 0u, k0, k1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float l = lv[j];
-      Stat& t = st[j];
-      if (l > t.m) {
-        if (t.m == -INFINITY) {
-          t.Z = 1.f; t.A = 0.f;
-        } else {
-          const float f = __expf(t.m - l);
-          t.A = f * (t.A + (t.m - l) * t.Z);
-          t.Z = f * t.Z + 1.f;
-        }
-        t.m = l;
-      } else {
-        const float e = __expf(l - t.m);
-        t.Z += e;
-        t.A += e * (l - t.m);
-      }
-      if (l > t.av) { t.av = l; t.ai = v; }   // v increasing per thread: ties keep the lower index
-      const float scaled = scale_logit(l, inv_tau);
-      const float sc = add_noise(scaled, gumbel_screen(dg_uniform_open01(w.x[j])));
-      if (sc > b1[j]) {
-        b2[j] = b1[j];
-        b1[j] = sc;
-        bl[j] = scaled;
-        bw[j] = w.x[j];
-        bv[j] = v;
-      } else {
-        b2[j] = fmaxf(b2[j], sc);
-      }
+      stat_push(st[j], lv[j], v);
+      screen_push(sc[j], lv[j], inv_tau, w.x[j], v);
     }
   };
   const int vlast = v1 - 1;
@@ -154,13 +181,8 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   }
   unsigned slow = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (bv[j] == 0x7FFFFFFF) continue;   // no entries
-    const float tol = kGumbelScreen + fmaxf(fabsf(b1[j]), fabsf(b2[j])) * 2.5e-7f;
-    if (b2[j] >= b1[j] - 2.f * tol) slow |= 1u << j;
-    st[j].gv = gumbel_score(bl[j], bw[j]);
-    st[j].gi = bv[j];
-  }
+  for (int j = 0; j < 4; ++j)
+    if (screen_close(sc[j], st[j])) slow |= 1u << j;
   if (slow) {
     for (int v = v0 + threadIdx.x; v < v1; v += 256) {
       const dg_u32x4 w = dg_philox4x32_10((uint32_t)v, (uint32_t)pg, (uint32_t)s, 0u, k0, k1);
@@ -176,14 +198,7 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      Stat y;
-      y.m = __shfl_xor(st[j].m, o, 64); y.Z = __shfl_xor(st[j].Z, o, 64); y.A = __shfl_xor(st[j].A, o, 64);
-      y.av = __shfl_xor(st[j].av, o, 64); y.ai = __shfl_xor(st[j].ai, o, 64);
-      y.gv = __shfl_xor(st[j].gv, o, 64); y.gi = __shfl_xor(st[j].gi, o, 64);
-      stat_merge(st[j], y);
-    }
+    stat_wave_merge(st[j]);
     if (lane == 0) red[wave][j] = st[j];
   }
   __syncthreads();
@@ -290,6 +305,86 @@ hipError_t sample_finish(const SampleArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !a.all_stopped) return e;
   hipLaunchKernelGGL(all_stopped_kernel, dim3(1), dim3(64), 0, s, a.stopped, a.B, a.all_stopped);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Next-token sampler of the autoregressive step (one position per row; the
+// step the article's section 5 compares a denoising step with): Gumbel-max
+// over softmax(l / tau), plus the argmax and entropy of the logits.  The
+// noise of vocab entry v at decode position p is word v & 3 of Philox block
+// (v >> 2, p, 0, 2) keyed by the row seed, so one 10-round call covers four
+// consecutive entries, read as one float4.  One workgroup per (row, vocab
+// slice of whole blocks of four); the finish kernel merges the slices.
+__global__ __launch_bounds__(256) void ar_sample_partial_kernel(ArSampleArgs a) {
+  __shared__ Stat red[4];
+  const int b = blockIdx.x / a.vsplit, sl = blockIdx.x % a.vsplit;
+  const uint64_t seed = a.seeds[b];
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  const int ng = a.V / 4;
+  const int per = (ng + a.vsplit - 1) / a.vsplit;
+  const int g0 = sl * per, g1 = min(ng, g0 + per);
+  const float* l = a.logits + (long)b * a.ldl;
+  Stat t = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
+  Screen c;
+  screen_init(c);
+  for (int g = g0 + (int)threadIdx.x; g < g1; g += 256) {
+    const float4 x = *reinterpret_cast<const float4*>(l + 4L * g);
+    const dg_u32x4 w = dg_philox4x32_10((uint32_t)g, (uint32_t)a.pos, 0u, 2u, k0, k1);
+    const float lv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      stat_push(t, lv[j], 4 * g + j);
+      screen_push(c, lv[j], a.inv_tau, w.x[j], 4 * g + j);
+    }
+  }
+  if (screen_close(c, t)) {
+    for (int g = g0 + (int)threadIdx.x; g < g1; g += 256) {
+      const dg_u32x4 w = dg_philox4x32_10((uint32_t)g, (uint32_t)a.pos, 0u, 2u, k0, k1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * g + j;
+        const float sc = gumbel_score(scale_logit(l[v], a.inv_tau), w.x[j]);
+        if (sc > t.gv || (sc == t.gv && v < t.gi)) { t.gv = sc; t.gi = v; }
+      }
+    }
+  }
+  stat_wave_merge(t);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Stat r = red[0];
+    for (int w = 1; w < 4; ++w) stat_merge(r, red[w]);
+    float* o = a.part + ((long)b * a.vsplit + sl) * 8;
+    o[0] = r.m; o[1] = r.Z; o[2] = r.A; o[3] = r.av;
+    o[4] = __int_as_float(r.ai); o[5] = r.gv; o[6] = __int_as_float(r.gi); o[7] = 0.f;
+  }
+}
+
+__global__ __launch_bounds__(64) void ar_sample_finish_kernel(ArSampleArgs a) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  Stat t = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
+  for (int sl = lane; sl < a.vsplit; sl += 64) {
+    const float* p = a.part + ((long)b * a.vsplit + sl) * 8;
+    Stat y{p[0], p[1], p[2], p[3], __float_as_int(p[4]), p[5], __float_as_int(p[6])};
+    stat_merge(t, y);
+  }
+  stat_wave_merge(t);
+  if (lane == 0) {
+    a.next[b] = t.gi;
+    if (a.argmax) a.argmax[b] = t.ai;
+    if (a.entropy) a.entropy[b] = logf(t.Z) - t.A / t.Z;
+  }
+}
+
+hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s) {
+  if (a.B < 1 || a.B > 16 || a.V % 4 != 0 || a.ldl % 4 != 0 || a.vsplit < 1 || !a.next || !a.part)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ar_sample_partial_kernel, dim3(a.B * a.vsplit), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ar_sample_finish_kernel, dim3(a.B), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -76,6 +76,8 @@ def lib():
             "dg_prefill_prefix": (st, [vp, vp, i32, i32, i32, vp, vp, sz, vp]),
             "dg_prefill_append": (st, [vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
             "dg_prefill_hidden": (st, [vp, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "dg_ar_step": (st, [vp, vp, i32, i32, i32, vp, C.c_float, C.POINTER(C.c_uint64), vp, vp, vp, vp,
+                                vp, sz, vp]),
             "dg_forward_hidden": (st, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dg_denoise_step": (st, [vp, vp, i32, i32, i32, i32, i32, C.POINTER(Canvas), i32,
                                      C.POINTER(Sampler), vp, sz, vp]),
@@ -163,6 +165,14 @@ def dg_prefill_prefix(h, prefix, Bp, P, P_max, kv, ws, stream=None):
 def dg_prefill_append(h, tokens, Bp, P0, n, P_max, kv, ws, stream=None):
     _ck(lib().dg_prefill_append(h, _ptr(tokens), Bp, P0, n, P_max, _ptr(kv), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)), "dg_prefill_append")
+
+
+def dg_ar_step(h, kv, B, P, P_max, token, tau, seeds, nxt, ws, argmax=None, entropy=None, logits_dump=None,
+               stream=None):
+    arr = (C.c_uint64 * len(seeds))(*[int(s) for s in seeds])
+    _ck(lib().dg_ar_step(h, _ptr(kv), B, P, P_max, _ptr(token), tau, C.cast(arr, C.POINTER(C.c_uint64)), _ptr(nxt),
+                         _ptr(argmax), _ptr(entropy), _ptr(logits_dump), _ptr(ws), ws.numel() * ws.element_size(),
+                         _stream(stream)), "dg_ar_step")
 
 
 def dg_prefill_hidden(h, prefix_hidden, Bp, P, P_max, kv, ws, stream=None):

@@ -31,8 +31,12 @@
  *     n_heads / n_kv_heads in {1, 2, 4}; d_model, d_expert, d_shared and
  *     n_heads*head_dim multiples of 64 and d_model <= 4096; n_experts <= 255;
  *     top_k in {1, 2, 4, 8}; canvas length T a multiple of 32 and <= 1024; prefix
- *     lengths P and capacities P_max multiples of 32; batch B <= 16; vocab a
- *     multiple of 128.
+ *     lengths P of a prefill or denoising step and capacities P_max multiples of
+ *     32 (dg_prefill_append and dg_ar_step start at any position); batch B <= 16;
+ *     vocab a multiple of 128.
+ *   - Cache positions not yet written must hold finite values (zero the cache
+ *     once when allocating it): a pass that ends inside a 32-key tile reads the
+ *     whole tile and masks the unwritten keys.
  */
 #ifndef DG_H
 #define DG_H
@@ -181,10 +185,31 @@ dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, int32_t Bp,
  * article section 2 and section 5): encodes tokens int32 [Bp][n] at positions
  * P0 .. P0+n-1 of each prompt, attending causally to the K/V of positions
  * 0 .. P0-1 already in kv and to each other, and writes their K and V into kv.
- * dg_prefill_prefix is the case P0 = 0.  P0 and n multiples of 32, n >= 32,
- * P0 + n <= P_max; else DG_ERR_SHAPE / DG_ERR_ARG before any device work. */
+ * dg_prefill_prefix is the case P0 = 0.  Any P0 >= 0 and n >= 1 with
+ * P0 + n <= P_max (else DG_ERR_ARG before any device work); a denoising step
+ * over the result needs P0 + n to be a multiple of 32. */
 dg_status dg_prefill_append(dg_model* m, const int32_t* tokens, int32_t Bp, int32_t P0, int32_t n, int32_t P_max,
                             void* kv, void* ws, size_t ws_bytes, dg_stream_t stream);
+
+/* One autoregressive decoding step (the model still generates token by token:
+ * arXiv abstract page; article section 5 compares a denoising step with this
+ * one) for B sequences with caches kv [B] of capacity P_max:
+ *   - token int32 [B] (device): the token at position P of each sequence; it
+ *     is encoded against the cached positions 0..P-1 and its K/V written at P;
+ *   - then the final norm, the LM head and the next token
+ *       next[b] = argmax_v fp32(l_v * inv_tau) + G_v   (ties -> lowest v),
+ *     inv_tau = fp32(1 / tau) taken in double, G_v the Gumbel variate of word
+ *     v & 3 of Philox4x32-10 block (v >> 2, P, 0, 2) keyed by row_seeds[b]
+ *     (host [B]): a sample of softmax(l / tau);
+ *   - argmax [B] (argmax of the logits), entropy [B] (nats, of softmax(l)) and
+ *     logits_dump fp32 [B][V] are optional outputs (NULL to skip).
+ * `next` may be the `token` buffer (the next call then reads it).  Sequences
+ * run one after another, each one row through every layer.  Needs
+ * dg_workspace_bytes(m, 1, P + 1).  B in 1..16, P + 1 <= P_max, tau > 0,
+ * vocab a multiple of 4; else a negative status before any device work. */
+dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int32_t P_max, const int32_t* token, float tau,
+                     const uint64_t* row_seeds, int32_t* next, int32_t* argmax, float* entropy, float* logits_dump,
+                     void* ws, size_t ws_bytes, dg_stream_t stream);
 
 /* Layer stack on canvas hidden states: hidden fp32 [B][T][d] in/out (input of
  * layer 0 in, output of the last layer out), bidirectional over the canvas and

@@ -118,15 +118,39 @@ def test_prefill_append_rejects_bad_arguments_before_any_device_work():
     L = dg.lib()
     kv, ws, tok = C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000)
     big = 1 << 30
-    # P0 or n not a multiple of 32
-    assert L.dg_prefill_append(h, tok, 1, 48, 32, 128, kv, ws, big, None) == dg.DG_ERR_SHAPE
-    assert L.dg_prefill_append(h, tok, 1, 64, 40, 128, kv, ws, big, None) == dg.DG_ERR_SHAPE
+    # capacity not a multiple of 32 (any start and length are accepted)
+    assert L.dg_prefill_append(h, tok, 1, 48, 40, 100, kv, ws, big, None) == dg.DG_ERR_SHAPE
     # P0 + n beyond the cache capacity; no tokens; n < 1
     assert L.dg_prefill_append(h, tok, 1, 96, 64, 128, kv, ws, big, None) == dg.DG_ERR_ARG
     assert L.dg_prefill_append(h, None, 1, 64, 32, 128, kv, ws, big, None) == dg.DG_ERR_ARG
     assert L.dg_prefill_append(h, tok, 1, 64, 0, 128, kv, ws, big, None) == dg.DG_ERR_ARG
     # workspace too small
     assert L.dg_prefill_append(h, tok, 1, 64, 32, 128, kv, ws, 1024, None) == dg.DG_ERR_WORKSPACE
+    dg.dg_model_destroy(h)
+
+
+def test_ar_step_rejects_bad_arguments_before_any_device_work():
+    w, keep = _fake_weights(TINY)
+    h = dg.dg_model_create(TINY, w)
+    L = dg.lib()
+    kv, ws, tok, nxt = C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000), C.c_void_p(0x6000)
+    seeds = (C.c_uint64 * 16)(*range(16))
+    sp = C.cast(seeds, C.POINTER(C.c_uint64))
+    big = 1 << 30
+
+    def call(B=1, P=70, P_max=96, tau=0.8, token=tok, seeds=sp, ws_bytes=big, next_=nxt):
+        return L.dg_ar_step(h, kv, B, P, P_max, token, tau, seeds, next_, None, None, None, ws, ws_bytes, None)
+
+    assert call(P=96) == dg.DG_ERR_ARG       # no room for position P
+    assert call(B=0) == dg.DG_ERR_ARG
+    assert call(B=17) == dg.DG_ERR_ARG
+    assert call(tau=0.0) == dg.DG_ERR_ARG
+    assert call(tau=float("nan")) == dg.DG_ERR_ARG
+    assert call(token=None) == dg.DG_ERR_ARG
+    assert call(next_=None) == dg.DG_ERR_ARG
+    assert call(seeds=None) == dg.DG_ERR_ARG
+    assert call(P_max=100) == dg.DG_ERR_SHAPE
+    assert call(ws_bytes=1024) == dg.DG_ERR_WORKSPACE
     dg.dg_model_destroy(h)
 
 

@@ -267,3 +267,48 @@ def test_long_block_four_canvases_sampled_rows(full):
         _check_sampler(got, b, T, int(seeds[b]), 0, sp, stopped_expect=False)
     del kv, ws, st
     torch.cuda.empty_cache()
+
+
+def test_full_ar_steps(full):
+    """Autoregressive steps of the full model after a 2048-token prompt, at
+    positions 2048..2050 (the last two unaligned): the K/V each step writes
+    in layer 0 match the oracle's projection of the token's embedding; on the
+    GPU's own fp32 logits over the full vocabulary the sampled token and the
+    argmax are the oracle sampler's, bit for bit, and the entropy agrees."""
+    dm, M = full
+    P0, n, tau = 2048, 3, 0.8
+    P_max = P0 + 32
+    prefix = synth.tokens(SEED, "prefix", (1, P0), FULL.vocab)
+    seeds = synth.row_seeds(SEED + 7, 1)
+    kv = dm.kv_cache(1, P_max)
+    ws = dm.workspace(256, P_max)
+    stream = torch.cuda.Stream()
+    announce("full ar: prefill 2048")
+    dg.dg_prefill_prefix(dm.handle, dev(prefix), 1, P0, P_max, kv, ws, stream=stream)
+    tok = dev(np.array([int(prefix[0, -1])], np.int32))
+    toks_in = [int(prefix[0, -1])]
+    logits = torch.zeros(n, FULL.vocab, device="cuda")
+    nxt = torch.zeros(n, dtype=torch.int32, device="cuda")
+    amax = torch.zeros(n, dtype=torch.int32, device="cuda")
+    ent = torch.zeros(n, device="cuda")
+    for i in range(n):
+        announce(f"full ar: dg_ar_step at P={P0 + i}")
+        dg.dg_ar_step(dm.handle, kv, 1, P0 + i, P_max, tok, tau, seeds, nxt[i:i + 1], ws, argmax=amax[i:i + 1],
+                      entropy=ent[i:i + 1], logits_dump=logits[i:i + 1], stream=stream)
+        tok = nxt[i:i + 1]
+    torch.cuda.synchronize()
+    lg, nx, am, H = host(logits), host(nxt), host(amax), host(ent)
+    K, V = kv_layer(kv, FULL, 1, P_max, 0, 0, P_max)
+    toks_in += [int(x) for x in nx[:-1]]
+    announce("full ar: oracle checks")
+    lw = M.layer_dense(0)
+    pos = np.arange(P0, P0 + n)
+    _, k, v = M.qkv(M.embed(np.array(toks_in)), lw, pos)
+    assert rel_l2(K[P0:P0 + n], k) <= 1e-2
+    assert rel_l2(V[P0:P0 + n], v) <= 1e-2
+    assert not K[P0 + n:].any() and not V[P0 + n:].any()
+    for i in range(n):
+        assert np.isfinite(lg[i]).all()
+        t_g, a_g, H_g, _ = osmp.ar_sample(lg[i], tau, seeds[0], P0 + i)
+        assert nx[i] == t_g and am[i] == a_g, i
+        assert np.isclose(H[i], H_g, rtol=1e-4), i

@@ -202,6 +202,61 @@ def test_block_append_extends_prefix_cache():
     dm.close()
 
 
+def test_ar_decode_matches_oracle():
+    """Autoregressive steps (dg_ar_step) after a 64-token prompt, at positions
+    64..69 (one row, unaligned): every step's logits and the K/V it writes at
+    its position in every layer match the oracle's one-token decode; on the
+    GPU's own logits the sampled token, argmax and entropy are the oracle
+    sampler's (token and argmax bit-exact); against the oracle's logits the
+    token is exact wherever the winning gap exceeds what the logit error
+    allows.  Each step decodes the GPU's previous token (teacher forcing)."""
+    wl = WORKLOADS["tiny_step"]
+    m = wl.model
+    P0, n, P_max, tau = wl.prefix_len, 6, 96, 0.8
+    announce(f"ar decode: upload, prefill {P0}")
+    dm = DeviceModel(m, SEED)
+    prompt = synth.tokens(SEED, "prefix", (1, P0 + 1), m.vocab)
+    seeds = synth.row_seeds(SEED, 1)
+    kv = dm.kv_cache(1, P_max)
+    ws = dm.workspace(P0, P_max)
+    dg.dg_prefill_prefix(dm.handle, dev(prompt[:, :P0]), 1, P0, P_max, kv, ws)
+    tok = dev(prompt[:, P0].astype(np.int32))
+    logits = torch.zeros(n, m.vocab, device="cuda")
+    nxt = torch.zeros(n, dtype=torch.int32, device="cuda")
+    amax = torch.zeros(n, dtype=torch.int32, device="cuda")
+    ent = torch.zeros(n, device="cuda")
+    for i in range(n):
+        announce(f"ar decode: dg_ar_step at P={P0 + i}")
+        dg.dg_ar_step(dm.handle, kv, 1, P0 + i, P_max, tok, tau, seeds, nxt[i:i + 1], ws, argmax=amax[i:i + 1],
+                      entropy=ent[i:i + 1], logits_dump=logits[i:i + 1])
+        tok = nxt[i:i + 1]
+    lg, nx, am, H = host(logits), host(nxt), host(amax), host(ent)
+    kvs = [kv_layer(kv, m, 1, P_max, l, 0, P_max) for l in range(m.n_layers)]
+    dm.close()
+    announce("ar decode: oracle")
+    M = om.Model(m, synth.SynthWeights(m, SEED, cache_layers=True))
+    kv_o, _ = M.prefill_tokens(prompt[0, :P0])
+    for i in range(n):
+        P = P0 + i
+        t_in = int(prompt[0, P0]) if i == 0 else int(nx[i - 1])
+        h, new = M.decode_token(t_in, kv_o, P)
+        lo = M.head(h)[0]
+        assert rel_l2(lg[i], lo) <= 1e-2, i
+        for l in range(m.n_layers):
+            assert rel_l2(kvs[l][0][P], new[l][0][0]) <= 1e-2, (i, l)
+            assert rel_l2(kvs[l][1][P], new[l][1][0]) <= 1e-2, (i, l)
+            kv_o[l] = (np.concatenate([kv_o[l][0], new[l][0]]), np.concatenate([kv_o[l][1], new[l][1]]))
+        # the sampler on the GPU's own logits: exact
+        t_g, a_g, H_g, _ = osmp.ar_sample(lg[i], tau, seeds[0], P)
+        assert nx[i] == t_g and am[i] == a_g, i
+        assert np.isclose(H[i], H_g, rtol=1e-4), i
+        # against the oracle's logits: exact outside the near ties the logit error allows
+        dl = float(np.abs(lg[i] - lo).max())
+        t_o, _, _, gap = osmp.ar_sample(lo.astype(np.float32), tau, seeds[0], P)
+        if gap > 2.5 * dl * float(osmp.ar_inv_tau(tau)) + 1e-6:
+            assert nx[i] == t_o, i
+
+
 def test_tiny_block_equals_repeated_steps():
     """dg_generate_block (device-driven step index, stop flag) equals the same
     number of host-driven dg_denoise_step calls, bit for bit."""
