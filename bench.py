@@ -171,6 +171,58 @@ def multi_block(dg, synth, dm, prefix, B, T, P, nb, sp, seed, stream):
             "append_ms": [round(x, 2) for x in append], "steps_taken": steps}
 
 
+# kernel classes summed into the groups the article's section 5 compares
+AR_GROUPS = {"moe": ("router", "expert_gateup", "expert_down", "shared"), "attention": ("attn",),
+             "sampling": ("lmhead", "sampler", "softemb")}
+
+
+def ar_leg(dg, synth, dm, prefix, P, n, seed, stream, step_kernel_ms, step_ms):
+    """Autoregressive decoding of n tokens after the prompt (dg_ar_step, one
+    token per call, kernels launched directly), timed with events; then one
+    profiled AR step, and the per-step ratios diffusion step / AR step."""
+    import torch
+    P_max = P + ((n + 2 + 31) // 32) * 32
+    kv = dm.kv_cache(1, P_max)
+    ws = dm.workspace(256, P_max)
+    dg.dg_prefill_prefix(dm.handle, prefix[:1], 1, P, P_max, kv, ws, stream=stream)
+    seeds = synth.row_seeds(seed + 100, 1)
+    tok = prefix[:1, -1].contiguous()
+    toks = torch.zeros(n + 2, dtype=torch.int32, device="cuda")
+    pos = P
+    for _ in range(2):   # warm-up
+        dg.dg_ar_step(dm.handle, kv, 1, pos, P_max, tok, 0.8, seeds, tok, ws, stream=stream)
+        pos += 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        dg.dg_ar_step(dm.handle, kv, 1, pos, P_max, tok, 0.8, seeds, toks[i:i + 1], ws, stream=stream)
+        tok = toks[i:i + 1]
+        pos += 1
+    e1.record()
+    torch.cuda.synchronize()
+    ms_tok = e0.elapsed_time(e1) / n
+    dg.dg_profile_enable(dm.handle, True)
+    dg.dg_ar_step(dm.handle, kv, 1, pos - 1, P_max, tok, 0.8, seeds, toks[n:n + 1], ws, stream=stream)
+    torch.cuda.synchronize()
+    prof = dg.dg_profile_read(dm.handle)
+    dg.dg_profile_enable(dm.handle, False)
+    ar_k = {k: round(v[0], 4) for k, v in prof.items()}
+    del kv, ws
+    out = {"tokens": n, "prompt": P, "ms_per_token": round(ms_tok, 4), "tok_s": round(1e3 / ms_tok, 2),
+           "launch": "direct (no graph)", "kernel_ms": ar_k, "kernel_sum_ms": round(sum(ar_k.values()), 4)}
+    if step_kernel_ms:
+        sk = {k: v["ms_per_step"] for k, v in step_kernel_ms.items()}
+        ratios = {"step_over_ar_wall": round(step_ms / ms_tok, 3),
+                  "step_over_ar_kernels": round(sum(sk.values()) / max(1e-9, sum(ar_k.values())), 3)}
+        for g, ks in AR_GROUPS.items():
+            a = sum(ar_k.get(k, 0.0) for k in ks)
+            d = sum(sk.get(k, 0.0) for k in ks)
+            ratios[g] = round(d / a, 3) if a > 0 else None
+        out["ratios"] = ratios
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +233,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--ar-steps", type=int, default=32,
+                    help="autoregressive tokens decoded after the prompt for the per-step comparison "
+                         "(0 skips it)")
     ap.add_argument("--blocks", type=int, default=2,
                     help="blocks generated one after another over a growing cache, each appended to it when "
                          "finished (end-to-end leg, prompt prefill included; 0 skips it)")
@@ -290,6 +345,10 @@ def main():
         block_ms = e0.elapsed_time(e1)
         steps_taken = st["steps"].cpu().numpy().tolist()
         log(f"block: steps taken {steps_taken}, {block_ms:.1f} ms")
+    ar = None
+    if args.ar_steps > 0 and Bp == B == 1:
+        ar = ar_leg(dg, synth, dm, prefix, P, args.ar_steps, args.seed, stream, kernel_ms, ms_per_step)
+        log(f"AR decode: {ar['ms_per_token']:.3f} ms/token; ratios {ar.get('ratios')}")
     multi = None
     if args.blocks > 0 and Bp == B:
         multi = multi_block(dg, synth, dm, prefix, B, T, P, args.blocks, sp, args.seed, stream)
@@ -330,7 +389,7 @@ def main():
                           "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms_per_step, 4)},
         "touched_experts_per_layer": float(np.mean(touched)),
         "kernel_ms": kernel_ms, "prefill_ms": round(prefill_ms, 2), "setup_s": round(setup_s, 1),
-        "multi_block": multi,
+        "multi_block": multi, "ar_decode": ar,
     }
     dm.close()
     if not args.no_cpu_baseline:
