@@ -223,6 +223,52 @@ def ar_leg(dg, synth, dm, prefix, P, n, seed, stream, step_kernel_ms, step_ms):
     return out
 
 
+def routing_leg(dg, synth, seed, stream):
+    """One full-width layer (2048-token prefix, 256 canvas rows) at three
+    routing spreads: iid canvas rows (every expert touched), rows sharing a
+    common direction so that about 84 distinct experts are touched (the
+    article's section 5 count), and a stronger common direction.  Reports the
+    touched experts and the grouped expert products' time and byte rate."""
+    import numpy as np
+    import torch
+    from discrete_diffusion_decoding_amd.configs import WORKLOADS
+    from discrete_diffusion_decoding_amd.device import DeviceModel
+    wl = WORKLOADS["layer_step_routed"]
+    m = wl.model
+    P, T, d = wl.prefix_len, wl.canvas_len, m.d_model
+    dm = DeviceModel(m, seed)
+    kv = dm.kv_cache(1, P)
+    ws = dm.workspace(T, P + T)
+    hp = torch.as_tensor(synth.hidden(seed, "prefix_hidden", (P, d))).cuda()
+    dg.dg_prefill_hidden(dm.handle, hp, 1, P, P, kv, ws, stream=stream)
+    out = []
+    reps = 5
+    for label, a in (("iid", 0.0), ("article_84", wl.hidden_common), ("concentrated", 2.5)):
+        hc = torch.as_tensor(synth.hidden_common(seed, "canvas_hidden", (T, d), a)).cuda()
+        h = hc.clone()
+        ed = torch.zeros(1, T, m.top_k, dtype=torch.int32, device="cuda")
+        dg.dg_forward_hidden(dm.handle, kv, 1, P, P, 1, T, h, ws, expert_dump=ed, stream=stream)
+        torch.cuda.synchronize()
+        touched = int(len(np.unique(ed.cpu().numpy())))
+        dg.dg_profile_enable(dm.handle, True)
+        for _ in range(reps):
+            h.copy_(hc)
+            dg.dg_forward_hidden(dm.handle, kv, 1, P, P, 1, T, h, ws, stream=stream)
+        torch.cuda.synchronize()
+        prof = dg.dg_profile_read(dm.handle)
+        dg.dg_profile_enable(dm.handle, False)
+        gu, dn = prof["expert_gateup"][0] / reps, prof["expert_down"][0] / reps
+        w_bytes = touched * 3 * m.d_expert * d * 2
+        out.append({"rows": label, "common": a, "touched_experts": touched,
+                    "expert_gateup_ms": round(gu, 4), "expert_down_ms": round(dn, 4),
+                    "expert_weight_bytes": int(w_bytes),
+                    "expert_GB_s": round(w_bytes / ((gu + dn) * 1e-3) / 1e9, 1),
+                    "layer_ms": round(sum(v[0] for v in prof.values()) / reps, 4)})
+    del kv, ws
+    dm.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +282,8 @@ def main():
     ap.add_argument("--ar-steps", type=int, default=32,
                     help="autoregressive tokens decoded after the prompt for the per-step comparison "
                          "(0 skips it)")
+    ap.add_argument("--no-routing", action="store_true",
+                    help="skip the one-layer leg at three routing spreads (iid / ~84 / fewer experts)")
     ap.add_argument("--blocks", type=int, default=2,
                     help="blocks generated one after another over a growing cache, each appended to it when "
                          "finished (end-to-end leg, prompt prefill included; 0 skips it)")
@@ -392,6 +440,10 @@ def main():
         "multi_block": multi, "ar_decode": ar,
     }
     dm.close()
+    if not args.no_routing and m.n_experts == 128:
+        out["routing"] = routing_leg(dg, synth, args.seed, stream)
+        log("routing: " + ", ".join(f"{r['rows']} {r['touched_experts']} experts "
+                                    f"{r['expert_gateup_ms'] + r['expert_down_ms']:.3f} ms" for r in out["routing"]))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(m, args.seed)

@@ -75,6 +75,7 @@ class Workload:
     steps: int          # denoising steps run by the workload (1 = single step)
     hidden_input: bool  # True: canvas/prefix given as hidden states (no embedding, no head)
     sampler: SamplerParams = SamplerParams()
+    hidden_common: float = 0.0  # hidden-state inputs: weight of a direction shared by every canvas row
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -98,6 +99,14 @@ WORKLOADS = {
     # one full-width layer over a 2048-token prefix; canvas hidden states in, out.
     "layer_step": Workload("layer_step", FULL_LAYER, batch=1, prefix_batch=1,
                            prefix_len=2048, canvas_len=256, steps=1, hidden_input=True),
+    # layer_step with canvas rows that share a common direction (weight 0.95):
+    # the router then picks about 84 distinct experts over the 256 rows (84 at
+    # seed 2024, 93 at seed 1234: the count depends on the draw), the count the
+    # article's section 5 gives for the trained model; iid rows pick all 128,
+    # and the 30-layer random model averages 57.
+    "layer_step_routed": Workload("layer_step_routed", FULL_LAYER, batch=1, prefix_batch=1,
+                                  prefix_len=2048, canvas_len=256, steps=1, hidden_input=True,
+                                  hidden_common=0.95),
     # full 30-layer model, one steady-state denoising step.
     "full_step": Workload("full_step", FULL, batch=1, prefix_batch=1, prefix_len=2048,
                           canvas_len=256, steps=1, hidden_input=False),

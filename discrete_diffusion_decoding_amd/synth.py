@@ -181,6 +181,15 @@ def hidden(seed: int, name: str, shape, std: float = 1.0) -> np.ndarray:
     return (std * g.standard_normal(size=shape)).astype(np.float32)
 
 
+def hidden_common(seed: int, name: str, shape, common: float) -> np.ndarray:
+    """Rows of N(0, 1) noise plus `common` times one fixed N(0, 1) direction
+    shared by every row: the larger `common`, the more alike the rows look to
+    a router, and the fewer distinct experts they pick."""
+    z = hidden(seed, name, shape).astype(np.float64)
+    c = hidden(seed, name + "/common", (shape[-1],)).astype(np.float64)
+    return (z + common * c).astype(np.float32)
+
+
 def row_seeds(seed: int, n: int) -> np.ndarray:
     g = np.random.Generator(np.random.Philox(key=[tensor_seed(seed, "row_seeds"), 3]))
     return g.integers(0, 2**63 - 1, size=n, dtype=np.int64).astype(np.uint64)

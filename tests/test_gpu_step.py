@@ -119,28 +119,33 @@ def test_tiny_step_matches_oracle(step):
         assert np.array_equal(got["tokens"][0][~lock_o & far], noise[~lock_o & far])
 
 
-def test_layer_step_matches_oracle():
-    wl = WORKLOADS["layer_step"]
+@pytest.mark.parametrize("name", ["layer_step", "layer_step_routed"])
+def test_layer_step_matches_oracle(name):
+    """One full-width layer over a 2048-token prefix.  layer_step_routed feeds
+    canvas rows sharing a common direction, so the router touches about 84
+    distinct experts (the article's count) instead of all 128: the grouped
+    expert products then skip the untouched experts."""
+    wl = WORKLOADS[name]
     m = wl.model
     T, P = wl.canvas_len, wl.prefix_len
     hp = synth.hidden(SEED, "prefix_hidden", (P, m.d_model))
-    hc = synth.hidden(SEED, "canvas_hidden", (T, m.d_model))
-    announce("layer_step: upload")
+    hc = synth.hidden_common(SEED, "canvas_hidden", (T, m.d_model), wl.hidden_common)
+    announce(f"{name}: upload")
     dm = DeviceModel(m, SEED)
     kv = dm.kv_cache(1, P)
     ws = dm.workspace(T, P + T)
-    announce("layer_step: prefill (hidden)")
+    announce(f"{name}: prefill (hidden)")
     dg.dg_prefill_hidden(dm.handle, dev(hp), 1, P, P, kv, ws)
     hidden = dev(hc)
     hd_ = torch.zeros(m.n_layers + 1, T, m.d_model, device="cuda")
     ed = torch.zeros(m.n_layers, T, m.top_k, dtype=torch.int32, device="cuda")
     gd = torch.zeros(m.n_layers, T, m.top_k, device="cuda")
-    announce("layer_step: forward")
+    announce(f"{name}: forward")
     dg.dg_forward_hidden(dm.handle, kv, 1, P, P, 1, T, hidden, ws, hd_, ed, gd)
     out, hdump, edump, gdump = host(hidden), host(hd_), host(ed), host(gd)
     kvh = host(kv)
     dm.close()
-    announce("layer_step: oracle")
+    announce(f"{name}: oracle")
     M = om.Model(m, synth.SynthWeights(m, SEED, cache_layers=True))
     kv_o, _ = M.prefill_hidden(hp)
     h_o, recs = M.canvas_hidden(hc, kv_o, P)
@@ -155,6 +160,12 @@ def test_layer_step_matches_oracle():
     excused = check_experts(edump[0], gdump[0], recs[0]["experts"], recs[0]["gates"], recs[0]["router_logits"],
                             m.top_k)
     assert excused <= 8
+    touched = len(np.unique(edump[0]))
+    assert touched == len(np.unique(recs[0]["experts"])) or excused > 0
+    if wl.hidden_common:
+        assert 70 <= touched <= 100, touched
+    else:
+        assert touched >= 120, touched
     assert rel_l2(out, h_o) <= 1e-2
     assert rel_l2(hdump[1], h_o) <= 1e-2
     # the layer's own contribution (h_out - h_in) is also matched
