@@ -531,17 +531,21 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
                          st));
     }
     // shared FFN: independent of the routed path, so (outside profiling) it runs
-    // on the side stream, forked here and joined before the combine
+    // on the side stream, forked here and joined before the combine.  Its
+    // kernels are enqueued after the router's: a captured graph then keeps the
+    // routed path (the critical one) on the main queue, and only the shared
+    // FFN pays the cross-queue latency of the fork; at the join its result is
+    // long done.
     Partials ysp{ys, 0, (long)R * D};
     bool forked = false;
-    if (fs) {
-      hipStream_t ss = st;
-      if (!m->prof.on && side_stream(m)) {
-        DG_CK(hipEventRecord(m->ev_fork, st));
-        DG_CK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
-        ss = m->side;
-        forked = true;
-      }
+    hipStream_t ss = st;
+    if (fs && !m->prof.on && side_stream(m)) {
+      DG_CK(hipEventRecord(m->ev_fork, st));
+      ss = m->side;
+      forked = true;
+    }
+    auto shared_ffn = [&]() -> dg_status {
+      if (forked) DG_CK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
       ProfScope ps_(m, DG_PROF_SHARED, ss);
       GemmArgs g = gargs();
       g.ring = m->d_ring;
@@ -557,7 +561,8 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
       DG_CK(gemm(EPI_STORE_F32, g2, ss));
       if (forked) DG_CK(hipEventRecord(m->ev_join, ss));
-    }
+      return DG_OK;
+    };
     // router logits (hi and lo rows, split-K partials) and top-k
     Partials rlp{rlog, 1, (long)2 * R * E};
     {
@@ -576,6 +581,10 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       DG_CK(router_topk(rlp, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
                         ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
       DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
+    }
+    if (fs) {
+      dg_status sr = shared_ffn();
+      if (sr != DG_OK) return sr;
     }
     // experts: gate/up (GEGLU) then down, grouped by expert over the permuted slots
     {
