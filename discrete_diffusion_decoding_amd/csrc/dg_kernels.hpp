@@ -32,7 +32,7 @@ struct GemmArgs {
   int items_max;
   int M;
   int k_split;
-  int tile_rows;   // 64-row kernel: activation rows per tile (64; also the work-list chunk size),
+  int tile_rows;   // 64-row kernel: activation rows per tile (64, the work-list chunk size; dense rows also 128),
   int tile_cols;   // weight rows per tile (64 | 128)
   int ring;        // and its LDS ring depth (64 wide: 4 | 5; 128 wide: 2 | 3)
   void* C;

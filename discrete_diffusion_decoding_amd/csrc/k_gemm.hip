@@ -4,8 +4,9 @@
 // tokens; ~16-100 per expert) with a large weight matrix, so the kernel is built
 // to keep many weight bytes in flight and to read each byte once:
 //   * a workgroup (4 waves) owns one output tile: <= 64 activation rows (one
-//     "item": a chunk of one expert's rows, or of the dense rows) x 64 weight rows
-//     (GEGLU: 32 gate rows and the 32 matching up rows);
+//     "item": a chunk of one expert's rows, or of the dense rows; dense products
+//     may take 128) x 64 or 128 weight rows (GEGLU: half gate rows, half the
+//     matching up rows);
 //   * the tiles are streamed through a 4-stage ring of LDS buffers, 64 columns
 //     per stage, with direct global->LDS loads (global_load_lds_dwordx4): every
 //     load instruction moves 8 whole 128-byte rows, three stages (48 KB) are in
@@ -38,9 +39,16 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >
 // stages in flight).  The weight stream is what the product is bound by; the
 // activation tile is re-read from L2 for every weight tile, so a wider BW
 // spends fewer DMA and LDS cycles per weight byte.
+// workgroups per CU a variant is built for: as many as its ring fits in the
+// 160 KB of LDS, at most two (three for double-buffered rings)
+template <int AR, int BW, int NS>
+constexpr int gemm_wg_per_cu() {
+  return NS * (AR + BW) * 128 > 80 * 1024 ? 1 : (NS == 2 && (AR + BW) * 128 * NS <= 53 * 1024 ? 3 : 2);
+}
+
 template <int EPI, bool ITEMS, int AR, int BW, int NS>
-__global__ __launch_bounds__(256, NS == 2 ? 3 : 2) void gemm_kernel(GemmArgs g) {
-  static_assert(AR == 32 || AR == 64, "activation tile of 32 or 64 rows");
+__global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kernel(GemmArgs g) {
+  static_assert(AR == 32 || AR == 64 || (AR == 128 && !ITEMS), "activation tile of 32, 64 (or dense 128) rows");
   static_assert(BW == 64 || BW == 128, "weight tile of 64 or 128 rows");
   static_assert(NS >= 2 && NS <= 6, "ring of 2..6 stages");
   constexpr int SE = (AR + BW) * 64;         // stage: AR activation rows then BW weight rows, 64 bf16 each
@@ -50,7 +58,7 @@ __global__ __launch_bounds__(256, NS == 2 ? 3 : 2) void gemm_kernel(GemmArgs g) 
   constexpr int WPW = BW / 4;                // weight rows per wave
   constexpr int NBF = WPW / 16;              // weight fragments per wave
   static_assert(NG % 4 == 0, "groups split evenly over 4 waves");
-  static_assert(NS * SE * 2 <= (NS == 2 ? 53 : 80) * 1024, "two (double-buffered: three) workgroups per CU");
+  static_assert(NS * SE * 2 * gemm_wg_per_cu<AR, BW, NS>() <= 160 * 1024, "the ring fits the LDS of a CU");
   __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
   __shared__ __attribute__((aligned(1024))) bf16_t S1[SE];
   __shared__ __attribute__((aligned(1024))) bf16_t S2[SE];
@@ -324,6 +332,14 @@ static hipError_t launch_v(GemmArgs a, hipStream_t s) {
 // (weight rows), a.ring (LDS ring depth)
 template <int EPI, bool ITEMS>
 static hipError_t launch(const GemmArgs& a, hipStream_t s) {
+  if (a.tile_rows == 128) {
+    if (ITEMS) return hipErrorInvalidValue;
+    switch (a.tile_cols * 10 + a.ring) {
+      case 643: return launch_v<EPI, false, 128, 64, 3>(a, s);
+      case 1282: return launch_v<EPI, false, 128, 128, 2>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (a.tile_rows != 64) return hipErrorInvalidValue;
   const int v = a.tile_cols * 10 + a.ring;
   switch (v) {
