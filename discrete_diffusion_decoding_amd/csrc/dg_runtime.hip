@@ -559,6 +559,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g2.ring = m->d_ring;
       g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
       dense_rows(g2, R);
+      g2.tile_rows = 128; g2.ring = 3; g2.items_max = cdiv(R, 128);   // as the O projection
       g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, g2.tile_cols), fs, kMaxDenseSplit, &g2.k_chunk);
       ysp.n = g2.k_split;
       g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
