@@ -69,9 +69,9 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kh):
+def traffic_from_profile(kh, workload):
     """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source."""
+    they were taken on the current kernel source and on this workload."""
     p = os.path.join(ROOT, "profiles", "expert_gateup_full_step_counters.json")
     if not os.path.exists(p):
         return None
@@ -79,7 +79,7 @@ def traffic_from_profile(kh):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("kernel_source_sha256_16") != kh:
+    if d.get("kernel_source_sha256_16") != kh or d.get("workload") != workload:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -415,7 +415,7 @@ def main():
         ach = bytes_l / (per_launch_ms * 1e-3) / 1e9
         kh = kernel_hash()
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(kh),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(kh, wl.name),
                 "kernel": "grouped expert gate/up GEMM (dg::gemm_kernel<4, true>)",
                 "bytes_per_launch": int(bytes_l), "avg_launch_ms": round(per_launch_ms, 4),
                 "kernel_source_sha256_16": kh}
