@@ -452,9 +452,10 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.ring = m->d_ring;
       g.A = xn; g.lda = D; g.W = lw(m, l, m->lay.w_qkv); g.ldw = D; g.K = D; g.N = qkvd; g.k_chunk = D;
       dense_rows(g, R); g.C = qkv; g.ldc = qkvd; g.flag = ps.flag;
-      // 128-wide weight tiles: without a k split there are enough of them, and
-      // each activation byte fetched then feeds twice the weight rows
-      g.tile_cols = 128; g.ring = 3;
+      // 128-wide weight tiles: without a k split there are enough of them at
+      // 128+ rows, and each activation byte fetched then feeds twice the weight
+      // rows; fewer rows (decoding) keep 64-wide tiles, twice as many workgroups
+      if (R >= 128) { g.tile_cols = 128; g.ring = 3; }
       ProfScope ps_(m, DG_PROF_DENSE, st);
       DG_CK(gemm(EPI_STORE_BF16, g, st));
     }
