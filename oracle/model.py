@@ -153,9 +153,10 @@ class Model:
         return h + y, info
 
     # -- prefix (causal) ------------------------------------------------------
-    def prefill_hidden(self, h):
+    def prefill_hidden(self, h, records=None):
         """Causal forward of one prefix given its input hidden states [P, d].
-        Returns per-layer (K, V) after QK-norm and RoPE, and the final hidden."""
+        Returns per-layer (K, V) after QK-norm and RoPE, and the final hidden;
+        if `records` is a list, each layer's routing record is appended to it."""
         h = np.asarray(h, dtype=F)
         P = h.shape[0]
         pos = np.arange(P)
@@ -165,15 +166,17 @@ class Model:
             lw = self.layer_dense(l)
             q, k, v = self.qkv(h, lw, pos)
             o = attention(q, k, v, causal)
-            h, _ = self.post_attention(h, o, lw)
+            h, info = self.post_attention(h, o, lw)
+            if records is not None:
+                records.append(info)
             kv.append((k, v))
         return kv, h
 
     def embed(self, tokens):
         return self.glob()["embed"][np.asarray(tokens)]
 
-    def prefill_tokens(self, tokens):
-        return self.prefill_hidden(self.embed(tokens))
+    def prefill_tokens(self, tokens, records=None):
+        return self.prefill_hidden(self.embed(tokens), records)
 
     # -- canvas (bidirectional over prefix + canvas) ---------------------------
     def canvas_hidden(self, h, kv, P):

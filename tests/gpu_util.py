@@ -35,6 +35,14 @@ def kv_layer(kv, m, Bp, P_max, l, bp, P):
     return K.astype(np.float64), V.astype(np.float64)
 
 
+def near_tie_rows(router_logits, k, margin):
+    """Rows whose k-th and (k+1)-th largest router logits lie within `margin`:
+    there a rounding-level difference may swap an expert (ties aside, the
+    choice is otherwise fixed)."""
+    s = -np.sort(-np.asarray(router_logits, dtype=np.float64), axis=-1)
+    return np.nonzero(s[:, k - 1] - s[:, k] < margin)[0]
+
+
 def rel_l2(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
