@@ -102,6 +102,12 @@ def test_sampler_pages_variant_rules_bit_exact():
     _run_sampler_case(1, 64, 2048, 6.0, 60.0, [0, 1, 2], sp, seed=9)
 
 
+def test_sampler_maximum_batch_and_canvas_bit_exact():
+    """The largest shapes the library accepts: 16 canvases of 1024 positions
+    (the finishing kernel then runs 1024 threads per row)."""
+    _run_sampler_case(16, 1024, 2048, 2.0, 20.0, [0, 5], SamplerParams(), seed=13)
+
+
 def test_sampler_full_vocab_one_canvas_bit_exact():
     _run_sampler_case(1, 256, 262144, 1.06, 0.0, [1], SamplerParams())
 

@@ -310,6 +310,41 @@ def test_ar_decode_matches_oracle():
             assert nx[i] == t_o, i
 
 
+def test_ar_decode_two_sequences():
+    """dg_ar_step over two sequences with their own caches and seeds: each
+    sequence's logits match the oracle's decode of its own prompt, and its
+    token is the oracle sampler's on the GPU's logits (bit-exact)."""
+    wl = WORKLOADS["tiny_step"]
+    m = wl.model
+    B, P, P_max, tau, n = 2, 32, 64, 0.7, 3
+    dm = DeviceModel(m, SEED)
+    prompts = synth.tokens(SEED, "ar2", (B, P + 1), m.vocab)
+    seeds = synth.row_seeds(SEED + 3, B)
+    kv = dm.kv_cache(B, P_max)
+    ws = dm.workspace(P, P_max)
+    announce("ar two sequences: prefill 2 x 32")
+    dg.dg_prefill_prefix(dm.handle, dev(np.ascontiguousarray(prompts[:, :P])), B, P, P_max, kv, ws)
+    tok = dev(np.ascontiguousarray(prompts[:, P]).astype(np.int32))
+    logits = torch.zeros(n, B, m.vocab, device="cuda")
+    nxt = torch.zeros(n, B, dtype=torch.int32, device="cuda")
+    for i in range(n):
+        announce(f"ar two sequences: step at P={P + i}")
+        dg.dg_ar_step(dm.handle, kv, B, P + i, P_max, tok, tau, seeds, nxt[i], ws, logits_dump=logits[i])
+        tok = nxt[i]
+    lg, nx = host(logits), host(nxt)
+    dm.close()
+    announce("ar two sequences: oracle")
+    M = om.Model(m, synth.SynthWeights(m, SEED, cache_layers=True))
+    for b in range(B):
+        kv_o, _ = M.prefill_tokens(prompts[b, :P])
+        for i in range(n):
+            t_in = int(prompts[b, P]) if i == 0 else int(nx[i - 1, b])
+            h, new = M.decode_token(t_in, kv_o, P + i)
+            assert rel_l2(lg[i, b], M.head(h)[0]) <= 1e-2, (b, i)
+            kv_o = [(np.concatenate([k, nk]), np.concatenate([v, nv])) for (k, v), (nk, nv) in zip(kv_o, new)]
+            assert nx[i, b] == osmp.ar_sample(lg[i, b], tau, seeds[b], P + i)[0], (b, i)
+
+
 def test_tiny_block_equals_repeated_steps():
     """dg_generate_block (device-driven step index, stop flag) equals the same
     number of host-driven dg_denoise_step calls, bit for bit."""
