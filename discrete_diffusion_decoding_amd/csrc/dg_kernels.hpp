@@ -81,10 +81,13 @@ struct QkRopeArgs {
   bf16_t* kdst; long k_bstride, k_hstride;            // K rows [.][Hkv][pitch][hd]
   bf16_t* vtdst; long v_bstride, v_hstride, v_pitch;  // V^T [.][Hkv][hd][pitch]
   int t_offset;                     // index of row 0 within the destination sequence
+  const int32_t* pos_dev;           // if set: t_offset read from the device
   const int32_t* flag;
 };
 hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s);
-hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta, hipStream_t s);
+// pos_dev (may be null): pos0 read from the device instead
+hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta, const int32_t* pos_dev,
+                      hipStream_t s);
 
 struct AttnArgs {
   const bf16_t* q; int H, Hkv, hd; float scale;
@@ -94,6 +97,8 @@ struct AttnArgs {
   const bf16_t* k2; const bf16_t* vt2; long k2_bstride, k2_hstride, v2_bstride, v2_hstride, v2_pitch; int n2;
   int causal; int qpos0;            // causal: query row r (within batch) sits at qpos0 + r
   int splits; int split_len;        // key splits (split_len multiple of 32)
+  const int32_t* pos_dev;           // causal pass (n2 = 0) whose first query position is read from the
+                                    // device: qpos0 = *pos_dev, n1 = that + rows rounded up to 32 keys
   bf16_t* out;                      // one split: O [B*rows][H][hd] (bf16, normalised)
   bf16_t* opart; float* mlpart;     // more: per split normalised O [splits][B*rows][H][hd] (bf16)
                                     // and (running max in log2 units, sum) [splits][B*rows][H][2]
@@ -141,6 +146,7 @@ struct SampleArgs {
 struct ArSampleArgs {
   const float* logits; int B, V; long ldl;
   float inv_tau; int pos;
+  const int32_t* pos_dev;           // if set: pos read from the device
   uint64_t seeds[16];
   int vsplit;                       // vocab slices per row
   float* part;                      // [B][vsplit][8]

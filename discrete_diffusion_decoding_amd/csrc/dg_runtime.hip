@@ -35,7 +35,7 @@ struct Prof {
 
 // A captured step (one hipGraph per distinct set of step arguments).
 struct GraphKey {
-  int kind;  // 0: dg_denoise_step, 1: a step of dg_generate_block (stop-flag early exits)
+  int kind;  // 0: dg_denoise_step, 1: a step of dg_generate_block (stop-flag early exits), 2: dg_ar_step
   const void* kv;
   int Bp, P, P_max, B, T;
   dg_canvas c;
@@ -211,7 +211,7 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // workspace plan
 struct Plan {
   size_t h, xn, qkv, q, kc, vc, rope, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
-      nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, P, separt, flag, total;
+      nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, P, separt, flag, pos, total;
   int splits_max, vsplit, ksplit, kchunk;
 };
 
@@ -333,6 +333,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
     }
   }
   p.flag = take(64);
+  p.pos = take(64);
   p.total = o;
   return p;
 }
@@ -360,6 +361,7 @@ struct Pass {
   float* gate_dump;
   bool final_norm;            // last combine writes the final-normed hidden into xn
   const int32_t* flag;
+  const int32_t* pos_dev;     // prefill of one position read from the device (q0, pos0 unused)
 };
 
 static const bf16_t* lw(const dg_model* m, int l, size_t off) { return m->layers[l] + off; }
@@ -431,7 +433,9 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
 
   // attention split choice: about one workgroup per CU
   const int GQ = H / Hkv;
-  const int nkeys = ps.prefill ? ps.q0 + R : ps.P + ps.per_batch;
+  // (a position read on the device: the split plan covers the whole capacity,
+  // and splits past the last key exit at once)
+  const int nkeys = ps.prefill ? (ps.pos_dev ? ps.P_max : ps.q0 + R) : ps.P + ps.per_batch;
   const int base_wg = cdiv(ps.per_batch, attn_rows_per_wg(hd) / GQ) * Hkv * ps.B;   // per key split
   int splits = std::max(1, std::min(p.splits_max, cdiv(256, base_wg)));
   const int split_len = cdiv(cdiv(nkeys, splits), 32) * 32;
@@ -439,7 +443,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
 
   {
     ProfScope ps_(m, DG_PROF_OTHER, st);
-    DG_CK(rope_table(at<float2>(ws, p.rope), ps.per_batch, ps.pos0, hd, d.rope_theta, st));
+    DG_CK(rope_table(at<float2>(ws, p.rope), ps.per_batch, ps.pos0, hd, d.rope_theta, ps.pos_dev, st));
   }
   for (int l = 0; l < d.n_layers; ++l) {
     const bf16_t* kvl = ps.kv ? ps.kv + (size_t)l * layer_kv : nullptr;
@@ -469,7 +473,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       if (ps.prefill) {
         a.kdst = const_cast<bf16_t*>(Kc); a.k_bstride = 0; a.k_hstride = (long)ps.P_max * hd;
         a.vtdst = const_cast<bf16_t*>(Vc); a.v_bstride = 0; a.v_hstride = (long)hd * ps.P_max; a.v_pitch = ps.P_max;
-        a.t_offset = ps.q0;
+        a.t_offset = ps.q0; a.pos_dev = ps.pos_dev;
       } else {
         const int T = ps.per_batch;
         a.kdst = at<bf16_t>(ws, p.kc); a.k_bstride = (long)Hkv * T * hd; a.k_hstride = (long)T * hd;
@@ -493,7 +497,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
         // mask hides the tail, so a pass may start and end anywhere
         a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max;
         a.n1 = cdiv(ps.q0 + R, 32) * 32; a.nb1 = 1;
-        a.n2 = 0; a.causal = 1; a.qpos0 = ps.q0;
+        a.n2 = 0; a.causal = 1; a.qpos0 = ps.q0; a.pos_dev = ps.pos_dev;
       } else {
         const int T = ps.per_batch;
         if (ps.P > 0) {
@@ -717,24 +721,57 @@ extern "C" dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, 
   return prefill_impl(m, nullptr, prefix_hidden, Bp, 0, P, P_max, kv, ws, ws_bytes, (hipStream_t)stream);
 }
 
+// Replay the graph cached under `key`, or capture `enqueue` on `st` into one,
+// cache it (up to 8, least recently used evicted) and launch it.
+template <class F>
+static dg_status graph_run(dg_model* m, const GraphKey& key, F&& enqueue, hipStream_t st) {
+  for (GraphEntry& g : m->graphs) {
+    if (memcmp(&g.key, &key, sizeof(key)) == 0) {
+      g.last_use = ++m->use_clock;
+      DG_CK(hipGraphLaunch(g.exec, st));
+      return DG_OK;
+    }
+  }
+  DG_CK(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
+  dg_status r = enqueue();
+  hipGraph_t graph = nullptr;
+  const hipError_t ec = hipStreamEndCapture(st, &graph);
+  if (r != DG_OK || ec != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    if (r != DG_OK) return r;
+    fprintf(stderr, "libdg: stream capture failed: %s\n", hipGetErrorString(ec));
+    return DG_ERR_HIP;
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(graph);
+  if (ei != hipSuccess) {
+    fprintf(stderr, "libdg: graph instantiation failed: %s\n", hipGetErrorString(ei));
+    return DG_ERR_HIP;
+  }
+  if (m->graphs.size() >= 8) {
+    size_t oldest = 0;
+    for (size_t i = 1; i < m->graphs.size(); ++i)
+      if (m->graphs[i].last_use < m->graphs[oldest].last_use) oldest = i;
+    (void)hipGraphExecDestroy(m->graphs[oldest].exec);
+    m->graphs.erase(m->graphs.begin() + oldest);
+  }
+  m->graphs.push_back(GraphEntry{key, exec, ++m->use_clock});
+  DG_CK(hipGraphLaunch(exec, st));
+  return DG_OK;
+}
+
 // One autoregressive step per sequence: the token at position P is encoded
 // against the cached positions 0..P-1 (its K/V written at P), then the final
 // norm, the LM head and the next-token sample.  Sequences run one after
-// another, each a one-row pass over the layers.
-extern "C" dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int32_t P_max, const int32_t* token,
-                                float tau, const uint64_t* row_seeds, int32_t* next, int32_t* argmax,
-                                float* entropy, float* logits_dump, void* ws, size_t ws_bytes,
-                                dg_stream_t stream) {
-  if (!m || !kv || !token || !next || !row_seeds || !ws) return DG_ERR_ARG;
-  if (m->d.vocab == 0) return DG_ERR_UNSUPPORTED;
-  if (B < 1 || B > 16 || P < 0 || P_max < P + 1 || !(tau > 0.f) || !std::isfinite(tau)) return DG_ERR_ARG;
-  if (P_max % 32 || m->d.vocab % 4) return DG_ERR_SHAPE;
-  const Plan p = make_plan(m->d, 1, P + 1);
-  if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
+// another, each a one-row pass over the layers.  pos_dev: the position is read
+// on the device (the P-dependent kernel arguments are then unused), so that
+// one captured graph serves every position.
+static dg_status ar_impl(dg_model* m, void* kv, int B, int P, int P_max, const int32_t* token, float inv_tau,
+                         const uint64_t* row_seeds, int32_t* next, int32_t* argmax, float* entropy,
+                         float* logits_dump, void* ws, const Plan& p, const int32_t* pos_dev, hipStream_t st) {
   const dg_model_desc& d = m->d;
   const int V = d.vocab, D = d.d_model;
-  hipStream_t st = (hipStream_t)stream;
-  const float inv_tau = (float)(1.0 / (double)tau);
   float* h = at<float>(ws, p.h);
   bf16_t* xn = at<bf16_t>(ws, p.xn);
   for (int b = 0; b < B; ++b) {
@@ -744,7 +781,7 @@ extern "C" dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int
     Pass ps{};
     ps.rows = 1; ps.B = 1; ps.per_batch = 1; ps.pos0 = P; ps.prefill = true; ps.bp = b; ps.q0 = P;
     ps.kv = (const bf16_t*)kv; ps.kv_Bp = B; ps.Bp = 1; ps.P = 0; ps.P_max = P_max;
-    ps.final_norm = true; ps.flag = nullptr;
+    ps.final_norm = true; ps.flag = nullptr; ps.pos_dev = pos_dev;
     dg_status s = run_layers(m, p, ws, ps, st);
     if (s != DG_OK) return s;
     float* logits = logits_dump ? logits_dump + (size_t)b * V : at<float>(ws, p.logits);
@@ -757,13 +794,47 @@ extern "C" dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int
     }
     ArSampleArgs sa;
     memset(&sa, 0, sizeof(sa));
-    sa.logits = logits; sa.B = 1; sa.V = V; sa.ldl = V; sa.inv_tau = inv_tau; sa.pos = P;
+    sa.logits = logits; sa.B = 1; sa.V = V; sa.ldl = V; sa.inv_tau = inv_tau; sa.pos = P; sa.pos_dev = pos_dev;
     sa.seeds[0] = row_seeds[b]; sa.vsplit = p.vsplit; sa.part = at<float>(ws, p.spart);
     sa.next = next + b; sa.argmax = argmax ? argmax + b : nullptr; sa.entropy = entropy ? entropy + b : nullptr;
     ProfScope ps_(m, DG_PROF_SAMPLER, st);
     DG_CK(ar_sample(sa, st));
   }
   return DG_OK;
+}
+
+extern "C" dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int32_t P_max, const int32_t* token,
+                                float tau, const uint64_t* row_seeds, int32_t* next, int32_t* argmax,
+                                float* entropy, float* logits_dump, void* ws, size_t ws_bytes,
+                                dg_stream_t stream) {
+  if (!m || !kv || !token || !next || !row_seeds || !ws) return DG_ERR_ARG;
+  if (m->d.vocab == 0) return DG_ERR_UNSUPPORTED;
+  if (B < 1 || B > 16 || P < 0 || P_max < P + 1 || !(tau > 0.f) || !std::isfinite(tau)) return DG_ERR_ARG;
+  if (P_max % 32 || m->d.vocab % 4) return DG_ERR_SHAPE;
+  const Plan p = make_plan(m->d, 1, P + 1);
+  if (ws_bytes < p.total) return DG_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const float inv_tau = (float)(1.0 / (double)tau);
+  if (!m->use_graphs || m->prof.on || st == nullptr)
+    return ar_impl(m, kv, B, P, P_max, token, inv_tau, row_seeds, next, argmax, entropy, logits_dump, ws, p,
+                   nullptr, st);
+  // graph replay: the position goes to the device first; every other argument
+  // is part of the graph's key
+  int32_t* pos_dev = at<int32_t>(ws, p.pos);
+  DG_CK(fill_i32(pos_dev, P, 1, st));
+  GraphKey key;
+  memset(&key, 0, sizeof(key));
+  key.kind = 2;
+  key.kv = kv; key.Bp = B; key.P_max = P_max; key.B = B; key.T = 1;
+  key.c.tokens = const_cast<int32_t*>(token); key.c.xhat = next; key.c.argmax = argmax; key.c.entropy = entropy;
+  key.c.logits_dump = logits_dump;
+  key.tau_start = inv_tau;
+  for (int b = 0; b < B; ++b) key.seeds[b] = row_seeds[b];
+  key.ws = ws; key.ws_bytes = ws_bytes;
+  return graph_run(m, key, [&]() -> dg_status {
+    return ar_impl(m, kv, B, P, P_max, token, inv_tau, row_seeds, next, argmax, entropy, logits_dump, ws, p,
+                   pos_dev, st);
+  }, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -897,40 +968,7 @@ static dg_status step_device_indexed(dg_model* m, const void* kv, int Bp, int P,
   key.stop_rule = sp->stop_rule;
   for (int b = 0; b < B && b < 16; ++b) key.seeds[b] = sp->row_seeds[b];
   key.ws = ws; key.ws_bytes = ws_bytes;
-  for (GraphEntry& g : m->graphs) {
-    if (memcmp(&g.key, &key, sizeof(key)) == 0) {
-      g.last_use = ++m->use_clock;
-      DG_CK(hipGraphLaunch(g.exec, st));
-      return DG_OK;
-    }
-  }
-  DG_CK(hipStreamBeginCapture(st, hipStreamCaptureModeThreadLocal));
-  dg_status r = enqueue();
-  hipGraph_t graph = nullptr;
-  const hipError_t ec = hipStreamEndCapture(st, &graph);
-  if (r != DG_OK || ec != hipSuccess) {
-    if (graph) (void)hipGraphDestroy(graph);
-    if (r != DG_OK) return r;
-    fprintf(stderr, "libdg: stream capture failed: %s\n", hipGetErrorString(ec));
-    return DG_ERR_HIP;
-  }
-  hipGraphExec_t exec = nullptr;
-  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  (void)hipGraphDestroy(graph);
-  if (ei != hipSuccess) {
-    fprintf(stderr, "libdg: graph instantiation failed: %s\n", hipGetErrorString(ei));
-    return DG_ERR_HIP;
-  }
-  if (m->graphs.size() >= 8) {
-    size_t oldest = 0;
-    for (size_t i = 1; i < m->graphs.size(); ++i)
-      if (m->graphs[i].last_use < m->graphs[oldest].last_use) oldest = i;
-    (void)hipGraphExecDestroy(m->graphs[oldest].exec);
-    m->graphs.erase(m->graphs.begin() + oldest);
-  }
-  m->graphs.push_back(GraphEntry{key, exec, ++m->use_clock});
-  DG_CK(hipGraphLaunch(exec, st));
-  return DG_OK;
+  return graph_run(m, key, enqueue, st);
 }
 
 extern "C" dg_status dg_denoise_step(dg_model* m, const void* kv, int32_t Bp, int32_t P, int32_t P_max, int32_t B,

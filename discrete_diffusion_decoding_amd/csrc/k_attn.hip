@@ -89,10 +89,12 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
   const int q0wg = qb * QPW;
   const int lr = lane & 15, lg = lane >> 4;
 
-  const int nk = a.n1 + a.n2;
+  const int qpos0 = a.pos_dev ? *a.pos_dev : a.qpos0;
+  const int n1 = a.pos_dev ? (qpos0 + R + 31) & ~31 : a.n1;
+  const int nk = n1 + a.n2;
   const int kbeg = split * a.split_len;
   int kend = min(nk, kbeg + a.split_len);
-  if (a.causal) kend = min(kend, a.qpos0 + min(q0wg + QPW, R));
+  if (a.causal) kend = min(kend, qpos0 + min(q0wg + QPW, R));
   const int ntile = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
 
   const int b1 = (a.nb1 == 1) ? 0 : b;
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     live[j] = qr0 < R;
     qrow[j] = qr0;
     const int myq = min(qr0 + lr, R - 1);
-    qpos[j] = a.qpos0 + myq;
+    qpos[j] = qpos0 + myq;
     qptr[j] = a.q + ((long)(b * R + myq) * a.H + h) * HD + lg * 8;
   }
 
@@ -141,9 +143,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
 #define DG_AISSUE(S, KT)                                                                           \
   do {                                                                                             \
     const int kt_ = (KT);                                                                          \
-    const bool one_ = kt_ < a.n1;                                                                  \
-    const bf16_t* kb_ = one_ ? K1 + (long)kt_ * HD : K2 + (long)(kt_ - a.n1) * HD;                 \
-    const bf16_t* vb_ = one_ ? V1 + kt_ : V2 + (kt_ - a.n1);                                       \
+    const bool one_ = kt_ < n1;                                                                    \
+    const bf16_t* kb_ = one_ ? K1 + (long)kt_ * HD : K2 + (long)(kt_ - n1) * HD;                   \
+    const bf16_t* vb_ = one_ ? V1 + kt_ : V2 + (kt_ - n1);                                         \
     _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                              \
       const bf16_t* src_ = (j < KI ? kb_ : vb_) + (soff[j] + (one_ ? 0 : dsoff[j]));              \
       const int dst_ = (j < KI ? (wave + NW * j) : 32 * HD / 512 + (wave + NW * (j - KI))) * 512;  \
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
   }
   const float sl2 = a.scale * 1.4426950408889634f;
   // keys below this bound are visible to every query of the workgroup
-  const int kfull = a.causal ? min(kend, a.qpos0 + q0wg + 1) : kend;
+  const int kfull = a.causal ? min(kend, qpos0 + q0wg + 1) : kend;
 
 #define DG_ATILE(S, KT)                                                                            \
   do {                                                                                             \
@@ -327,6 +329,7 @@ hipError_t attention(const AttnArgs& a, hipStream_t s) {
   const int GQ = a.H / a.Hkv;
   if (a.H % a.Hkv != 0 || (GQ != 1 && GQ != 2 && GQ != 4)) return hipErrorInvalidValue;
   if (a.split_len % 32 != 0 || a.rows_per_batch <= 0 || a.n1 % 32 != 0 || a.n2 % 32 != 0) return hipErrorInvalidValue;
+  if (a.pos_dev && (!a.causal || a.n2 != 0)) return hipErrorInvalidValue;
   if (a.splits < 1 || (a.splits == 1 && !a.out) || (a.splits > 1 && (!a.opart || !a.mlpart)))
     return hipErrorInvalidValue;
   switch (a.hd * 10 + GQ) {

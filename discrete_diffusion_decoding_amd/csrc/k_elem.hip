@@ -139,8 +139,10 @@ hipError_t rmsnorm_rows(float* h, const bf16_t* w, int rows, int d, float eps, b
 // ---------------------------------------------------------------------------
 // Rotary table of one pass: cos / sin of position pos0 + (r % per_batch) at
 // frequency theta^(-2j/hd), computed once in fp64 for all layers of the pass.
-__global__ void rope_table_kernel(float2* tab, int per_batch, int pos0, int half, float theta) {
+__global__ void rope_table_kernel(float2* tab, int per_batch, int pos0, int half, float theta,
+                                  const int32_t* pos_dev) {
   const int t = blockIdx.x;
+  if (pos_dev) pos0 = *pos_dev;
   for (int j = threadIdx.x; j < half; j += blockDim.x) {
     const double freq = exp(-(2.0 * (double)j / (double)(2 * half)) * log((double)theta));
     double sv, cv;
@@ -149,9 +151,11 @@ __global__ void rope_table_kernel(float2* tab, int per_batch, int pos0, int half
   }
 }
 
-hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta, hipStream_t s) {
+hipError_t rope_table(float2* tab, int per_batch, int pos0, int hd, float theta, const int32_t* pos_dev,
+                      hipStream_t s) {
   if (per_batch <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_table_kernel, dim3(per_batch), dim3(128), 0, s, tab, per_batch, pos0, hd / 2, theta);
+  hipLaunchKernelGGL(rope_table_kernel, dim3(per_batch), dim3(128), 0, s, tab, per_batch, pos0, hd / 2, theta,
+                     pos_dev);
   return hipGetLastError();
 }
 
@@ -214,7 +218,7 @@ __device__ __forceinline__ void qk_rope_head(const QkRopeArgs& a, int r, int hh)
   for (int j = 0; j < EPL; ++j) x[j] = x[j] * inv * w[j];
   const float sgn = e0 < HALF ? -1.f : 1.f;
   bf16_t* dst = isq ? a.q + ((long)r * a.H + hh) * HD + e0
-                    : a.kdst + bidx * a.k_bstride + (hh - a.H) * a.k_hstride + (long)(a.t_offset + tloc) * HD + e0;
+                    : a.kdst + bidx * a.k_bstride + (hh - a.H) * a.k_hstride + (long)((a.pos_dev ? *a.pos_dev : a.t_offset) + tloc) * HD + e0;
   uint16_t y[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
@@ -248,7 +252,7 @@ __device__ __forceinline__ void vt_scatter_block(const QkRopeArgs& a, int g, int
     dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
   }
   __syncthreads();
-  const int bidx = t0 / a.per_batch, p0 = a.t_offset + t0 % a.per_batch;
+  const int bidx = t0 / a.per_batch, p0 = (a.pos_dev ? *a.pos_dev : a.t_offset) + t0 % a.per_batch;
   const int dim = tid >> 2, pg = (tid & 3) * 8;
   const int nval = min(32, a.rows - t0);
   bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (long)(d0 + dim) * a.v_pitch + p0 + pg;

@@ -325,12 +325,13 @@ __global__ __launch_bounds__(256) void ar_sample_partial_kernel(ArSampleArgs a) 
   const int per = (ng + a.vsplit - 1) / a.vsplit;
   const int g0 = sl * per, g1 = min(ng, g0 + per);
   const float* l = a.logits + (long)b * a.ldl;
+  const int pos = a.pos_dev ? *a.pos_dev : a.pos;
   Stat t = Stat{-INFINITY, 0.f, 0.f, -INFINITY, 0x7FFFFFFF, -INFINITY, 0x7FFFFFFF};
   Screen c;
   screen_init(c);
   for (int g = g0 + (int)threadIdx.x; g < g1; g += 256) {
     const float4 x = *reinterpret_cast<const float4*>(l + 4L * g);
-    const dg_u32x4 w = dg_philox4x32_10((uint32_t)g, (uint32_t)a.pos, 0u, 2u, k0, k1);
+    const dg_u32x4 w = dg_philox4x32_10((uint32_t)g, (uint32_t)pos, 0u, 2u, k0, k1);
     const float lv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(256) void ar_sample_partial_kernel(ArSampleArgs a) 
   }
   if (screen_close(c, t)) {
     for (int g = g0 + (int)threadIdx.x; g < g1; g += 256) {
-      const dg_u32x4 w = dg_philox4x32_10((uint32_t)g, (uint32_t)a.pos, 0u, 2u, k0, k1);
+      const dg_u32x4 w = dg_philox4x32_10((uint32_t)g, (uint32_t)pos, 0u, 2u, k0, k1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v = 4 * g + j;

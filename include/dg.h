@@ -204,7 +204,10 @@ dg_status dg_prefill_append(dg_model* m, const int32_t* tokens, int32_t Bp, int3
  *   - argmax [B] (argmax of the logits), entropy [B] (nats, of softmax(l)) and
  *     logits_dump fp32 [B][V] are optional outputs (NULL to skip).
  * `next` may be the `token` buffer (the next call then reads it).  Sequences
- * run one after another, each one row through every layer.  Needs
+ * run one after another, each one row through every layer.  On a non-default
+ * stream (graphs enabled) the step is a captured hipGraph: P is written to
+ * the workspace and read on the device, so calls that differ only in P (for
+ * example decoding in place, token == next) replay one graph.  Needs
  * dg_workspace_bytes(m, 1, P + 1).  B in 1..16, P + 1 <= P_max, tau > 0,
  * vocab a multiple of 4; else a negative status before any device work. */
 dg_status dg_ar_step(dg_model* m, void* kv, int32_t B, int32_t P, int32_t P_max, const int32_t* token, float tau,

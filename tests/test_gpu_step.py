@@ -345,6 +345,39 @@ def test_ar_decode_two_sequences():
             assert nx[i, b] == osmp.ar_sample(lg[i, b], tau, seeds[b], P + i)[0], (b, i)
 
 
+def test_ar_graph_replay_equals_eager_launches():
+    """dg_ar_step on a non-default stream replays one captured graph for every
+    position (the position is read on the device); it writes the same tokens,
+    logits and cache as the kernels launched one by one, bit for bit."""
+    wl = WORKLOADS["tiny_step"]
+    m = wl.model
+    P, P_max, n = 64, 96, 5
+    dm = DeviceModel(m, SEED)
+    prompt = synth.tokens(SEED, "argraph", (1, P + 1), m.vocab)
+    seeds = synth.row_seeds(SEED + 5, 1)
+    out = {}
+    for mode in ("eager", "graph"):
+        kv = dm.kv_cache(1, P_max)
+        ws = dm.workspace(P, P_max)
+        stream = torch.cuda.Stream() if mode == "graph" else None
+        dg.dg_prefill_prefix(dm.handle, dev(prompt[:, :P]), 1, P, P_max, kv, ws, stream=stream)
+        tok = dev(prompt[:, P].astype(np.int32))
+        dump = torch.zeros(1, m.vocab, device="cuda")   # one buffer: the same graph serves every position
+        toks, logits = [], []
+        for i in range(n):
+            announce(f"ar {mode}: P={P + i}")
+            dg.dg_ar_step(dm.handle, kv, 1, P + i, P_max, tok, 0.8, seeds, tok, ws, logits_dump=dump,
+                          stream=stream)
+            torch.cuda.synchronize()
+            toks.append(int(host(tok)[0]))
+            logits.append(host(dump)[0].copy())
+        out[mode] = (toks, np.stack(logits), host(kv))
+    dm.close()
+    assert out["graph"][0] == out["eager"][0]
+    assert np.array_equal(out["graph"][1], out["eager"][1])
+    assert np.array_equal(out["graph"][2], out["eager"][2])
+
+
 def test_tiny_block_equals_repeated_steps():
     """dg_generate_block (device-driven step index, stop flag) equals the same
     number of host-driven dg_denoise_step calls, bit for bit."""
