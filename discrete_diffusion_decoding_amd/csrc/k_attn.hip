@@ -183,34 +183,55 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
   // keys below this bound are visible to every query of the workgroup
   const int kfull = a.causal ? min(kend, qpos0 + q0wg + 1) : kend;
 
-#define DG_ATILE(S, KT)                                                                            \
+// Raw scores S^T = K Q^T of the tile in stage S, into SC (two chains of MFMAs
+// interleaved over the head dim)
+#define DG_ASCORE(S, SC)                                                                           \
   do {                                                                                             \
-    const int kt = (KT);                                                                           \
-    floatx4 s[NF][2];                                                                              \
-    _Pragma("unroll") for (int j = 0; j < NF; ++j) s[j][0] = s[j][1] = floatx4{0.f, 0.f, 0.f, 0.f}; \
-    _Pragma("unroll") for (int kf = 0; kf < 2; ++kf)                                               \
-      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                          \
+    _Pragma("unroll") for (int j = 0; j < NF; ++j) SC[j][0] = SC[j][1] = floatx4{0.f, 0.f, 0.f, 0.f}; \
+    _Pragma("unroll") for (int ks = 0; ks < KS; ++ks)                                              \
+      _Pragma("unroll") for (int kf = 0; kf < 2; ++kf) {                                           \
         const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(&S[koff[kf][ks % KSB] + 128 * (ks / KSB)]); \
         _Pragma("unroll") for (int j = 0; j < NF; ++j)                                             \
-          s[j][kf] = mfma16x16x32(kfr, qfr[j][ks], s[j][kf]);                                      \
+          SC[j][kf] = mfma16x16x32(kfr, qfr[j][ks], SC[j][kf]);                                    \
       }                                                                                            \
-    const bool masked_ = kt + 32 > kfull;                                                          \
-    bf16x8 pf[NF];                                                                                 \
+  } while (0)
+
+// -inf for the keys of tile KT that a query may not see
+#define DG_AMASK(SC, KT)                                                                           \
+  do {                                                                                             \
+    _Pragma("unroll") for (int j = 0; j < NF; ++j)                                                 \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                              \
+        const int key = (KT) + 8 * lg + e;                                                         \
+        if (!(key < kend && (!a.causal || key <= qpos[j]))) SC[j][e >> 2][e & 3] = -INFINITY;      \
+      }                                                                                            \
+  } while (0)
+
+// Probabilities of the scores SC against the running max, as bf16 in PF; the
+// row sums go to l_run.  The exponentials are taken first against the current
+// max; a row whose max grew by more than 8 (log2 units) raises it, rescales its
+// accumulator and takes them again (the first tiles, rarely after).  A row
+// with no visible key yet (max -inf) gets zeros.
+#define DG_ASOFT(SC, PF)                                                                           \
+  do {                                                                                             \
+    float mx_[NF], ps_[NF];                                                                        \
+    bool up_ = false;                                                                              \
     _Pragma("unroll") for (int j = 0; j < NF; ++j) {                                               \
       float p[8];                                                                                  \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) p[e] = s[j][e >> 2][e & 3];                    \
-      if (masked_) {                                                                               \
-        _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                            \
-          const int key = kt + 8 * lg + e;                                                         \
-          if (!(key < kend && (!a.causal || key <= qpos[j]))) p[e] = -INFINITY;                    \
-        }                                                                                          \
-      }                                                                                            \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) p[e] = SC[j][e >> 2][e & 3];                   \
       float mx = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])), fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7]))); \
       mx = xrow_max(mx) * sl2;                                                                     \
-      /* raise the running max only when it grows by more than 8 (log2 units) */                   \
-      const bool up = mx > m_run[j] + 8.0f;                                                        \
-      if (__builtin_amdgcn_ballot_w64(up)) {                                                       \
-        const float m_new = fmaxf(m_run[j], mx);                                                   \
+      mx_[j] = mx;                                                                                 \
+      up_ = up_ || (mx > m_run[j] + 8.0f);                                                         \
+      const float nm = m_run[j] == -INFINITY ? 0.f : -m_run[j];                                    \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(p[e], sl2, nm)); \
+      ps_[j] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));                 \
+      _Pragma("unroll") for (int e = 0; e < 8; ++e) PF[j][e] = (__bf16)p[e];                       \
+      /* keeps this path ahead of the branch, beside the MFMAs (not sunk into its else) */         \
+      asm volatile("" ::"v"(PF[j]), "v"(ps_[j]));                                                  \
+    }                                                                                              \
+    if (__builtin_amdgcn_ballot_w64(up_)) {                                                        \
+      _Pragma("unroll") for (int j = 0; j < NF; ++j) {                                             \
+        const float m_new = fmaxf(m_run[j], mx_[j]);                                               \
         const float alpha = (m_run[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[j] - m_new); \
         l_run[j] *= alpha;                                                                         \
         m_run[j] = m_new;                                                                          \
@@ -218,36 +239,46 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
           const float ai = __shfl(alpha, lg * 4 + i, 64);                                          \
           _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) O[j][nf][i] *= ai;                    \
         }                                                                                          \
-      }                                                                                            \
-      const float nm_ = -m_run[j];                                                                 \
-      if (masked_) {                                                                               \
-        const bool any_ = m_run[j] != -INFINITY;                                                   \
+        const float nm = m_new == -INFINITY ? 0.f : -m_new;                                        \
+        float p[8];                                                                                \
         _Pragma("unroll") for (int e = 0; e < 8; ++e)                                              \
-          p[e] = any_ ? __builtin_amdgcn_exp2f(fmaf(p[e], sl2, nm_)) : 0.f;                        \
-      } else {                                                                                     \
-        _Pragma("unroll") for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(p[e], sl2, nm_)); \
+          p[e] = __builtin_amdgcn_exp2f(fmaf(SC[j][e >> 2][e & 3], sl2, nm));                      \
+        ps_[j] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));               \
+        _Pragma("unroll") for (int e = 0; e < 8; ++e) PF[j][e] = (__bf16)p[e];                     \
       }                                                                                            \
-      l_run[j] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));               \
-      _Pragma("unroll") for (int e = 0; e < 8; ++e) pf[j][e] = (__bf16)p[e];                       \
     }                                                                                              \
+    _Pragma("unroll") for (int j = 0; j < NF; ++j) l_run[j] += ps_[j];                             \
+  } while (0)
+
+// O += P V with V^T of the tile in stage S
+#define DG_APV(S, PF)                                                                              \
+  do {                                                                                             \
     _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) {                                           \
       const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&S[voff[nf & 1] + 512 * nf]);             \
-      _Pragma("unroll") for (int j = 0; j < NF; ++j) O[j][nf] = mfma16x16x32(pf[j], vb, O[j][nf]); \
+      _Pragma("unroll") for (int j = 0; j < NF; ++j) O[j][nf] = mfma16x16x32(PF[j], vb, O[j][nf]); \
     }                                                                                              \
   } while (0)
 
-  // Ring of 4: when tile t is read, tiles t+1 and t+2 may still be in flight.
-  // All LDS reads of tile t precede the DMA of tile t+3 (start clamped to the
-  // last tile, so every iteration issues the same count), which goes to the
-  // buffer of tile t-1, free once every wave passed this iteration's barrier;
-  // with the reads first the compiler adds no wait of its own.
-#define DG_AITER(T, CUR, NXT)                                                                      \
+  // Software pipeline over a ring of 4 stages.  Iteration T holds the scores
+  // of tile T in SCUR; it waits for tile T+1 (tile T+2 may still be in
+  // flight), computes the scores of tile T+1 into SNXT from stage KB while the
+  // softmax of tile T runs, then P V from stage VB.  The scores of the tile
+  // past the last are computed from a clamped copy and dropped.  The DMA of
+  // tile T+3 (clamped to the last tile, so every iteration issues the same
+  // count) follows every LDS read of the iteration and goes to the stage of
+  // tile T-1, which every wave left before this iteration's barrier.
+#define DG_AITER(T, VB, KB, DB, SCUR, SNXT)                                                        \
   do {                                                                                             \
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm_attn(2 * IPW));                                          \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_attn(IPW));                                              \
     __builtin_amdgcn_s_barrier();                                                                  \
-    DG_ATILE(CUR, kbeg + 32 * (T));                                                                \
+    const int kt_ = kbeg + 32 * (T);                                                               \
+    if (kt_ + 32 > kfull) DG_AMASK(SCUR, kt_);                                                     \
+    bf16x8 pf_[NF];                                                                                \
+    DG_ASCORE(KB, SNXT);                                                                           \
+    DG_ASOFT(SCUR, pf_);                                                                           \
+    DG_APV(VB, pf_);                                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                             \
-    DG_AISSUE(NXT, kbeg + 32 * min((T) + 3, ntile - 1));                                           \
+    DG_AISSUE(DB, kbeg + 32 * min((T) + 3, ntile - 1));                                            \
     __builtin_amdgcn_sched_barrier(0);                                                             \
   } while (0)
 
@@ -262,21 +293,28 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     DG_AISSUE(S0, kbeg);
     DG_AISSUE(S1, kbeg + 32 * min(1, ntile - 1));
     DG_AISSUE(S2, kbeg + 32 * min(2, ntile - 1));
+    floatx4 sa[NF][2], sb[NF][2];
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_attn(2 * IPW));
+    __builtin_amdgcn_s_barrier();
+    DG_ASCORE(S0, sa);
     // full rounds of four, then the last 0-3 tiles: a loop without early
     // exits keeps the compiler from draining the ring at its head
     int t = 0;
     for (; t + 4 <= ntile; t += 4) {
-      DG_AITER(t, S0, S3);
-      DG_AITER(t + 1, S1, S0);
-      DG_AITER(t + 2, S2, S1);
-      DG_AITER(t + 3, S3, S2);
+      DG_AITER(t, S0, S1, S3, sa, sb);
+      DG_AITER(t + 1, S1, S2, S0, sb, sa);
+      DG_AITER(t + 2, S2, S3, S1, sa, sb);
+      DG_AITER(t + 3, S3, S0, S2, sb, sa);
     }
-    if (t < ntile) DG_AITER(t, S0, S3);
-    if (t + 1 < ntile) DG_AITER(t + 1, S1, S0);
-    if (t + 2 < ntile) DG_AITER(t + 2, S2, S1);
+    if (t < ntile) DG_AITER(t, S0, S1, S3, sa, sb);
+    if (t + 1 < ntile) DG_AITER(t + 1, S1, S2, S0, sb, sa);
+    if (t + 2 < ntile) DG_AITER(t + 2, S2, S3, S1, sa, sb);
   }
 #undef DG_AITER
-#undef DG_ATILE
+#undef DG_APV
+#undef DG_ASOFT
+#undef DG_AMASK
+#undef DG_ASCORE
 #undef DG_AISSUE
   __builtin_amdgcn_s_waitcnt(0);
 
