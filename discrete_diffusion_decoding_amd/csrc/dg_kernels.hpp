@@ -35,6 +35,8 @@ struct GemmArgs {
   int tile_rows;   // 64-row kernel: activation rows per tile (64, the work-list chunk size; dense rows also 128),
   int tile_cols;   // weight rows per tile (64 | 128)
   int ring;        // and its LDS ring depth (64 wide: 4 | 5; 128 wide: 2 | 3)
+  int few_rows;    // work-list products: a bound (1..kGemvRows) on the rows of every item, when one is
+                   // known (decoding); 0 otherwise.  Dense products use M.
   void* C;
   long ldc;
   long c_kstride;
@@ -55,6 +57,10 @@ inline bool gemm_fat2_pitch_ok(long lda, long ldw) {
   return (long)kFatRowChunk * lda * 2 < 0x7FFFFFFFL && 256L * ldw * 2 < 0x7FFFFFFFL;
 }
 constexpr int kGemmRowChunk = 64;
+// products whose items hold at most kGemvRows rows (and k chunks of at most
+// kGemvK columns) run on the weight-streaming GEMV kernel instead
+constexpr int kGemvRows = 4;
+constexpr int kGemvK = 4096;
 
 // ---- elementwise / reduction kernels (k_elem.hip) ----
 

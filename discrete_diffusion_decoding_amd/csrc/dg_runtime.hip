@@ -425,7 +425,8 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   int32_t* slot_row = at<int32_t>(ws, p.slot_row);
   int4* items = at<int4>(ws, p.items);
   int32_t* nitems = at<int32_t>(ws, p.nitems);
-  const int items_max = E + cdiv((long)R * k, m->x_rows);
+  // every item holds at least one of the R k slots
+  const int items_max = (int)std::min<long>(E + cdiv((long)R * k, m->x_rows), (long)R * k);
   bf16_t* hbuf = at<bf16_t>(ws, p.hbuf);
   bf16_t* ybuf = at<bf16_t>(ws, p.ybuf);
   bf16_t* hs = at<bf16_t>(ws, p.hs);
@@ -601,6 +602,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.A = xn2; g.lda = D; g.a_rows = slot_row; g.W = lw(m, l, m->lay.w_gate); g.W2 = lw(m, l, m->lay.w_up);
       g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D;
       g.items = items; g.n_items = nitems; g.items_max = items_max; g.tile_rows = m->x_rows; g.tile_cols = m->x_cols; g.ring = m->x_ring;
+      g.few_rows = R <= kGemvRows ? R : 0;   // an expert takes each row at most once
       g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_GATEUP, st);
       DG_CK(gemm(EPI_GEGLU_BF16, g, st));
@@ -610,6 +612,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.A = hbuf; g.lda = fe; g.W = lw(m, l, m->lay.w_down); g.ldw = fe; g.w_gstride = (long)D * fe; g.K = fe;
       g.N = D; g.k_chunk = fe; g.items = items; g.n_items = nitems; g.items_max = items_max;
       g.tile_rows = m->x_rows; g.tile_cols = m->xd_cols; g.ring = m->xd_ring;
+      g.few_rows = R <= kGemvRows ? R : 0;
       g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_BF16, g, st));

@@ -351,10 +351,193 @@ static hipError_t launch(const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few-row products (decoding: one activation row per sequence, a handful per
+// expert).  The MFMA tile would spend 64 activation rows of DMA and LDS on each
+// live row, so these stream the weights straight into registers instead: the
+// item's activation rows (<= RB, its k chunk) are staged once in LDS, and a
+// wave takes 8 weight rows, read 8 x 128 contiguous bytes per load
+// instruction (lane l: row l / 8, 16-byte part l % 8 of each 128-byte step).
+// KW waves share the same 8 rows and split the k steps into KW contiguous
+// ranges of at most 16 steps, each issued as one batch of loads, so a wave
+// makes about one round trip to memory (KW = 1, 2, 4 for slices of up to 16,
+// 32, 64+ steps).  Lanes accumulate bf16 pair products in fp32
+// (v_dot2_f32_bf16); the 8 lanes of a row are summed by shuffles and the KW
+// waves through LDS.  Units are (item, column tile, k slice), as in the MFMA
+// kernel, with the same epilogues (GEGLU: 4 gate rows and their 4 up rows per
+// row set).
+template <int KW>
+constexpr int gemv_cols(bool geglu) { return (geglu ? 4 : 8) * (4 / KW); }
+template <int EPI, bool ITEMS, int RB, int KW>
+__global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
+  constexpr bool GEGLU = EPI == EPI_GEGLU_BF16;
+  constexpr int NCOL = gemv_cols<KW>(GEGLU);   // output columns per workgroup
+  constexpr int U = 16;                        // 128-byte steps per batch of loads
+  __shared__ __attribute__((aligned(16))) bf16_t X[RB * kGemvK];
+  __shared__ float red[4][8][RB];
+  if (g.flag && *g.flag) return;
+  const int ntiles = (g.N + NCOL - 1) / NCOL;
+  const long per = (long)ntiles * g.k_split;
+  const long nunits = (ITEMS ? (long)*g.n_items : 1L) * per;
+  const long u = blockIdx.x;
+  if (u >= nunits) return;
+  const int item = (int)(u / per);
+  const int tile = (int)((u % per) % ntiles), zk = (int)((u % per) / ntiles);
+  int grp, r0, nrows;
+  if (ITEMS) {
+    const int4 it = g.items[item];
+    grp = it.x;
+    r0 = it.y;
+    nrows = min(it.z, RB);
+  } else {
+    grp = 0;
+    r0 = 0;
+    nrows = min(g.M, RB);
+  }
+  if (nrows <= 0) return;
+  const int kb = zk * g.k_chunk;
+  const int nk = min(g.K, kb + g.k_chunk) - kb;   // a multiple of 64
+  if (nk <= 0) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int rs = lane >> 3, part = lane & 7;
+  const int set = wave / KW, kw = wave % KW;   // row set of this wave, and its k range
+  const int col = tile * NCOL + set * (GEGLU ? 4 : 8) + (GEGLU ? (rs & 3) : rs);
+  const bf16_t* Wb = (GEGLU && rs >= 4) ? g.W2 : g.W;
+  const bf16_t* wp = Wb + (long)grp * g.w_gstride + (long)min(col, g.N - 1) * g.ldw + kb + 8 * part;
+  const int nst = nk >> 6;
+  const int st_lo = (kw * nst) / KW, st_hi = ((kw + 1) * nst) / KW;
+  // the first batch of weight loads goes out before the activation staging
+  bf16x8 w[U];
+  if (st_lo < st_hi) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) w[j] = load_bf16x8(wp + 64 * min(st_lo + j, st_hi - 1));
+  }
+
+  // stage the activation rows (16 bytes per thread and pass; rows past the
+  // item's end are zero)
+  const int c16 = nk >> 3;
+  for (int i = tid; i < RB * c16; i += 256) {
+    const int r = i / c16, c = i - r * c16;
+    bf16x8 v;
+    if (r < nrows) {
+      const int ar = g.a_rows ? g.a_rows[r0 + r] : r0 + r;
+      v = load_bf16x8(g.A + (long)ar * g.lda + kb + 8 * c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.f;
+    }
+    *reinterpret_cast<bf16x8*>(&X[r * nk + 8 * c]) = v;
+  }
+  __syncthreads();
+
+  const bf16_t* xp = X + 8 * part;
+  float acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = 0.f;
+  for (int s0 = st_lo; s0 < st_hi; s0 += U) {
+    if (s0 != st_lo) {
+#pragma unroll
+      for (int j = 0; j < U; ++j) w[j] = load_bf16x8(wp + 64 * min(s0 + j, st_hi - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (s0 + j < st_hi) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const bf16x8 xv = *reinterpret_cast<const bf16x8*>(xp + r * nk + 64 * (s0 + j));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 wa = {w[j][2 * e], w[j][2 * e + 1]};
+            const bf16x2 xa = {xv[2 * e], xv[2 * e + 1]};
+            acc[r] = __builtin_amdgcn_fdot2_f32_bf16(wa, xa, acc[r], false);
+          }
+        }
+      }
+    }
+  }
+  // sum the 8 parts of each row (lanes 8 rs .. 8 rs + 7), then the KW waves
+  // of the row set (in k order)
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    acc[r] += __shfl_xor(acc[r], 1, 64);
+    acc[r] += __shfl_xor(acc[r], 2, 64);
+    acc[r] += __shfl_xor(acc[r], 4, 64);
+  }
+  if (KW > 1) {
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) red[wave][rs][r] = acc[r];
+    }
+    __syncthreads();
+    if (kw != 0) return;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      float v = red[wave][rs][r];
+#pragma unroll
+      for (int q = 1; q < KW; ++q) v += red[wave + q][rs][r];
+      acc[r] = v;
+    }
+  }
+  float up[RB];
+  if (GEGLU) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) up[r] = __shfl(acc[r], (lane + 32) & 63, 64);
+  }
+  if (part != 0 || col >= g.N || (GEGLU && rs >= 4)) return;
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    if (r >= nrows) break;
+    const float v = acc[r];
+    const long off = (long)(r0 + r) * g.ldc + col;
+    if (EPI == EPI_STORE_BF16) {
+      reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(v);
+    } else if (EPI == EPI_STORE_F32) {
+      reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = v;
+    } else {
+      reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(gelu_tanh(v) * up[r]);
+    }
+  }
+}
+
+template <int EPI, bool ITEMS, int RB, int KW>
+static hipError_t gemv_launch(const GemmArgs& a, hipStream_t s) {
+  constexpr int NCOL = gemv_cols<KW>(EPI == EPI_GEGLU_BF16);
+  const long units = (ITEMS ? (long)a.items_max : 1L) * ((a.N + NCOL - 1) / NCOL) * a.k_split;
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemv_kernel<EPI, ITEMS, RB, KW>), dim3(units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int EPI, bool ITEMS, int RB>
+static hipError_t gemv_split(const GemmArgs& a, hipStream_t s) {
+  const int nst = a.k_chunk / 64;   // longest k slice, in 128-byte steps
+  if (nst <= 16) return gemv_launch<EPI, ITEMS, RB, 1>(a, s);
+  if (nst <= 32) return gemv_launch<EPI, ITEMS, RB, 2>(a, s);
+  return gemv_launch<EPI, ITEMS, RB, 4>(a, s);
+}
+
+template <int EPI, bool ITEMS>
+static hipError_t gemv_rows(const GemmArgs& a, int rows, hipStream_t s) {
+  if (rows == 1) return gemv_split<EPI, ITEMS, 1>(a, s);
+  if (rows == 2) return gemv_split<EPI, ITEMS, 2>(a, s);
+  return gemv_split<EPI, ITEMS, 4>(a, s);
+}
+
 hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
   if (a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;   // 16-byte aligned rows
   const bool it = a.items != nullptr;
+  const int few = it ? a.few_rows : a.M;
+  if (few >= 1 && few <= kGemvRows && a.k_chunk <= kGemvK) {
+    switch (epi) {
+      case EPI_STORE_BF16: return it ? gemv_rows<EPI_STORE_BF16, true>(a, few, s) : gemv_rows<EPI_STORE_BF16, false>(a, few, s);
+      case EPI_STORE_F32: return it ? gemv_rows<EPI_STORE_F32, true>(a, few, s) : gemv_rows<EPI_STORE_F32, false>(a, few, s);
+      case EPI_GEGLU_BF16: return it ? gemv_rows<EPI_GEGLU_BF16, true>(a, few, s) : gemv_rows<EPI_GEGLU_BF16, false>(a, few, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (epi) {
     case EPI_STORE_BF16: return it ? launch<EPI_STORE_BF16, true>(a, s) : launch<EPI_STORE_BF16, false>(a, s);
     case EPI_STORE_F32: return it ? launch<EPI_STORE_F32, true>(a, s) : launch<EPI_STORE_F32, false>(a, s);

@@ -22,9 +22,12 @@ def _bf16(x):
     return synth.f32_to_bf16_bits(x)
 
 
-# M < 192 runs on the 64-row tile kernel, M >= 192 on the 256-row one; the
-# cases cover ragged row chunks, ragged weight tiles and single-stage K.
-@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (37, 200, 192), (256, 2816, 2816), (300, 1024, 704),
+# M <= 4 runs on the weight-streaming GEMV kernel (k slices of up to 16, 32
+# and 64 steps of 64 columns take 1, 2 and 4 waves per row set), M < 192 on the
+# 64-row tile kernel, M >= 192 on the 256-row one; the cases cover ragged row
+# chunks, ragged weight tiles and single-stage K.
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (2, 200, 1536), (3, 136, 4096), (4, 72, 2816), (1, 8, 704),
+                                   (37, 200, 192), (256, 2816, 2816), (300, 1024, 704),
                                    (64, 8, 256), (192, 72, 64), (260, 200, 192), (513, 136, 320)])
 def test_gemm_matches_float64(M, N, K):
     announce(f"gemm M={M} N={N} K={K}")
