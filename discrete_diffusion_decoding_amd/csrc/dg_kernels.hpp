@@ -37,6 +37,13 @@ struct GemmArgs {
   int ring;        // and its LDS ring depth (64 wide: 4 | 5; 128 wide: 2 | 3)
   int few_rows;    // work-list products: a bound (1..kGemvRows) on the rows of every item, when one is
                    // known (decoding); 0 otherwise.  Dense products use M.
+  // GEMV work lists only: items of group >= grp_x read Wx (GEGLU up: Wx2) +
+  // (group - grp_x) * wx_gstride, rows ldwx apart (the shared FFN's blocks as
+  // extra experts); Wx == nullptr: none
+  const bf16_t* Wx;
+  const bf16_t* Wx2;
+  long ldwx, wx_gstride;
+  int grp_x;
   void* C;
   long ldc;
   long c_kstride;
@@ -120,8 +127,11 @@ hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits,
                            bf16_t* out, const int32_t* flag, hipStream_t s);
 
 // router logits = sum over split-K partials of the hi rows [0, rows) and lo rows [rows, 2 rows)
-hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
+// idx / gate [rows][k + ns]: the top-k, then experts E .. E + ns - 1 with gate 1
+hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate, int32_t* idx_dump,
                        float* gate_dump, const int32_t* flag, hipStream_t s);
+// k values moe_combine takes
+inline bool combine_k_ok(int k) { return k == 1 || k == 2 || k == 4 || k == 8 || k == 11; }
 // also emits the GEMM work list: int4 {expert, first slot, rows, chunk index << 16 |
 // chunks of the expert} per chunk of <= chunk rows of every touched expert, and
 // its length in *n_items

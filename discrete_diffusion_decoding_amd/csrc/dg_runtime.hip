@@ -286,6 +286,17 @@ static int vsplit_of(int rows, int V) {
   return vs;
 }
 
+// Decoding (at most kGemvRows rows): the shared FFN runs as d_shared / d_expert
+// extra experts E .. E + ns - 1 that every row takes with gate 1, inside the
+// grouped GEMV products (no second stream, no fork / join).  Returns ns, or 0
+// when the shared FFN runs as its own dense products.
+static int shared_as_experts(const dg_model_desc& d, int rows) {
+  if (d.d_shared == 0 || rows > kGemvRows || d.d_shared % d.d_expert) return 0;
+  const int ns = d.d_shared / d.d_expert;
+  if (d.n_experts + ns > 255 || !combine_k_ok(d.top_k + ns)) return 0;
+  return ns;
+}
+
 static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   Plan p{};
   const size_t R = rows, D = d.d_model, hd = d.head_dim, H = d.n_heads, Hkv = d.n_kv_heads, E = d.n_experts,
@@ -309,16 +320,18 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.xn2 = take(R * D * 2);
   p.xr = take(2 * R * D * 2);
   p.rlog = take((size_t)kMaxRouterSplit * 2 * R * E * 4);
-  p.eidx = take(R * k * 4);
-  p.egate = take(R * k * 4);
-  p.cnt = take((E + 1) * 4);
-  p.off = take((E + 1) * 4);
-  p.slot_of = take(R * k * 4);
-  p.slot_row = take(R * k * 4);
-  p.items = take((E + (R * k + 31) / 32) * 16);   // work list for chunks of >= 32 rows
+  // expert slots per row: top-k, plus the shared FFN's blocks when they run as experts
+  const size_t ns = shared_as_experts(d, rows), Ex = E + ns, kx = k + ns;
+  p.eidx = take(R * kx * 4);
+  p.egate = take(R * kx * 4);
+  p.cnt = take((Ex + 1) * 4);
+  p.off = take((Ex + 1) * 4);
+  p.slot_of = take(R * kx * 4);
+  p.slot_row = take(R * kx * 4);
+  p.items = take((Ex + (R * kx + 31) / 32) * 16);   // work list for chunks of >= 32 rows
   p.nitems = take(16);
-  p.hbuf = take(R * k * d.d_expert * 2);
-  p.ybuf = take(R * k * D * 2);
+  p.hbuf = take(R * kx * d.d_expert * 2);
+  p.ybuf = take(R * kx * D * 2);
   p.hs = take(R * std::max(d.d_shared, 1) * 2);
   p.ys = take(d.d_shared ? (size_t)kMaxDenseSplit * R * D * 4 : 0);
   if (V) {
@@ -425,8 +438,10 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   int32_t* slot_row = at<int32_t>(ws, p.slot_row);
   int4* items = at<int4>(ws, p.items);
   int32_t* nitems = at<int32_t>(ws, p.nitems);
-  // every item holds at least one of the R k slots
-  const int items_max = (int)std::min<long>(E + cdiv((long)R * k, m->x_rows), (long)R * k);
+  // shared FFN blocks as experts E .. Ex - 1 (decoding), in slots k .. kx - 1 of every row
+  const int ns = shared_as_experts(d, R), Ex = E + ns, kx = k + ns;
+  // every item holds at least one of the R kx slots
+  const int items_max = (int)std::min<long>(Ex + cdiv((long)R * kx, m->x_rows), (long)R * kx);
   bf16_t* hbuf = at<bf16_t>(ws, p.hbuf);
   bf16_t* ybuf = at<bf16_t>(ws, p.ybuf);
   bf16_t* hs = at<bf16_t>(ws, p.hs);
@@ -548,7 +563,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     Partials ysp{ys, 0, (long)R * D};
     bool forked = false;
     hipStream_t ss = st;
-    if (fs && !m->prof.on && side_stream(m)) {
+    if (fs && !ns && !m->prof.on && side_stream(m)) {
       DG_CK(hipEventRecord(m->ev_fork, st));
       ss = m->side;
       forked = true;
@@ -588,11 +603,12 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     }
     {
       ProfScope psr_(m, DG_PROF_ROUTER, st);
-      DG_CK(router_topk(rlp, R, E, k, eidx, egate, ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
+      DG_CK(router_topk(rlp, R, E, k, ns, eidx, egate,
+                        ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
                         ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
-      DG_CK(moe_permute(eidx, R, k, E, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
+      DG_CK(moe_permute(eidx, R, kx, Ex, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
     }
-    if (fs) {
+    if (fs && !ns) {
       dg_status sr = shared_ffn();
       if (sr != DG_OK) return sr;
     }
@@ -603,6 +619,10 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.ldw = D; g.w_gstride = (long)fe * D; g.K = D; g.N = fe; g.k_chunk = D;
       g.items = items; g.n_items = nitems; g.items_max = items_max; g.tile_rows = m->x_rows; g.tile_cols = m->x_cols; g.ring = m->x_ring;
       g.few_rows = R <= kGemvRows ? R : 0;   // an expert takes each row at most once
+      if (ns) {   // shared gate / up blocks [ns][fe][D]
+        g.Wx = lw(m, l, m->lay.w_gate_sh); g.Wx2 = lw(m, l, m->lay.w_up_sh); g.ldwx = D;
+        g.wx_gstride = (long)fe * D; g.grp_x = E;
+      }
       g.C = hbuf; g.ldc = fe; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_GATEUP, st);
       DG_CK(gemm(EPI_GEGLU_BF16, g, st));
@@ -613,6 +633,9 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       g.N = D; g.k_chunk = fe; g.items = items; g.n_items = nitems; g.items_max = items_max;
       g.tile_rows = m->x_rows; g.tile_cols = m->xd_cols; g.ring = m->xd_ring;
       g.few_rows = R <= kGemvRows ? R : 0;
+      if (ns) {   // shared down block c: columns c fe .. of [D][fs]
+        g.Wx = lw(m, l, m->lay.w_down_sh); g.ldwx = fs; g.wx_gstride = fe; g.grp_x = E;
+      }
       g.C = ybuf; g.ldc = D; g.flag = ps.flag;
       ProfScope ps_(m, DG_PROF_EXPERT_DOWN, st);
       DG_CK(gemm(EPI_STORE_BF16, g, st));
@@ -623,7 +646,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     else if (ps.final_norm) nw = (const bf16_t*)m->w.final_norm;
     {
       ProfScope psc_(m, DG_PROF_OTHER, st);
-      DG_CK(moe_combine(h, ysp, ybuf, slot_of, egate, R, D, k, nw, d.rms_eps, xn,
+      DG_CK(moe_combine(h, ysp, ybuf, slot_of, egate, R, D, kx, nw, d.rms_eps, xn,
                         ps.hidden_dump ? ps.hidden_dump + (size_t)(l + 1) * R * D : nullptr, ps.flag, st));
     }
   }

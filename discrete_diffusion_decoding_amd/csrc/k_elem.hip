@@ -409,8 +409,11 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t x) {
   return umax64_swap<true>(x);
 }
 
+// Row r's slots: its NK routed experts (gates: softmax over their logits),
+// then ns always-on experts E .. E + ns - 1 with gate 1 (the shared FFN's
+// blocks, when they run as experts); the dumps hold the routed ones only.
 template <int NS, int NK>
-__global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, int32_t* idx, float* gate,
+__global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, int ns, int32_t* idx, float* gate,
                                                   int32_t* idx_dump, float* gate_dump, const int32_t* flag) {
   if (flag && *flag) return;
   const int lane = threadIdx.x;
@@ -455,30 +458,34 @@ __global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, 
   float den = ex;
 #pragma unroll
   for (int o = 1; o < NK; o <<= 1) den += __shfl_xor(den, o, 64);
+  const int ko = NK + ns;
   if (lane < NK) {
     const float gt = ex / den;
-    idx[(long)r * NK + lane] = mine_e;
-    gate[(long)r * NK + lane] = gt;
+    idx[(long)r * ko + lane] = mine_e;
+    gate[(long)r * ko + lane] = gt;
     if (idx_dump) idx_dump[(long)r * NK + lane] = mine_e;
     if (gate_dump) gate_dump[(long)r * NK + lane] = gt;
+  } else if (lane < ko) {
+    idx[(long)r * ko + lane] = E + lane - NK;
+    gate[(long)r * ko + lane] = 1.f;
   }
 }
 
-hipError_t router_topk(Partials rlog, int rows, int E, int k, int32_t* idx, float* gate, int32_t* idx_dump,
+hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate, int32_t* idx_dump,
                        float* gate_dump, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (E > 256 || k > E || rlog.n < 1 || rlog.n > 8) return hipErrorInvalidValue;
+  if (E > 256 || k > E || ns < 0 || k + ns > 64 || rlog.n < 1 || rlog.n > 8) return hipErrorInvalidValue;
   const dim3 grid(rows), block(64);
 #define DG_TOPK_NS(NK)                                                                                   \
   switch (rlog.n) {                                                                                      \
-    case 1: hipLaunchKernelGGL((topk_kernel<1, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 2: hipLaunchKernelGGL((topk_kernel<2, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 3: hipLaunchKernelGGL((topk_kernel<3, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 4: hipLaunchKernelGGL((topk_kernel<4, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 5: hipLaunchKernelGGL((topk_kernel<5, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 6: hipLaunchKernelGGL((topk_kernel<6, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 7: hipLaunchKernelGGL((topk_kernel<7, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
-    default: hipLaunchKernelGGL((topk_kernel<8, NK>), grid, block, 0, s, rlog, rows, E, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 1: hipLaunchKernelGGL((topk_kernel<1, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 2: hipLaunchKernelGGL((topk_kernel<2, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 3: hipLaunchKernelGGL((topk_kernel<3, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 4: hipLaunchKernelGGL((topk_kernel<4, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 5: hipLaunchKernelGGL((topk_kernel<5, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 6: hipLaunchKernelGGL((topk_kernel<6, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 7: hipLaunchKernelGGL((topk_kernel<7, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    default: hipLaunchKernelGGL((topk_kernel<8, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
   }
   switch (k) {
     case 1: DG_TOPK_NS(1) break;
@@ -665,6 +672,7 @@ hipError_t moe_combine(float* h, Partials ys, const bf16_t* Y, const int32_t* sl
     case 2: return combine_k<2>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
     case 4: return combine_k<4>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
     case 8: return combine_k<8>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
+    case 11: return combine_k<11>(h, ys, Y, slot_of, gate, rows, d, next_w, eps, xn, dump, flag, s);
     default: return hipErrorInvalidValue;
   }
 }

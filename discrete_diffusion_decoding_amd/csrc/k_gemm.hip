@@ -404,8 +404,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs g) {
   const int rs = lane >> 3, part = lane & 7;
   const int set = wave / KW, kw = wave % KW;   // row set of this wave, and its k range
   const int col = tile * NCOL + set * (GEGLU ? 4 : 8) + (GEGLU ? (rs & 3) : rs);
-  const bf16_t* Wb = (GEGLU && rs >= 4) ? g.W2 : g.W;
-  const bf16_t* wp = Wb + (long)grp * g.w_gstride + (long)min(col, g.N - 1) * g.ldw + kb + 8 * part;
+  const bool alt = ITEMS && g.Wx && grp >= g.grp_x;
+  const bf16_t* Wb = alt ? ((GEGLU && rs >= 4) ? g.Wx2 : g.Wx) + (long)(grp - g.grp_x) * g.wx_gstride
+                         : ((GEGLU && rs >= 4) ? g.W2 : g.W) + (long)grp * g.w_gstride;
+  const bf16_t* wp = Wb + (long)min(col, g.N - 1) * (alt ? g.ldwx : g.ldw) + kb + 8 * part;
   const int nst = nk >> 6;
   const int st_lo = (kw * nst) / KW, st_hi = ((kw + 1) * nst) / KW;
   // the first batch of weight loads goes out before the activation staging
@@ -530,7 +532,9 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;   // 16-byte aligned rows
   const bool it = a.items != nullptr;
   const int few = it ? a.few_rows : a.M;
-  if (few >= 1 && few <= kGemvRows && a.k_chunk <= kGemvK) {
+  const bool gemv = few >= 1 && few <= kGemvRows && a.k_chunk <= kGemvK;
+  if (a.Wx && (!it || !gemv || a.ldwx % 8 != 0)) return hipErrorInvalidValue;   // alternate weights: GEMV only
+  if (gemv) {
     switch (epi) {
       case EPI_STORE_BF16: return it ? gemv_rows<EPI_STORE_BF16, true>(a, few, s) : gemv_rows<EPI_STORE_BF16, false>(a, few, s);
       case EPI_STORE_F32: return it ? gemv_rows<EPI_STORE_F32, true>(a, few, s) : gemv_rows<EPI_STORE_F32, false>(a, few, s);
