@@ -363,6 +363,207 @@ static void attn_shape(const AttnArgs& a, hipStream_t s) {
   attn_launch<HD, GQ, NW, NF>(a, s);
 }
 
+// ---------------------------------------------------------------------------
+// Decoding: at most 8 (query, head) rows per kv head (one token, or a few, per
+// sequence) over a causal prefix.  The 16-row MFMA tile and its LDS ring would
+// move every K/V tile for 1-2 live rows, so a workgroup of 8 waves takes one
+// (sequence, kv head, key split) and issues all its K and V^T loads at once
+// (one round trip), straight to registers:
+//   scores: LPK = HD / 32 lanes per key, each with 32 dims of the K row (four
+//           16-byte loads) against the NQ query rows held in LDS, summed over
+//           the LPK lanes by shuffles (bf16 pair products in fp32, dot2);
+//   softmax: wave q takes query row q over the split's keys in LDS (max in
+//           log2 units, exp2, sum), as the MFMA kernel's (m, l);
+//   P V:    8 lanes per V^T row read 64 consecutive keys (128 bytes), summed
+//           over the 8 lanes.
+// Outputs match the MFMA kernel's: normalised O per split plus (m, l), merged
+// by attention_merge, or the final O for one split.
+constexpr int kDecThreads = 512;
+constexpr int dec_max_keys(int hd) { return 4 * kDecThreads / (hd / 32); }   // 4 passes of keys
+
+template <int HD, int NQ>
+__global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnArgs a) {
+  constexpr int LPK = HD / 32;              // lanes per key
+  constexpr int KPP = kDecThreads / LPK;    // keys per pass
+  constexpr int MAXK = 4 * KPP;             // keys per split
+  constexpr int VCH = MAXK / 64;            // 64-key chunks of a V^T row
+  constexpr int VDP = HD / 64;              // dim passes of P V (64 rows each)
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[NQ * HD];
+  __shared__ __attribute__((aligned(16))) float Ps[NQ * MAXK];
+  if (a.flag && *a.flag) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int GQ = a.H / a.Hkv, R = a.rows_per_batch, nq = R * GQ;
+  const int split = blockIdx.x % a.splits;
+  const int g = (blockIdx.x / a.splits) % a.Hkv;
+  const int b = blockIdx.x / (a.splits * a.Hkv);
+  const int qpos0 = a.pos_dev ? *a.pos_dev : a.qpos0;
+  const int n1 = a.pos_dev ? (qpos0 + R + 31) & ~31 : a.n1;
+  const int kbeg = split * a.split_len;
+  const int kend = min(min(n1, kbeg + a.split_len), qpos0 + R);   // causal: keys up to the last row
+  const int b1 = (a.nb1 == 1) ? 0 : b;
+  const bf16_t* K1 = a.k1 + b1 * a.k1_bstride + g * a.k1_hstride;
+  const bf16_t* V1 = a.vt1 + b1 * a.v1_bstride + g * a.v1_hstride;
+
+  // all K and V^T loads first
+  const int kpart = tid % LPK, kslot = tid / LPK;
+  bf16x8 kv[4][4];
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    const int key = kbeg + ps * KPP + kslot;
+    if (key < kend) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[ps][i] = load_bf16x8(K1 + (long)key * HD + 32 * kpart + 8 * i);
+    }
+  }
+  const int vpart = tid & 7, vrow = tid >> 3;
+  bf16x8 vv[VDP][VCH];
+#pragma unroll
+  for (int dp = 0; dp < VDP; ++dp)
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int k0 = kbeg + 64 * c + 8 * vpart;
+      if (k0 < kend) vv[dp][c] = load_bf16x8(V1 + (long)(64 * dp + vrow) * a.v1_pitch + k0);
+    }
+  // query rows q = r GQ + j (head g GQ + j, row r) into LDS
+  for (int i = tid; i < NQ * (HD / 8); i += kDecThreads) {
+    const int q = i / (HD / 8), c = i % (HD / 8);
+    bf16x8 v;
+    if (q < nq) {
+      const int h = g * GQ + q % GQ, r = q / GQ;
+      v = load_bf16x8(a.q + ((long)(b * R + r) * a.H + h) * HD + 8 * c);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.f;
+    }
+    *reinterpret_cast<bf16x8*>(&Qs[q * HD + 8 * c]) = v;
+  }
+  __syncthreads();
+
+  // scores (raw dot products; -inf where a row may not see the key)
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    const int kl = ps * KPP + kslot, key = kbeg + kl;
+    float sc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float acc = 0.f;
+      if (key < kend) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&Qs[q * HD + 32 * kpart + 8 * i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 x = {kv[ps][i][2 * e], kv[ps][i][2 * e + 1]};
+            const bf16x2 y = {qv[2 * e], qv[2 * e + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+          }
+        }
+      }
+      sc[q] = acc;
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1) sc[q] += __shfl_xor(sc[q], o, 64);
+    if (kpart == 0) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const bool vis = key < kend && q < nq && key <= qpos0 + q / GQ;
+        Ps[q * MAXK + kl] = vis ? sc[q] : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+
+  // softmax of row q = wave over the split (log2 units, as the MFMA kernel)
+  const float sl2 = a.scale * 1.4426950408889634f;
+  __shared__ float mls[NQ][2];
+  const int nk = max(kend - kbeg, 0);
+  if (wave < NQ) {
+    const int q = wave;
+    float mx = -INFINITY;
+    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, Ps[q * MAXK + k]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    const float m2 = mx * sl2;
+    float l = 0.f;
+    for (int k = lane; k < MAXK; k += 64) {
+      const float sv = Ps[q * MAXK + k];
+      const float pv = (k < nk && mx != -INFINITY) ? __builtin_amdgcn_exp2f(fmaf(sv, sl2, -m2)) : 0.f;
+      Ps[q * MAXK + k] = pv;
+      l += pv;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane == 0) {
+      mls[q][0] = m2;
+      mls[q][1] = l;
+    }
+  }
+  __syncthreads();
+
+  // O = P V over the split, normalised by the split's sum
+  float o[VDP][NQ];
+#pragma unroll
+  for (int dp = 0; dp < VDP; ++dp)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) o[dp][q] = 0.f;
+#pragma unroll
+  for (int c = 0; c < VCH; ++c) {
+    if (kbeg + 64 * c + 8 * vpart < kend) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float4 p0 = *reinterpret_cast<const float4*>(&Ps[q * MAXK + 64 * c + 8 * vpart]);
+        const float4 p1 = *reinterpret_cast<const float4*>(&Ps[q * MAXK + 64 * c + 8 * vpart + 4]);
+        const float pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int dp = 0; dp < VDP; ++dp) {
+          float acc = o[dp][q];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fmaf(pw[e], (float)vv[dp][c][e], acc);
+          o[dp][q] = acc;
+        }
+      }
+    }
+  }
+  const long BR = (long)a.B * R;
+#pragma unroll
+  for (int dp = 0; dp < VDP; ++dp)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float v = o[dp][q];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      if (vpart == 0 && q < nq) {
+        const int h = g * GQ + q % GQ, r = q / GQ, d = 64 * dp + vrow;
+        const float l = mls[q][1];
+        const float y = l > 0.f ? v / l : 0.f;
+        bf16_t* op = a.splits == 1 ? a.out + ((long)(b * R + r) * a.H + h) * HD
+                                   : a.opart + (((long)split * BR + (long)b * R + r) * a.H + h) * HD;
+        op[d] = f2bf(y);
+      }
+    }
+  if (a.splits > 1 && tid < nq) {
+    const int q = tid, h = g * GQ + q % GQ, r = q / GQ;
+    float* mp = a.mlpart + (((long)split * BR + (long)b * R + r) * a.H + h) * 2;
+    mp[0] = mls[q][0];
+    mp[1] = mls[q][1];
+  }
+}
+
+template <int HD>
+static bool attn_decode(const AttnArgs& a, hipStream_t s) {
+  const int nq = a.rows_per_batch * (a.H / a.Hkv);
+  if (!a.causal || a.n2 != 0 || nq > 8 || a.split_len > dec_max_keys(HD)) return false;
+  const dim3 grid(a.B * a.Hkv * a.splits), block(kDecThreads);
+  if (nq <= 1) hipLaunchKernelGGL((attn_decode_kernel<HD, 1>), grid, block, 0, s, a);
+  else if (nq <= 2) hipLaunchKernelGGL((attn_decode_kernel<HD, 2>), grid, block, 0, s, a);
+  else if (nq <= 4) hipLaunchKernelGGL((attn_decode_kernel<HD, 4>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_decode_kernel<HD, 8>), grid, block, 0, s, a);
+  return true;
+}
+
 hipError_t attention(const AttnArgs& a, hipStream_t s) {
   const int GQ = a.H / a.Hkv;
   if (a.H % a.Hkv != 0 || (GQ != 1 && GQ != 2 && GQ != 4)) return hipErrorInvalidValue;
@@ -370,6 +571,9 @@ hipError_t attention(const AttnArgs& a, hipStream_t s) {
   if (a.pos_dev && (!a.causal || a.n2 != 0)) return hipErrorInvalidValue;
   if (a.splits < 1 || (a.splits == 1 && !a.out) || (a.splits > 1 && (!a.opart || !a.mlpart)))
     return hipErrorInvalidValue;
+  // decoding passes (a few rows per sequence, causal prefix only)
+  if (a.hd == 64 ? attn_decode<64>(a, s) : a.hd == 128 ? attn_decode<128>(a, s) : a.hd == 256 && attn_decode<256>(a, s))
+    return hipGetLastError();
   switch (a.hd * 10 + GQ) {
     case 641: attn_shape<64, 1>(a, s); break;
     case 642: attn_shape<64, 2>(a, s); break;
