@@ -214,6 +214,43 @@ def test_ragged_append_extends_prefix_cache():
     dm.close()
 
 
+def test_small_appends_extend_prefix_cache():
+    """Appends of 3, 1 and 2 tokens after a 32-token prefill (at most 4 rows
+    per pass: the GEMV products and the decode attention kernel, several query
+    rows with their own causal bounds) give K/V within rel-L2 1e-2 of the
+    oracle's prefill of the whole sequence in every layer."""
+    wl = WORKLOADS["tiny_step"]
+    m = wl.model
+    P_max = 64
+    sizes = (3, 1, 2)
+    P = 32 + sum(sizes)
+    dm = DeviceModel(m, SEED)
+    toks = synth.tokens(SEED, "small", (1, P), m.vocab)
+    kv = dm.kv_cache(1, P_max)
+    ws = dm.workspace(32, P_max)
+    announce("small appends: prefill 32")
+    dg.dg_prefill_prefix(dm.handle, dev(toks[:, :32]), 1, 32, P_max, kv, ws)
+    p0 = 32
+    for n in sizes:
+        announce(f"small appends: {n} tokens at {p0}")
+        dg.dg_prefill_append(dm.handle, dev(toks[:, p0:p0 + n]), 1, p0, n, P_max, kv, ws)
+        p0 += n
+    announce("small appends: oracle")
+    M = om.Model(m, synth.SynthWeights(m, SEED, cache_layers=True))
+    recs = []
+    kv_o, _ = M.prefill_tokens(toks[0], recs)
+    skip = np.zeros(P, dtype=bool)
+    for l in range(m.n_layers):
+        K, V = kv_layer(kv, m, 1, P_max, l, 0, P_max)
+        assert not K[P:].any() and not V[P:].any(), l
+        rows = ~skip
+        assert rel_l2(K[:P][rows], kv_o[l][0][rows]) <= 1e-2, l
+        assert rel_l2(V[:P][rows], kv_o[l][1][rows]) <= 1e-2, l
+        skip[near_tie_rows(recs[l]["router_logits"], m.top_k, 1e-3)] = True
+    assert skip.sum() <= 4
+    dm.close()
+
+
 def test_block_append_extends_prefix_cache():
     """A finished block appended with dg_prefill_append leaves the cache as a
     prefill of the whole sequence would: K/V of the new positions match the
