@@ -130,6 +130,11 @@ hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits,
 // idx / gate [rows][k + ns]: the top-k, then experts E .. E + ns - 1 with gate 1
 hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate, int32_t* idx_dump,
                        float* gate_dump, const int32_t* flag, hipStream_t s);
+// at most 4 rows: router_topk then moe_permute (chunk >= rows) in one launch
+hipError_t router_topk_permute(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate,
+                               int32_t* idx_dump, float* gate_dump, int32_t* counts, int32_t* offsets,
+                               int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
+                               const int32_t* flag, hipStream_t s);
 // k values moe_combine takes
 inline bool combine_k_ok(int k) { return k == 1 || k == 2 || k == 4 || k == 8 || k == 11; }
 // also emits the GEMM work list: int4 {expert, first slot, rows, chunk index << 16 |

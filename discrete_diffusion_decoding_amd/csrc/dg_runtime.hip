@@ -603,10 +603,15 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     }
     {
       ProfScope psr_(m, DG_PROF_ROUTER, st);
-      DG_CK(router_topk(rlp, R, E, k, ns, eidx, egate,
-                        ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr,
-                        ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr, ps.flag, st));
-      DG_CK(moe_permute(eidx, R, kx, Ex, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
+      int32_t* edump = ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr;
+      float* gdump = ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr;
+      if (R <= 4) {   // decoding: one launch
+        DG_CK(router_topk_permute(rlp, R, E, k, ns, eidx, egate, edump, gdump, cnt, off, slot_of, slot_row, items,
+                                  nitems, m->x_rows, ps.flag, st));
+      } else {
+        DG_CK(router_topk(rlp, R, E, k, ns, eidx, egate, edump, gdump, ps.flag, st));
+        DG_CK(moe_permute(eidx, R, kx, Ex, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
+      }
     }
     if (fs && !ns) {
       dg_status sr = shared_ffn();

@@ -506,18 +506,17 @@ hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* i
 // activation row only, and the combine reads the k slots of a row in j
 // order), then goes to slot offsets[e] + p.  p is parked in slot_of[a] (this
 // thread's own write) until the offsets are known.
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int na, int k, int E, int32_t* counts,
-                                                       int32_t* offsets, int32_t* slot_of, int32_t* slot_row,
-                                                       int4* items, int32_t* n_items, int chunk,
-                                                       const int32_t* flag) {
-  if (flag && *flag) return;
+template <int NT>
+__device__ __forceinline__ void permute_body(const int32_t* idx, int na, int k, int E, int32_t* counts,
+                                             int32_t* offsets, int32_t* slot_of, int32_t* slot_row, int4* items,
+                                             int32_t* n_items, int chunk) {
   __shared__ int cnt[256];
   __shared__ int off[257];
   __shared__ int ibase[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < 256) cnt[tid] = 0;
   __syncthreads();
-  for (int a = tid; a < na; a += 1024) slot_of[a] = atomicAdd(&cnt[idx[a]], 1);
+  for (int a = tid; a < na; a += NT) slot_of[a] = atomicAdd(&cnt[idx[a]], 1);
   __syncthreads();
   // exclusive scans over the experts of the row counts and of the item counts:
   // waves 0-3 scan 64 experts each (shuffle scan), then add the wave totals
@@ -558,7 +557,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
     }
   }
   __syncthreads();
-  for (int e = tid; e <= E; e += 1024) {
+  for (int e = tid; e <= E; e += NT) {
     offsets[e] = off[e];
     if (e < E) {
       counts[e] = cnt[e];
@@ -568,12 +567,124 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
         items[i] = make_int4(e, off[e] + r, min(chunk, cnt[e] - r), (c << 16) | nc);
     }
   }
-  for (int a = tid; a < na; a += 1024) {
+  for (int a = tid; a < na; a += NT) {
     const int e = idx[a];
     const int slot = off[e] + slot_of[a];
     slot_of[a] = slot;
     slot_row[slot] = a / k;
   }
+}
+
+__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int na, int k, int E, int32_t* counts,
+                                                       int32_t* offsets, int32_t* slot_of, int32_t* slot_row,
+                                                       int4* items, int32_t* n_items, int chunk,
+                                                       const int32_t* flag) {
+  if (flag && *flag) return;
+  permute_body<1024>(idx, na, k, E, counts, offsets, slot_of, slot_row, items, n_items, chunk);
+}
+
+// Few rows (decoding, at most 4): the top-k of row r (wave r, as topk_kernel)
+// and the expert permutation (as permute_kernel, over the slots in LDS) in one
+// workgroup, one launch instead of two.
+template <int NS, int NK>
+__global__ __launch_bounds__(256) void topk_permute_kernel(Partials rl, int rows, int E, int ns, int32_t* idx,
+                                                           float* gate, int32_t* idx_dump, float* gate_dump,
+                                                           int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                                                           int32_t* slot_row, int4* items, int32_t* n_items,
+                                                           int chunk, const int32_t* flag) {
+  if (flag && *flag) return;
+  __shared__ int32_t sidx[4 * 64];
+  const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int ko = NK + ns;
+  if (r < rows) {
+    uint64_t key[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      key[j] = 0;
+      if (64 * j < E) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+          float h = 0.f, l = 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < NS; ++s2) {
+            h += rl.p[s2 * rl.stride + (long)r * E + e];
+            l += rl.p[s2 * rl.stride + (long)(rows + r) * E + e];
+          }
+          key[j] = topk_key(h + l, e);
+        }
+      }
+    }
+    float mine_v = 0.f, top_v = 0.f;
+    int mine_e = 0;
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      const uint64_t best = wave_umax64(max(max(key[0], key[1]), max(key[2], key[3])));
+      const int e = 0xFFFF - (int)(best & 0xFFFF);
+      const float v = topk_key_value(best);
+      if (t == 0) top_v = v;
+      if (lane == t) {
+        mine_v = v;
+        mine_e = e;
+      }
+      if ((e & 63) == lane) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if ((e >> 6) == j) key[j] = 0;
+      }
+    }
+    float ex = lane < NK ? expf(mine_v - top_v) : 0.f;
+    float den = ex;
+#pragma unroll
+    for (int o = 1; o < NK; o <<= 1) den += __shfl_xor(den, o, 64);
+    if (lane < NK) {
+      const float gt = ex / den;
+      sidx[r * ko + lane] = mine_e;
+      idx[(long)r * ko + lane] = mine_e;
+      gate[(long)r * ko + lane] = gt;
+      if (idx_dump) idx_dump[(long)r * NK + lane] = mine_e;
+      if (gate_dump) gate_dump[(long)r * NK + lane] = gt;
+    } else if (lane < ko) {
+      sidx[r * ko + lane] = E + lane - NK;
+      idx[(long)r * ko + lane] = E + lane - NK;
+      gate[(long)r * ko + lane] = 1.f;
+    }
+  }
+  __syncthreads();
+  permute_body<256>(sidx, rows * ko, ko, E + ns, counts, offsets, slot_of, slot_row, items, n_items, chunk);
+}
+
+hipError_t router_topk_permute(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate,
+                               int32_t* idx_dump, float* gate_dump, int32_t* counts, int32_t* offsets,
+                               int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
+                               const int32_t* flag, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (rows > 4 || E > 256 || k > E || ns < 0 || k + ns > 64 || E + ns > 255 || chunk < 1 || rlog.n < 1 ||
+      rlog.n > 8)
+    return hipErrorInvalidValue;
+#define DG_TP(NS_, NK_)                                                                                       \
+  hipLaunchKernelGGL((topk_permute_kernel<NS_, NK_>), dim3(1), dim3(256), 0, s, rlog, rows, E, ns, idx, gate, \
+                     idx_dump, gate_dump, counts, offsets, slot_of, slot_row, items, n_items, chunk, flag)
+#define DG_TP_NS(NK_)                       \
+  switch (rlog.n) {                         \
+    case 1: DG_TP(1, NK_); break;           \
+    case 2: DG_TP(2, NK_); break;           \
+    case 3: DG_TP(3, NK_); break;           \
+    case 4: DG_TP(4, NK_); break;           \
+    case 5: DG_TP(5, NK_); break;           \
+    case 6: DG_TP(6, NK_); break;           \
+    case 7: DG_TP(7, NK_); break;           \
+    default: DG_TP(8, NK_); break;          \
+  }
+  switch (k) {
+    case 1: DG_TP_NS(1) break;
+    case 2: DG_TP_NS(2) break;
+    case 4: DG_TP_NS(4) break;
+    case 8: DG_TP_NS(8) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DG_TP_NS
+#undef DG_TP
+  return hipGetLastError();
 }
 
 hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* counts, int32_t* offsets,
