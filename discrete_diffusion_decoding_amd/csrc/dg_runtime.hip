@@ -419,7 +419,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
   const int R = ps.rows, D = d.d_model, H = d.n_heads, Hkv = d.n_kv_heads, hd = d.head_dim, E = d.n_experts,
             k = d.top_k, fe = d.d_expert, fs = d.d_shared;
   const int qkvd = (H + 2 * Hkv) * hd;
-  // cache of one layer: K [kv_Bp][Hkv][P_max][hd], then V^T [kv_Bp][Hkv][hd][P_max]
+  // cache of one layer: K [kv_Bp][Hkv][P_max][hd], then V^T [kv_Bp][Hkv][P_max / 32][hd][32]
   const size_t kv_one = (size_t)Hkv * ps.P_max * hd;  // elements of one prefix, K or V
   const size_t layer_kv = (size_t)2 * ps.kv_Bp * kv_one;
   float* h = at<float>(ws, p.h);

@@ -13,7 +13,8 @@
 // combines the splits.
 //
 // Key / value tiles (32 keys) stream through a 4-deep LDS ring by direct
-// global->LDS DMA: K rows [32][hd] and V^T rows [hd][32 keys], 16-byte slots
+// global->LDS DMA: K rows [32][hd] and V^T rows [hd][32 keys] (the V^T caches
+// are stored tile-major, so a tile's V^T is one contiguous block), 16-byte slots
 // XOR-swizzled (K: slot ^ kswz(key), V^T: slot ^ vswz(dim)) so that every 8
 // and every 16 lanes of an MFMA operand read hit distinct banks.
 //
@@ -121,10 +122,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
   }
 
   // ---- DMA sources: every key count is a multiple of 32, so a tile lies in one
-  // source; per-lane element offsets are fixed for the whole loop
-  // (source 2 differs only in the V^T pitch: dsoff holds the difference, kept
-  // as a value so that choosing the source is a select, not an indexed array)
-  int soff[IPW], dsoff[IPW];
+  // source; per-lane element offsets within a tile are fixed for the whole loop
+  int soff[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     if (j < KI) {
@@ -132,12 +131,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
       const int key = (wave + NW * j) * KPI + lane / CK;
       const int c = (lane % CK) ^ kswz(key, CK);
       soff[j] = key * HD + c * 8;
-      dsoff[j] = 0;
     } else {
+      // a V^T tile is a contiguous [HD][32] block: one instruction moves 16 whole rows (1 KB)
       const int row = (wave + NW * (j - KI)) * 16 + (lane >> 2);
       const int c = (lane & 3) ^ vswz(row);
-      soff[j] = row * (int)a.v1_pitch + c * 8;    // < 2^31: pitches are key capacities
-      dsoff[j] = row * (int)(a.v2_pitch - a.v1_pitch);
+      soff[j] = row * 32 + c * 8;
     }
   }
 #define DG_AISSUE(S, KT)                                                                           \
@@ -145,9 +143,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     const int kt_ = (KT);                                                                          \
     const bool one_ = kt_ < n1;                                                                    \
     const bf16_t* kb_ = one_ ? K1 + (long)kt_ * HD : K2 + (long)(kt_ - n1) * HD;                   \
-    const bf16_t* vb_ = one_ ? V1 + kt_ : V2 + (kt_ - n1);                                         \
+    const bf16_t* vb_ = one_ ? V1 + (long)(kt_ >> 5) * (32 * HD) : V2 + (long)((kt_ - n1) >> 5) * (32 * HD); \
     _Pragma("unroll") for (int j = 0; j < IPW; ++j) {                                              \
-      const bf16_t* src_ = (j < KI ? kb_ : vb_) + (soff[j] + (one_ ? 0 : dsoff[j]));              \
+      const bf16_t* src_ = (j < KI ? kb_ : vb_) + soff[j];                                         \
       const int dst_ = (j < KI ? (wave + NW * j) : 32 * HD / 512 + (wave + NW * (j - KI))) * 512;  \
       __builtin_amdgcn_global_load_lds((const void*)src_, (lds_void_t*)&S[dst_], 16, 0, 0);        \
     }                                                                                              \
@@ -374,8 +372,8 @@ static void attn_shape(const AttnArgs& a, hipStream_t s) {
 //           the LPK lanes by shuffles (bf16 pair products in fp32, dot2);
 //   softmax: wave q takes query row q over the split's keys in LDS (max in
 //           log2 units, exp2, sum), as the MFMA kernel's (m, l);
-//   P V:    8 lanes per V^T row read 64 consecutive keys (128 bytes), summed
-//           over the 8 lanes.
+//   P V:    8 lanes per V^T row read 64 consecutive keys (two 64-byte runs of
+//           the tile-major cache), summed over the 8 lanes.
 // Outputs match the MFMA kernel's: normalised O per split plus (m, l), merged
 // by attention_merge, or the final O for one split.
 constexpr int kDecThreads = 512;
@@ -422,7 +420,7 @@ __global__ __launch_bounds__(kDecThreads) void attn_decode_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int k0 = kbeg + 64 * c + 8 * vpart;
-      if (k0 < kend) vv[dp][c] = load_bf16x8(V1 + (long)(64 * dp + vrow) * a.v1_pitch + k0);
+      if (k0 < kend) vv[dp][c] = load_bf16x8(V1 + (long)(k0 >> 5) * (32 * HD) + (64 * dp + vrow) * 32 + (k0 & 31));
     }
   // query rows q = r GQ + j (head g GQ + j, row r) into LDS
   for (int i = tid; i < NQ * (HD / 8); i += kDecThreads) {

@@ -237,8 +237,10 @@ __device__ __forceinline__ void qk_rope_head(const QkRopeArgs& a, int r, int hh)
 
 // V^T scatter: a workgroup moves 32 positions x 64 dims of one kv head through
 // LDS (one 16-byte load per thread), then each thread writes 8 positions of
-// one dim as a 16-byte store, so every V^T row gets one 64-byte run.  The LDS
-// row pitch of 66 values staggers the banks of the 8-row steps read together.
+// one dim as a 16-byte store.  The V^T caches are tile-major: position p of
+// dim d sits at ((p / 32) hd + d) 32 + p % 32, so a 32-key tile is one
+// contiguous block.  The LDS row pitch of 66 values staggers the banks of the
+// 8-row steps read together.
 constexpr int kVtPitch = 66;
 template <int HD>
 __device__ __forceinline__ void vt_scatter_block(const QkRopeArgs& a, int g, int t0, int d0, bf16_t* tile) {
@@ -255,15 +257,17 @@ __device__ __forceinline__ void vt_scatter_block(const QkRopeArgs& a, int g, int
   const int bidx = t0 / a.per_batch, p0 = (a.pos_dev ? *a.pos_dev : a.t_offset) + t0 % a.per_batch;
   const int dim = tid >> 2, pg = (tid & 3) * 8;
   const int nval = min(32, a.rows - t0);
-  bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (long)(d0 + dim) * a.v_pitch + p0 + pg;
+  bf16_t* vt = a.vtdst + bidx * a.v_bstride + g * a.v_hstride + (long)(d0 + dim) * 32;
   uint16_t v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = tile[(pg + i) * kVtPitch + dim];
-  if (pg + 8 <= nval && ((a.v_pitch | p0) & 7) == 0) {
-    *reinterpret_cast<uint4*>(vt) = make_uint4((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
-                                               (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16));
+  const int p = p0 + pg;
+  if (pg + 8 <= nval && (p0 & 7) == 0) {   // 8 positions inside one tile
+    *reinterpret_cast<uint4*>(vt + (long)(p >> 5) * (32 * HD) + (p & 31)) =
+        make_uint4((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16),
+                   (uint32_t)v[4] | ((uint32_t)v[5] << 16), (uint32_t)v[6] | ((uint32_t)v[7] << 16));
   } else {
-    for (int i = 0; i < 8 && pg + i < nval; ++i) vt[i] = v[i];
+    for (int i = 0; i < 8 && pg + i < nval; ++i) vt[(long)((p + i) >> 5) * (32 * HD) + ((p + i) & 31)] = v[i];
   }
 }
 

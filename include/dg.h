@@ -164,7 +164,9 @@ void dg_model_destroy(dg_model* m);
 dg_status dg_set_graphs(dg_model* m, int32_t enable);
 
 /* Bytes of the key/value cache for Bp prefixes of capacity P_max:
- * per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][hd][P_max], bf16. */
+ * per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][P_max / 32][hd][32] (tile-major:
+ * position p of dim d at ((p / 32) hd + d) 32 + p % 32, each 32-key tile one contiguous
+ * block), bf16. */
 size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max);
 
 /* Workspace bytes for passes over up to `rows` token rows attending up to

@@ -24,14 +24,16 @@ def host(t):
 
 def kv_layer(kv, m, Bp, P_max, l, bp, P):
     """(K, V) of prefix bp at layer l as float64 [P][Hkv][hd]; the cache holds
-    per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][hd][P_max]."""
+    per layer K [Bp][Hkv][P_max][hd] then V^T [Bp][Hkv][P_max / 32][hd][32]
+    (tile-major)."""
     from discrete_diffusion_decoding_amd import synth
     n = Bp * m.n_kv_heads * P_max * m.head_dim
     x = kv.view(torch.int16)[2 * n * l: 2 * n * (l + 1)]
     K = x[:n].view(Bp, m.n_kv_heads, P_max, m.head_dim)[bp, :, :P, :]
-    Vt = x[n:].view(Bp, m.n_kv_heads, m.head_dim, P_max)[bp, :, :, :P]
+    Vt = x[n:].view(Bp, m.n_kv_heads, P_max // 32, m.head_dim, 32)[bp]
+    Vt = Vt.permute(1, 3, 0, 2).reshape(P_max, m.n_kv_heads, m.head_dim)[:P]
     K = synth.bf16_bits_to_f32(K.permute(1, 0, 2).contiguous().cpu().numpy().view(np.uint16))
-    V = synth.bf16_bits_to_f32(Vt.permute(2, 0, 1).contiguous().cpu().numpy().view(np.uint16))
+    V = synth.bf16_bits_to_f32(Vt.contiguous().cpu().numpy().view(np.uint16))
     return K.astype(np.float64), V.astype(np.float64)
 
 

@@ -153,7 +153,7 @@ def test_layer_step_matches_oracle(name):
     Hkv, hd = m.n_kv_heads, m.head_dim
     kvb = synth.bf16_bits_to_f32(kvh.view(np.uint16)).reshape(2, Hkv, -1)
     K = kvb[0].reshape(Hkv, P, hd).transpose(1, 0, 2)
-    Vt = kvb[1].reshape(Hkv, hd, P).transpose(2, 0, 1)
+    Vt = kvb[1].reshape(Hkv, P // 32, hd, 32).transpose(1, 3, 0, 2).reshape(P, Hkv, hd)   # tile-major V^T
     assert rel_l2(K, kv_o[0][0]) <= 1e-2
     assert rel_l2(Vt, kv_o[0][1]) <= 1e-2
     assert np.array_equal(hdump[0], hc)
