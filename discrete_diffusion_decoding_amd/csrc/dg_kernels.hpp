@@ -92,7 +92,7 @@ struct QkRopeArgs {
   bf16_t* q;                        // [rows][H][hd]
   int per_batch, pos0;              // position of row r = pos0 + (r % per_batch)
   bf16_t* kdst; long k_bstride, k_hstride;            // K rows [.][Hkv][pitch][hd]
-  bf16_t* vtdst; long v_bstride, v_hstride, v_pitch;  // V^T [.][Hkv][hd][pitch]
+  bf16_t* vtdst; long v_bstride, v_hstride;  // V^T [.][Hkv][positions / 32][hd][32] (tile-major)
   int t_offset;                     // index of row 0 within the destination sequence
   const int32_t* pos_dev;           // if set: t_offset read from the device
   const int32_t* flag;
@@ -106,8 +106,9 @@ struct AttnArgs {
   const bf16_t* q; int H, Hkv, hd; float scale;
   int rows_per_batch; int B;
   // key source 1 (cache) and 2 (canvas); batch b reads source-1 element b1 = (nb1 == 1 ? 0 : b)
-  const bf16_t* k1; const bf16_t* vt1; long k1_bstride, k1_hstride, v1_bstride, v1_hstride, v1_pitch; int n1; int nb1;
-  const bf16_t* k2; const bf16_t* vt2; long k2_bstride, k2_hstride, v2_bstride, v2_hstride, v2_pitch; int n2;
+  // (V^T tile-major: [keys / 32][hd][32] from each head's base)
+  const bf16_t* k1; const bf16_t* vt1; long k1_bstride, k1_hstride, v1_bstride, v1_hstride; int n1; int nb1;
+  const bf16_t* k2; const bf16_t* vt2; long k2_bstride, k2_hstride, v2_bstride, v2_hstride; int n2;
   int causal; int qpos0;            // causal: query row r (within batch) sits at qpos0 + r
   int splits; int split_len;        // key splits (split_len multiple of 32)
   const int32_t* pos_dev;           // causal pass (n2 = 0) whose first query position is read from the

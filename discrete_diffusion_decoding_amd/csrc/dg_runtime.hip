@@ -488,12 +488,12 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       a.per_batch = ps.per_batch; a.pos0 = ps.pos0; a.flag = ps.flag; a.rope = at<float2>(ws, p.rope);
       if (ps.prefill) {
         a.kdst = const_cast<bf16_t*>(Kc); a.k_bstride = 0; a.k_hstride = (long)ps.P_max * hd;
-        a.vtdst = const_cast<bf16_t*>(Vc); a.v_bstride = 0; a.v_hstride = (long)hd * ps.P_max; a.v_pitch = ps.P_max;
+        a.vtdst = const_cast<bf16_t*>(Vc); a.v_bstride = 0; a.v_hstride = (long)hd * ps.P_max;
         a.t_offset = ps.q0; a.pos_dev = ps.pos_dev;
       } else {
         const int T = ps.per_batch;
         a.kdst = at<bf16_t>(ws, p.kc); a.k_bstride = (long)Hkv * T * hd; a.k_hstride = (long)T * hd;
-        a.vtdst = at<bf16_t>(ws, p.vc); a.v_bstride = (long)Hkv * hd * T; a.v_hstride = (long)hd * T; a.v_pitch = T;
+        a.vtdst = at<bf16_t>(ws, p.vc); a.v_bstride = (long)Hkv * hd * T; a.v_hstride = (long)hd * T;
         a.t_offset = 0;
       }
       ProfScope ps_(m, DG_PROF_OTHER, st);
@@ -511,21 +511,21 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
         a.k1 = Kc; a.vt1 = Vc; a.k1_bstride = 0; a.k1_hstride = (long)ps.P_max * hd;
         // keys up to the last row's position, in whole 32-key tiles: the causal
         // mask hides the tail, so a pass may start and end anywhere
-        a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max;
+        a.v1_bstride = 0; a.v1_hstride = (long)hd * ps.P_max;
         a.n1 = cdiv(ps.q0 + R, 32) * 32; a.nb1 = 1;
         a.n2 = 0; a.causal = 1; a.qpos0 = ps.q0; a.pos_dev = ps.pos_dev;
       } else {
         const int T = ps.per_batch;
         if (ps.P > 0) {
           a.k1 = Kc; a.vt1 = Vc; a.k1_bstride = (long)Hkv * ps.P_max * hd; a.k1_hstride = (long)ps.P_max * hd;
-          a.v1_bstride = (long)Hkv * hd * ps.P_max; a.v1_hstride = (long)hd * ps.P_max; a.v1_pitch = ps.P_max;
+          a.v1_bstride = (long)Hkv * hd * ps.P_max; a.v1_hstride = (long)hd * ps.P_max;
         } else {
           a.k1 = at<bf16_t>(ws, p.kc); a.vt1 = at<bf16_t>(ws, p.vc);
         }
         a.n1 = ps.P; a.nb1 = ps.Bp;
         a.k2 = at<bf16_t>(ws, p.kc); a.vt2 = at<bf16_t>(ws, p.vc);
         a.k2_bstride = (long)Hkv * T * hd; a.k2_hstride = (long)T * hd;
-        a.v2_bstride = (long)Hkv * hd * T; a.v2_hstride = (long)hd * T; a.v2_pitch = T; a.n2 = T;
+        a.v2_bstride = (long)Hkv * hd * T; a.v2_hstride = (long)hd * T; a.n2 = T;
         a.causal = 0; a.qpos0 = ps.P;
       }
       ProfScope ps_(m, DG_PROF_ATTN, st);

@@ -9,6 +9,8 @@
 // slot counts are template parameters, so the loops fully unroll).
 #include <math.h>
 
+#include <algorithm>
+
 #include "dg_kernels.hpp"
 
 namespace dg {
@@ -305,17 +307,20 @@ hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of key-split attention partials (scores kept in log2 units): per row,
-// the split weights 2^(m_s - M) / L of every head are formed once in LDS, then
-// each thread sums its float4 columns over the splits.
+// Merge of key-split attention partials (scores kept in log2 units): block
+// (r, y) takes heads y hpb .. y hpb + hpb - 1 of row r; the split weights
+// 2^(m_s - M) / L of its heads are formed once in LDS, then each thread sums
+// its float4 columns over the splits.  Few rows (decoding) take 1024 / hd heads
+// per block, so that a thread makes one pass; many rows take every head.
 template <int NSP>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16_t* op, const float* ml, int rows, int H, int hd,
-                                                         bf16_t* out, const int32_t* flag) {
+                                                         int hpb, bf16_t* out, const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ float wts[64 * NSP];
   const int r = blockIdx.x;
+  const int h0 = blockIdx.y * hpb, h1 = min(H, h0 + hpb);
   const long srow = (long)rows * H;
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+  for (int h = h0 + threadIdx.x; h < h1; h += blockDim.x) {
     const long base = (long)r * H + h;
     float mv[NSP], lv[NSP];
     float M = -INFINITY;
@@ -339,8 +344,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16_t* op, const
   __syncthreads();
   const long rowoff = (long)r * H * hd;
   const long sstride = srow * hd;
-  const int n4 = H * hd / 4;
-  for (int i4 = threadIdx.x; i4 < n4; i4 += blockDim.x) {
+  const int n4 = h1 * hd / 4;
+  for (int i4 = h0 * hd / 4 + threadIdx.x; i4 < n4; i4 += blockDim.x) {
     const int h = (4 * i4) / hd;
     float4 vals[NSP];
 #pragma unroll
@@ -356,9 +361,11 @@ hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits,
                            bf16_t* out, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (H > 64 || hd % 4) return hipErrorInvalidValue;
+  const int hpb = rows < 64 ? std::max(1, 1024 / hd) : H;
+  const dim3 grid(rows, (H + hpb - 1) / hpb);
 #define DG_MERGE_CASE(N)                                                                               \
   case N:                                                                                              \
-    hipLaunchKernelGGL(attn_merge_kernel<N>, dim3(rows), dim3(256), 0, s, opart, mlpart, rows, H, hd, out, flag); \
+    hipLaunchKernelGGL(attn_merge_kernel<N>, grid, dim3(256), 0, s, opart, mlpart, rows, H, hd, hpb, out, flag); \
     break;
   switch (splits) {
     DG_MERGE_CASE(1) DG_MERGE_CASE(2) DG_MERGE_CASE(3) DG_MERGE_CASE(4) DG_MERGE_CASE(5) DG_MERGE_CASE(6)
