@@ -84,6 +84,10 @@ class Workload:
 TINY = ModelShape(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64,
                   n_experts=8, top_k=2, d_expert=512, d_shared=0, vocab=2048, self_cond=0)
 
+# the tiny model with a shared FFN two expert widths wide: decoding runs it as
+# two extra experts of the grouped products
+TINY_SHARED = dataclasses.replace(TINY, d_shared=1024)
+
 FULL_LAYER = ModelShape(n_layers=1, d_model=2816, n_heads=16, n_kv_heads=8, head_dim=256,
                         n_experts=128, top_k=8, d_expert=704, d_shared=2112, vocab=0,
                         self_cond=0)

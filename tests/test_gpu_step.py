@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from discrete_diffusion_decoding_amd import dg, synth
-from discrete_diffusion_decoding_amd.configs import WORKLOADS, SamplerParams
+from discrete_diffusion_decoding_amd.configs import TINY, TINY_SHARED, WORKLOADS, SamplerParams
 from discrete_diffusion_decoding_amd.device import DeviceModel
 from oracle import model as om
 from oracle import sampler as osmp
@@ -292,16 +292,19 @@ def test_block_append_extends_prefix_cache():
     dm.close()
 
 
-def test_ar_decode_matches_oracle():
+@pytest.mark.parametrize("shape", [TINY, TINY_SHARED], ids=["tiny", "tiny_shared"])
+def test_ar_decode_matches_oracle(shape):
     """Autoregressive steps (dg_ar_step) after a 64-token prompt, at positions
     64..69 (one row, unaligned): every step's logits and the K/V it writes at
     its position in every layer match the oracle's one-token decode; on the
     GPU's own logits the sampled token, argmax and entropy are the oracle
     sampler's (token and argmax bit-exact); against the oracle's logits the
     token is exact wherever the winning gap exceeds what the logit error
-    allows.  Each step decodes the GPU's previous token (teacher forcing)."""
+    allows.  Each step decodes the GPU's previous token (teacher forcing).
+    tiny_shared adds a shared FFN, which decoding runs as two extra experts of
+    the grouped products."""
     wl = WORKLOADS["tiny_step"]
-    m = wl.model
+    m = shape
     P0, n, P_max, tau = wl.prefix_len, 6, 96, 0.8
     announce(f"ar decode: upload, prefill {P0}")
     dm = DeviceModel(m, SEED)
