@@ -320,18 +320,20 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
   p.xn2 = take(R * D * 2);
   p.xr = take(2 * R * D * 2);
   p.rlog = take((size_t)kMaxRouterSplit * 2 * R * E * 4);
-  // expert slots per row: top-k, plus the shared FFN's blocks when they run as experts
-  const size_t ns = shared_as_experts(d, rows), Ex = E + ns, kx = k + ns;
-  p.eidx = take(R * kx * 4);
-  p.egate = take(R * kx * 4);
+  // expert slots: top-k per row, plus the shared FFN's blocks in passes of at
+  // most kGemvRows rows (any pass this workspace serves may be one)
+  const size_t ns = shared_as_experts(d, 1), Ex = E + ns;
+  const size_t slots = std::max(R * k, std::min(R, (size_t)kGemvRows) * (k + ns));
+  p.eidx = take(slots * 4);
+  p.egate = take(slots * 4);
   p.cnt = take((Ex + 1) * 4);
   p.off = take((Ex + 1) * 4);
-  p.slot_of = take(R * kx * 4);
-  p.slot_row = take(R * kx * 4);
-  p.items = take((Ex + (R * kx + 31) / 32) * 16);   // work list for chunks of >= 32 rows
+  p.slot_of = take(slots * 4);
+  p.slot_row = take(slots * 4);
+  p.items = take((Ex + (slots + 31) / 32) * 16);   // work list for chunks of >= 32 rows
   p.nitems = take(16);
-  p.hbuf = take(R * kx * d.d_expert * 2);
-  p.ybuf = take(R * kx * D * 2);
+  p.hbuf = take(slots * d.d_expert * 2);
+  p.ybuf = take(slots * D * 2);
   p.hs = take(R * std::max(d.d_shared, 1) * 2);
   p.ys = take(d.d_shared ? (size_t)kMaxDenseSplit * R * D * 4 : 0);
   if (V) {
