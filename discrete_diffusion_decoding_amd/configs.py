@@ -88,6 +88,10 @@ TINY = ModelShape(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64,
 # two extra experts of the grouped products
 TINY_SHARED = dataclasses.replace(TINY, d_shared=1024)
 
+# the tiny model with the gated self-conditioning projection (the block tests
+# follow the soft-prediction state from step to step)
+TINY_SELF_COND = dataclasses.replace(TINY, self_cond=1)
+
 FULL_LAYER = ModelShape(n_layers=1, d_model=2816, n_heads=16, n_kv_heads=8, head_dim=256,
                         n_experts=128, top_k=8, d_expert=704, d_shared=2112, vocab=0,
                         self_cond=0)

@@ -161,6 +161,7 @@ struct SampleArgs {
   float* rowstat;                   // [B*T][2]: max, Z (softmax of the logits)
   int32_t* tokens; uint8_t* locked; float* entropy; int32_t* xhat; int32_t* argmax;
   int32_t* stopped; int32_t* steps; int32_t* all_stopped;
+  int32_t* live;                    // [B] (optional): 1 if the row ran this step (not stopped on entry)
   const int32_t* flag;
 };
 // autoregressive next-token sample: B rows of V logits (row pitch ldl), one
@@ -177,10 +178,12 @@ struct ArSampleArgs {
 hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s);
 hipError_t sample_partial(const SampleArgs& a, hipStream_t s);
 hipError_t sample_finish(const SampleArgs& a, hipStream_t s);
+// the soft-prediction embedding of the rows that ran this step (live[r / T] != 0);
+// rows of a canvas that had stopped before the step are left as they are
 hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,
-                         const int32_t* flag, hipStream_t s);
+                         const int32_t* live, int T, const int32_t* flag, hipStream_t s);
 hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out,
-                             const int32_t* stopped, int T, const int32_t* flag, hipStream_t s);
+                             const int32_t* live, int T, const int32_t* flag, hipStream_t s);
 hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* seeds, hipStream_t s);
 hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
 hipError_t fill_u16(uint16_t* p, uint16_t v, long n, hipStream_t s);

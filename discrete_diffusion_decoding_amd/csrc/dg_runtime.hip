@@ -211,7 +211,7 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // workspace plan
 struct Plan {
   size_t h, xn, qkv, q, kc, vc, rope, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
-      nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, P, separt, flag, pos, total;
+      nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, live, P, separt, flag, pos, total;
   int splits_max, vsplit, ksplit, kchunk;
 };
 
@@ -341,6 +341,7 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
     p.logits = take(R * V * 4);
     p.spart = take(R * p.vsplit * 8 * 4);
     p.rowstat = take(R * 2 * 4);
+    p.live = take(64 * 4);   // one flag per canvas (B <= 16)
     if (d.self_cond) {
       soft_split(d, rows, &p.ksplit, &p.kchunk);
       p.P = take(R * V * 2);
@@ -946,6 +947,8 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   float* rowstat = at<float>(ws, p.rowstat);
   SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, rowstat,
                               nullptr, flag);
+  int32_t* live = at<int32_t>(ws, p.live);
+  sa.live = live;
   {
     ProfScope ps_(m, DG_PROF_SAMPLER, st);
     DG_CK(sample_partial(sa, st));
@@ -954,14 +957,13 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   if (d.self_cond) {
     ProfScope ps_(m, DG_PROF_SOFTEMB, st);
     bf16_t* P_ = at<bf16_t>(ws, p.P);
-    DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, flag, st));
+    DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, live, T, flag, st));
     GemmArgs g = gargs();
     g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
     g.k_split = p.ksplit; g.C = at<float>(ws, p.separt); g.ldc = D;
     g.c_kstride = (long)R * D; g.flag = flag;
     DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
-    DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, c->stopped, T, flag,
-                            st));
+    DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, live, T, flag, st));
   }
   (void)all_stopped;
   return DG_OK;

@@ -227,7 +227,9 @@ __global__ __launch_bounds__(1024) void sample_finish_kernel(SampleArgs a) {
   __shared__ float red[16];
   __shared__ int unstable;
   const int b = blockIdx.x;
-  if (a.stopped && a.stopped[b]) return;
+  const bool was_stopped = a.stopped && a.stopped[b];
+  if (a.live && threadIdx.x == 0) a.live[b] = was_stopped ? 0 : 1;
+  if (was_stopped) return;
   const int s = row_step(a, b);
   const uint64_t seed = a.seeds[b];
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
@@ -391,9 +393,10 @@ hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void probs_kernel(const float* logits, const float* rowstat, int V, long ldl,
-                                                    bf16_t* P, const int32_t* flag) {
+                                                    bf16_t* P, const int32_t* live, int T, const int32_t* flag) {
   if (flag && *flag) return;
   const int r = blockIdx.y;
+  if (live && !live[r / T]) return;   // rowstat of a row that did not run is stale
   const float m = rowstat[r * 2], iz = 1.0f / rowstat[r * 2 + 1];
   const long v = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (v >= V) return;
@@ -405,30 +408,32 @@ __global__ __launch_bounds__(256) void probs_kernel(const float* logits, const f
 }
 
 hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,
-                         const int32_t* flag, hipStream_t s) {
-  if (V % 4 != 0 || ldl % 4 != 0) return hipErrorInvalidValue;
+                         const int32_t* live, int T, const int32_t* flag, hipStream_t s) {
+  if (V % 4 != 0 || ldl % 4 != 0 || T < 1) return hipErrorInvalidValue;
   dim3 grid((unsigned)((V / 4 + 255) / 256), rows);
-  hipLaunchKernelGGL(probs_kernel, grid, dim3(256), 0, s, logits, rowstat, V, ldl, P, flag);
+  hipLaunchKernelGGL(probs_kernel, grid, dim3(256), 0, s, logits, rowstat, V, ldl, P, live, T, flag);
   return hipGetLastError();
 }
 
 __global__ __launch_bounds__(256) void reduce_soft_kernel(const float* part, int ksplit, int rows, int d,
-                                                          bf16_t* out, const int32_t* flag) {
+                                                          bf16_t* out, const int32_t* live, int T,
+                                                          const int32_t* flag) {
   if (flag && *flag) return;
   const long n = (long)rows * d;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
+  if (live && !live[(i / d) / T]) return;   // a canvas stopped before this step keeps its state
   float acc = 0.f;
   for (int k = 0; k < ksplit; ++k) acc += part[k * n + i];
   out[i] = f2bf(acc);
 }
 
-hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out, const int32_t* stopped,
+hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out, const int32_t* live,
                              int T, const int32_t* flag, hipStream_t s) {
-  (void)stopped; (void)T;
+  if (T < 1) return hipErrorInvalidValue;
   const long n = (long)rows * d;
   hipLaunchKernelGGL(reduce_soft_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, ksplit, rows, d,
-                     out, flag);
+                     out, live, T, flag);
   return hipGetLastError();
 }
 

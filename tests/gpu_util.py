@@ -77,3 +77,89 @@ def check_experts(gpu_idx, gpu_gate, orc_idx, orc_gate, orc_logits, k, margin_to
             assert abs(gv - og[e]) <= gate_tol + gate_rtol * og[e], (r, e, gv, og[e])
         assert abs(float(np.sum(gpu_gate[r])) - 1.0) < 1e-5
     return excused
+
+
+class ScaledFinalNorm:
+    """A weight provider whose final RMSNorm weight is `alpha` instead of 1:
+    the logits scale by alpha, so the entropy falls and positions lock and
+    canvases stop within a few steps (the random model's logits have std ~0.3
+    at alpha 1, far from any lock).  Both the GPU model and the oracle read
+    the same provider."""
+
+    def __init__(self, base, alpha: float):
+        from discrete_diffusion_decoding_amd import synth
+        self.base, self.m = base, base.m
+        self._fn = synth.f32_to_bf16_bits(np.full(base.m.d_model, alpha, np.float32))
+
+    def glob(self):
+        g = dict(self.base.glob())
+        g["final_norm"] = self._fn
+        return g
+
+    def layer(self, l):
+        return self.base.layer(l)
+
+
+def lock_margin(H, rule: int, thresh: float):
+    """Distance of each position's lock decision from its threshold: |H_i - t|
+    for rule 0; for rule 1 (positions sorted by (H, index), locked while the
+    running sum stays <= t) the distance of the running sum at the position's
+    rank."""
+    H = np.asarray(H, dtype=np.float64)
+    if rule == 0:
+        return np.abs(H - thresh)
+    order = np.lexsort((np.arange(H.size), H))
+    cum = np.empty(H.size)
+    cum[order] = np.cumsum(H[order])
+    return np.abs(cum - thresh)
+
+
+
+def moe_given_experts(shape, xn2, lw, idx):
+    """The oracle's MoE output with the expert ids fixed to idx [n][k]: gates
+    are the softmax of the oracle's router logits at those ids (for rows where
+    the GPU's choice differs from the oracle's inside the near-tie margin)."""
+    from oracle import model as om
+    bits = lw["_bits"]
+    logits = xn2 @ lw["w_router"].T
+    gates = om.softmax(np.take_along_axis(logits, idx, axis=1), axis=-1)
+    y = np.zeros_like(xn2)
+    for r in range(xn2.shape[0]):
+        for j in range(idx.shape[1]):
+            e = int(idx[r, j])
+            y[r] += gates[r, j] * om.gated_ffn(xn2[r:r + 1], om.widen(bits["w_gate"][e]),
+                                               om.widen(bits["w_up"][e]), om.widen(bits["w_down"][e]))[0]
+    if shape.d_shared:
+        y += om.gated_ffn(xn2, lw["w_gate_sh"], lw["w_up_sh"], lw["w_down_sh"])
+    return y
+
+
+def layer_teacher_forced(M, lw, h_in, kp, vp, P, g_idx, g_gate, margin_tol=1e-3, gate_tol=2e-3):
+    """Layer output of one canvas [T, d] recomputed by the oracle from the GPU's
+    layer input h_in and the GPU's prefix cache (kp, vp) of that layer.
+    Expert sets must match the GPU's (g_idx, g_gate) except where the oracle's
+    k-th / (k+1)-th router-logit margin is below margin_tol; there the oracle
+    adopts the GPU's experts.  Returns (output, excused row count)."""
+    from oracle import model as om
+    m = M.m
+    T = h_in.shape[0]
+    q, k, v = M.qkv(h_in, lw, P + np.arange(T))
+    o = om.attention(q, np.concatenate([kp, k]), np.concatenate([vp, v]), np.ones((T, P + T), dtype=bool))
+    h_out, info = M.post_attention(h_in, o, lw)
+    excused = []
+    margin = topk_margin(info["router_logits"], m.top_k)
+    for r in range(T):
+        gs, os_ = set(g_idx[r].tolist()), set(info["experts"][r].tolist())
+        if gs != os_:
+            assert margin[r] < margin_tol, (r, sorted(gs ^ os_), float(margin[r]))
+            excused.append(r)
+            continue
+        og = dict(zip(info["experts"][r].tolist(), info["gates"][r].tolist()))
+        for e, gv in zip(g_idx[r].tolist(), g_gate[r].tolist()):
+            assert abs(gv - og[e]) <= gate_tol, (r, e, gv, og[e])
+    if excused:
+        ex = np.array(excused)
+        h_att = h_in[ex] + o[ex].reshape(len(ex), -1) @ lw["w_o"].T
+        xn2 = om.rms_norm(h_att, lw["ffn_norm"], m.rms_eps)
+        h_out[ex] = h_att + moe_given_experts(m, xn2, lw, np.asarray(g_idx[ex], dtype=np.int64))
+    return h_out, len(excused)

@@ -1,19 +1,34 @@
 """Parity at the full model sizes, in the launch configuration bench.py times
-(hipGraph replay on a non-default stream): the 30-layer full_step, the 48-step
-full_block and the long_block case (4 canvases over one 32768-token prefix).
+(hipGraph replay on a non-default stream):
+* full_step: the 30-layer model, steps 0 and 1 (step 1 consumes step 0's
+  self-conditioning), one canvas over a 2048-token prompt;
+* full_block: dg_generate_block over the 48-step budget; the same block run
+  step by step must end in the same state bit for bit, and that run is checked
+  at steps 0, 1 and 47;
+* long_block: 4 canvases over one shared 32768-token prompt, steps 0 and 1,
+  and a 48-step dg_generate_block against the step-by-step run.
 
-The oracle cannot run a 25B-parameter step in seconds, so every check samples
-what the oracle can recompute one piece at a time:
-* layer outputs of sampled canvas rows, teacher-forced: the oracle takes the
-  GPU's layer input (all rows, for the canvas keys and values) and the GPU's
-  prefix KV cache of that layer, and recomputes the layer for the sampled rows
-  (hidden state, expert choice, gates);
-* the prefix KV of layer 0 at sampled positions, from the prefix embeddings;
-* logits of sampled rows from the GPU's final hidden state;
-* the sampler on the GPU's own fp32 logits at every position (Gumbel-max
-  sample bit-exact; entropy; lock mask; re-randomised tokens; stop);
-* the self-conditioning state of sampled rows and the next step's input.
-Tolerances are those of test_gpu_step.py."""
+The oracle cannot run a 25B-parameter step in seconds, so every check is
+teacher-forced, one layer at a time, from what the GPU wrote:
+* canvas rows: the oracle takes the GPU's input of layer l (all rows of the
+  canvas, for the canvas keys and values) and the GPU's prefix cache of layer
+  l, and recomputes the layer.  full_step: every row of every layer at both
+  steps; full_block step 47: every row; full_block steps 0 and 1: 64 rows;
+  long_block: 32 rows per canvas.  The layer output (the hidden state) is held
+  to relative L2 <= 1e-2; expert sets must be identical except where the
+  oracle's 8th/9th router-logit margin is below 1e-3 (there the oracle adopts
+  the GPU's choice); gates within 2e-3.  The layer's own contribution
+  (output - input) is reported beside it;
+* the prompt cache: at 64 positions of each prompt, every layer's K and V,
+  computed as a causal step of that position against the GPU's cache of the
+  positions before it (a position whose routing is a near tie in some layer
+  is not followed past it);
+* logits from the GPU's final hidden state;
+* the sampler on the GPU's own fp32 logits at every position: the Gumbel-max
+  sample and argmax bit-exact; entropy; lock mask; re-randomised tokens; stop;
+* the self-conditioning state: the GPU's s_next against softmax(l) E.
+
+Each test checks a group of layers, so no single test runs for long."""
 import numpy as np
 import pytest
 import torch
@@ -23,259 +38,373 @@ from discrete_diffusion_decoding_amd.configs import WORKLOADS, SamplerParams
 from discrete_diffusion_decoding_amd.device import DeviceModel
 from oracle import model as om
 from oracle import sampler as osmp
-from tests.gpu_util import announce, check_experts, dev, host, kv_layer, rel_l2
+from tests.gpu_util import announce, dev, host, kv_layer, rel_l2, topk_margin
 
 pytestmark = pytest.mark.gpu
 SEED = 2024
 FULL = WORKLOADS["full_step"].model
-CHECK_LAYERS = (0, 1, FULL.n_layers // 2, FULL.n_layers - 1)
-# Router logits (std ~1 in this model) inherit the relative error of the
-# layer's hidden state, held to 1e-2, so each logit may move by up to
-# LOGIT_ERR.  Two experts whose logits the oracle separates by less than twice
-# that may swap (ROUTER_MARGIN), and a softmax gate g over the selected logits
-# may move by up to 2 LOGIT_ERR g (first order: dg_i = g_i (dl_i - sum_j g_j
-# dl_j)).  Deep layers and the 32768-key attention reach that level; the
-# single-layer tests keep the tighter 1e-3 margin and 2e-3 gate bound.
-LOGIT_ERR = 1e-2
-ROUTER_MARGIN = 2 * LOGIT_ERR
-GATE_RTOL = 2 * LOGIT_ERR
+L = FULL.n_layers
+ROUTER_MARGIN = 1e-3
+GATE_TOL = 2e-3
+HIDDEN_TOL = 1e-2
+N_PREFIX_POS = 64
+LAYER_GROUPS = [(0, 6), (6, 12), (12, 18), (18, 24), (24, 30)]
+STATE = ("tokens", "locked", "entropy", "xhat", "argmax", "self_cond", "stopped", "steps")
+
+
+def _bf16(x):
+    return synth.bf16_bits_to_f32(np.asarray(x).view(np.uint16)).astype(np.float64)
+
+
+def _dumps(B, T):
+    R = B * T
+    return {
+        "logits_dump": torch.zeros(B, T, FULL.vocab, dtype=torch.float32, device="cuda"),
+        "hidden_dump": torch.zeros(L + 1, R, FULL.d_model, dtype=torch.float32, device="cuda"),
+        "expert_dump": torch.zeros(L, R, FULL.top_k, dtype=torch.int32, device="cuda"),
+        "gate_dump": torch.zeros(L, R, FULL.top_k, dtype=torch.float32, device="cuda"),
+    }
+
+
+def _run_steps(dm, kv, Bp, P, B, T, seeds, sp, n_steps, dump_steps, stream, name):
+    """dg_denoise_step for steps 0 .. n_steps-1 from dg_init_canvas; returns
+    the final state and a record per dumped step (inputs, outputs, dumps)."""
+    st = dm.canvas_state(B, T)
+    torch.cuda.synchronize()
+    sampler, keep = dg.make_sampler(sp, seeds)
+    dg.dg_init_canvas(dm.handle, dg.make_canvas(st), B, T, seeds, stream=stream)
+    dmp = _dumps(B, T)
+    c_plain, c_dump = dg.make_canvas(st), dg.make_canvas({**st, **dmp})
+    recs = []
+    for s in range(n_steps):
+        if s in dump_steps:
+            stream.synchronize()
+            inp = {k: host(st[k]).copy() for k in STATE}
+            dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, c_dump, s, sampler, ws_of(dm, B, T, P), stream=stream)
+            stream.synchronize()
+            out = {k: host(st[k]).copy() for k in STATE}
+            rec = {"name": f"{name} step {s}", "step": s, "B": B, "T": T, "P": P, "Bp": Bp, "kv": kv,
+                   "seeds": seeds, "sp": sp, "inp": inp, "out": out,
+                   "hidden": host(dmp["hidden_dump"]).copy(), "experts": host(dmp["expert_dump"]).copy(),
+                   "gates": host(dmp["gate_dump"]).copy(), "logits": host(dmp["logits_dump"]).copy()}
+            recs.append(rec)
+            announce(f"{rec['name']}: dumped")
+        else:
+            dg.dg_denoise_step(dm.handle, kv, Bp, P, P, B, T, c_plain, s, sampler, ws_of(dm, B, T, P), stream=stream)
+    stream.synchronize()
+    final = {k: host(st[k]).copy() for k in STATE}
+    del st, dmp
+    return final, recs
+
+
+_WS = {}
+
+
+def ws_of(dm, B, T, P):
+    key = (B * T, P + T)
+    if key not in _WS:
+        _WS.clear()
+        torch.cuda.empty_cache()
+        _WS[key] = dm.workspace(B * T, P + T)
+    return _WS[key]
+
+
+def _block(dm, kv, Bp, P, B, T, seeds, sp, stream):
+    st = dm.canvas_state(B, T)
+    torch.cuda.synchronize()
+    sampler, keep = dg.make_sampler(sp, seeds)
+    dg.dg_init_canvas(dm.handle, dg.make_canvas(st), B, T, seeds, stream=stream)
+    dg.dg_generate_block(dm.handle, kv, Bp, P, P, B, T, dg.make_canvas(st), sampler, ws_of(dm, B, T, P),
+                         poll_every=8, stream=stream)
+    stream.synchronize()
+    return {k: host(st[k]).copy() for k in STATE}
 
 
 @pytest.fixture(scope="module")
-def full():
+def runs():
     announce("full model: generate and upload 25.2B parameters")
     dm = DeviceModel(FULL, SEED)
-    M = om.Model(FULL, synth.SynthWeights(FULL, SEED, cache_layers=True))
-    yield dm, M
+    stream = torch.cuda.Stream()
+    sp = SamplerParams()
+    R = {"cases": [], "prefixes": [], "blocks": [], "dm": dm}
+    rng = np.random.default_rng(7)
+
+    # full_step: steps 0 and 1, every row
+    wl = WORKLOADS["full_step"]
+    B, T, P = wl.batch, wl.canvas_len, wl.prefix_len
+    prefix = synth.tokens(SEED, "prefix", (1, P), FULL.vocab)
+    kv = dm.kv_cache(1, P)
+    announce("full_step: prefill 2048 tokens")
+    pre = dev(prefix)
+    torch.cuda.synchronize()
+    dg.dg_prefill_prefix(dm.handle, pre, 1, P, P, kv, ws_of(dm, B, T, P), stream=stream)
+    _, recs = _run_steps(dm, kv, 1, P, B, T, synth.row_seeds(SEED, B), sp, 2, (0, 1), stream, "full_step")
+    for r in recs:
+        r["rows"] = {0: np.arange(T)}
+    R["cases"] += recs
+    R["prefixes"].append({"name": "full_step prompt", "kv": kv, "Bp": 1, "P": P, "tokens": prefix[0],
+                          "pos": np.sort(rng.choice(P, N_PREFIX_POS, replace=False))})
+
+    # full_block: the block against the step loop; dumps at steps 0, 1, 47
+    wl = WORKLOADS["full_block"]
+    seeds = synth.row_seeds(SEED + 1, B)
+    announce("full_block: dg_generate_block, 48 steps")
+    blk = _block(dm, kv, 1, P, B, T, seeds, sp, stream)
+    announce("full_block: the same block step by step")
+    final, recs = _run_steps(dm, kv, 1, P, B, T, seeds, sp, sp.max_steps, (0, 1, sp.max_steps - 1), stream,
+                             "full_block")
+    R["blocks"].append(("full_block", blk, final, sp.max_steps))
+    for r in recs:
+        r["rows"] = {0: np.arange(T) if r["step"] == sp.max_steps - 1 else np.sort(rng.choice(T, 64, replace=False))}
+    R["cases"] += recs
+
+    # long_block: 4 canvases over one 32768-token prompt
+    wl = WORKLOADS["long_block"]
+    B, T, P = wl.batch, wl.canvas_len, wl.prefix_len
+    lprefix = synth.tokens(SEED, "long_prefix", (1, P), FULL.vocab)
+    lkv = dm.kv_cache(1, P)
+    announce("long_block: prefill 32768 tokens")
+    pre = dev(lprefix)
+    torch.cuda.synchronize()
+    dg.dg_prefill_prefix(dm.handle, pre, 1, P, P, lkv, ws_of(dm, B, T, P), stream=stream)
+    seeds = synth.row_seeds(SEED + 2, B)
+    announce("long_block: dg_generate_block, 48 steps, 4 canvases")
+    blk = _block(dm, lkv, 1, P, B, T, seeds, sp, stream)
+    announce("long_block: the same block step by step")
+    final, recs = _run_steps(dm, lkv, 1, P, B, T, seeds, sp, sp.max_steps, (0, 1), stream, "long_block")
+    R["blocks"].append(("long_block", blk, final, sp.max_steps))
+    for r in recs:
+        r["rows"] = {b: np.sort(rng.choice(T, 32, replace=False)) for b in range(B)}
+    R["cases"] += recs
+    R["prefixes"].append({"name": "long_block prompt", "kv": lkv, "Bp": 1, "P": P, "tokens": lprefix[0],
+                          "pos": np.sort(rng.choice(P, N_PREFIX_POS, replace=False))})
+    _WS.clear()
+
+    announce("oracle weights")
+    R["M"] = om.Model(FULL, synth.SynthWeights(FULL, SEED))
+    R["prefix_state"] = {}
+    yield R
     dm.close()
+    del R
     torch.cuda.empty_cache()
 
 
-def _check_prefix_layer0(M, kv, Bp, P_max, prefix, positions):
-    lw = M.layer_dense(0)
-    for bp in range(Bp):
-        K, V = kv_layer(kv, FULL, Bp, P_max, 0, bp, prefix.shape[1])
-        _, k, v = M.qkv(M.embed(prefix[bp][positions]), lw, positions)
-        assert rel_l2(K[positions], k) <= 1e-2
-        assert rel_l2(V[positions], v) <= 1e-2
+def test_full_block_equals_its_steps(runs):
+    """dg_generate_block (device step index, stop-flag polling, captured
+    graphs) ends in the state of the same steps run one by one; with random
+    weights nothing locks and every block takes the 48-step budget."""
+    for name, blk, final, S in runs["blocks"]:
+        for k in STATE:
+            assert np.array_equal(blk[k], final[k]), (name, k)
+        assert (final["steps"] == S).all() and (final["stopped"] == 1).all(), name
 
 
-def _moe_given_experts(M, xn2, lw, idx):
+@pytest.mark.parametrize("which", ["full_step", "full_block", "long_block"])
+def test_full_sampler_decisions(runs, which):
+    """The sampler of every dumped step on the GPU's own fp32 logits."""
+    for rec in runs["cases"]:
+        if not rec["name"].startswith(which):
+            continue
+        announce(f"{rec['name']}: sampler replay")
+        s, sp, T = rec["step"], rec["sp"], rec["T"]
+        inp, out = rec["inp"], rec["out"]
+        _, inv_tau = osmp.temperature(s, sp.tau_start, sp.tau_end, sp.max_steps)
+        for b in range(rec["B"]):
+            l32 = rec["logits"][b]
+            assert np.isfinite(l32).all()
+            H = osmp.entropy(l32)
+            assert np.all(np.abs(out["entropy"][b] - H) <= 1e-4 + 1e-3 * H), b
+            xhat, _, _ = osmp.gumbel_argmax(l32, inv_tau, rec["seeds"][b], s)
+            assert np.array_equal(out["xhat"][b], xhat), b
+            assert np.array_equal(out["argmax"][b], np.argmax(l32, axis=-1)), b
+            lock = osmp.lock_mask(H, sp.lock_rule, sp.lock_thresh)
+            far = np.abs(H - sp.lock_thresh) > 1e-4
+            assert np.array_equal(out["locked"][b].astype(bool)[far], lock[far]), b
+            stop, meanH = osmp.stop_decision(H, out["argmax"][b], inp["argmax"][b], s > 0, s, sp.max_steps,
+                                             sp.stop_rule, sp.stop_thresh)
+            assert bool(out["stopped"][b]) == stop and out["steps"][b] == s + 1, b
+            if stop:
+                assert np.array_equal(out["tokens"][b], xhat), b
+            else:
+                noise = osmp.rerandomized_tokens(rec["seeds"][b], s, T, FULL.vocab)
+                assert np.array_equal(out["tokens"][b], np.where(out["locked"][b].astype(bool), xhat, noise)), b
+            # the canvas input of the step: embedding + gated self-conditioning
+            rows = rec["rows"][b] if b in rec["rows"] else np.arange(8)
+            s_prev = _bf16(inp["self_cond"][b][rows]) if s > 0 else None
+            h0 = runs["M"].canvas_input(inp["tokens"][b][rows], s_prev)
+            assert rel_l2(rec["hidden"][0][b * T + rows], h0) <= HIDDEN_TOL, b
+            # the next step's self-conditioning state
+            s_next = runs["M"].soft_embedding(l32[rows])
+            assert rel_l2(_bf16(out["self_cond"][b][rows]), s_next) <= HIDDEN_TOL, b
+
+
+def test_full_logits_from_final_hidden(runs):
+    """Final norm and LM head of the sampled rows from the GPU's final hidden state."""
+    M = runs["M"]
+    for rec in runs["cases"]:
+        T = rec["T"]
+        for b, rows in rec["rows"].items():
+            logits = M.head(rec["hidden"][L][b * T + rows].astype(np.float64))
+            err = rel_l2(rec["logits"][b][rows], logits)
+            assert err <= HIDDEN_TOL, (rec["name"], b, err)
+
+
+def _moe_given_experts(xn2, lw, idx):
     """The oracle's MoE output with the expert ids fixed to idx [n][k]: gates
-    are the softmax of the oracle's router logits at those ids (used where the
-    GPU's choice differs from the oracle's inside the near-tie margin)."""
+    are the softmax of the oracle's router logits at those ids (for rows where
+    the GPU's choice differs from the oracle's inside the near-tie margin)."""
     bits = lw["_bits"]
     logits = xn2 @ lw["w_router"].T
-    sel = np.take_along_axis(logits, idx, axis=1)
-    gates = om.softmax(sel, axis=-1)
+    gates = om.softmax(np.take_along_axis(logits, idx, axis=1), axis=-1)
     y = np.zeros_like(xn2)
     for r in range(xn2.shape[0]):
         for j in range(idx.shape[1]):
             e = int(idx[r, j])
-            y[r] += gates[r, j] * om.gated_ffn(xn2[r:r + 1], om.widen(bits["w_gate"][e]),
-                                               om.widen(bits["w_up"][e]), om.widen(bits["w_down"][e]))[0]
+            y[r] += gates[r, j] * om.gated_ffn(xn2[r:r + 1], om.widen(bits["w_gate"][e]), om.widen(bits["w_up"][e]),
+                                               om.widen(bits["w_down"][e]))[0]
     if FULL.d_shared:
         y += om.gated_ffn(xn2, lw["w_gate_sh"], lw["w_up_sh"], lw["w_down_sh"])
     return y
 
 
-def _check_layers(M, got, kv, Bp, P_max, P, T, rows_by_canvas):
-    """Teacher-forced layer outputs for the sampled rows of each canvas.
+def _prefix_state(runs, pf_i, l):
+    """Hidden states (and near-tie skip masks) at the input of layer l for the
+    sampled prompt positions, advancing from the latest layer already done."""
+    st = runs["prefix_state"].setdefault(pf_i, {})
+    if l in st:
+        return st[l]
+    pf = runs["prefixes"][pf_i]
+    M = runs["M"]
+    start = max([k for k in st if k < l], default=None)
+    if start is None:
+        start = 0
+        st[0] = (M.embed(pf["tokens"][pf["pos"]]), np.zeros(len(pf["pos"]), dtype=bool))
+    for ll in range(start, l):
+        lw = M.layer_dense(ll)
+        h, skip = st[ll]
+        o = _prefix_attention(runs, pf, ll, lw, h, skip, check=False)
+        h_next, info = M.post_attention(h, o, lw)
+        st[ll + 1] = (h_next, skip | (topk_margin(info["router_logits"], FULL.top_k) < ROUTER_MARGIN))
+    return st[l]
 
-    The layer's own contribution h_out - h_in is held to rel-L2 <= 2e-2, the
-    bar of the single-layer test (the full model's layer inputs start as
-    embeddings of norm ~1, so the contribution dominates h_out).  Expert sets
-    must agree except inside the near-tie margin, where the oracle adopts the
-    GPU's choice for its recomputation."""
-    hd = got["hidden_dump"]
-    ed, gd = got["expert_dump"], got["gate_dump"]
-    pos = P + np.arange(T)
-    for l in CHECK_LAYERS:
+
+def _prefix_attention(runs, pf, l, lw, h, skip, check=True):
+    """The attention output of the sampled prompt positions at layer l, each a
+    causal step against the GPU's cache of the positions before it; checks
+    the K/V the GPU wrote at those positions (rows not skipped)."""
+    M = runs["M"]
+    pos = pf["pos"]
+    q, k, v = M.qkv(h, lw, pos)
+    K, V = _kv(pf["kv"], pf["Bp"], pf["P"], l, 0)
+    if check:
+        live = ~skip
+        ek = rel_l2(K[pos][live], k[live])
+        ev = rel_l2(V[pos][live], v[live])
+        assert ek <= HIDDEN_TOL and ev <= HIDDEN_TOL, (pf["name"], l, ek, ev)
+    n = int(pos.max())
+    keys = np.concatenate([K[:n], k], axis=0)
+    vals = np.concatenate([V[:n], v], axis=0)
+    allowed = np.zeros((len(pos), n + len(pos)), dtype=bool)
+    allowed[:, :n] = np.arange(n)[None, :] < pos[:, None]
+    allowed[np.arange(len(pos)), n + np.arange(len(pos))] = True
+    return om.attention(q, keys, vals, allowed)
+
+
+_KV = {}
+
+
+def _kv(kv, Bp, P, l, bp):
+    """(K, V) of layer l as float64, cached for the current layer."""
+    key = (kv.data_ptr(), bp)
+    if _KV.get("layer") != l:
+        _KV.clear()
+        _KV["layer"] = l
+    if key not in _KV:
+        _KV[key] = kv_layer(kv, FULL, Bp, P, l, bp, P)
+    return _KV[key]
+
+
+def _canvas_layer_pieces(runs, rec, l, lw):
+    """(record, canvas, rows, h_in, o) for the rows checked at layer l."""
+    M = runs["M"]
+    T, P = rec["T"], rec["P"]
+    out = []
+    for b, rows in rec["rows"].items():
+        h_all = rec["hidden"][l][b * T:(b + 1) * T].astype(np.float64)
+        q, k, v = M.qkv(h_all, lw, P + np.arange(T))
+        Kp, Vp = _kv(rec["kv"], rec["Bp"], P, l, 0 if rec["Bp"] == 1 else b)
+        o = om.attention(q[rows], np.concatenate([Kp, k]), np.concatenate([Vp, v]),
+                         np.ones((len(rows), P + T), dtype=bool))
+        out.append((rec, b, rows, h_all[rows], o))
+    return out
+
+
+@pytest.mark.parametrize("group", LAYER_GROUPS, ids=[f"layers{a}-{b - 1}" for a, b in LAYER_GROUPS])
+def test_full_layers_teacher_forced(runs, group):
+    M = runs["M"]
+    for l in range(*group):
         lw = M.layer_dense(l)
-        for b, rows in rows_by_canvas.items():
-            r0 = b * T
-            h_in = hd[l][r0:r0 + T].astype(np.float64)
-            q, k, v = M.qkv(h_in, lw, pos)
-            Kp, Vp = kv_layer(kv, FULL, Bp, P_max, l, 0 if Bp == 1 else b, P)
-            kk = np.concatenate([Kp, k], axis=0)
-            vv = np.concatenate([Vp, v], axis=0)
-            o = om.attention(q[rows], kk, vv, np.ones((len(rows), P + T), dtype=bool))
-            h_out, info = M.post_attention(h_in[rows], o, lw)
-            gidx = ed[l][r0 + rows]
-            excused = check_experts(gidx, gd[l][r0 + rows], info["experts"], info["gates"],
-                                    info["router_logits"], FULL.top_k, margin_tol=ROUTER_MARGIN,
-                                    gate_rtol=GATE_RTOL)
+        pieces = []
+        for rec in runs["cases"]:
+            pieces += _canvas_layer_pieces(runs, rec, l, lw)
+        pre = []
+        for i, pf in enumerate(runs["prefixes"]):
+            h, skip = _prefix_state(runs, i, l)
+            pre.append((i, h, skip, _prefix_attention(runs, pf, l, lw, h, skip, check=True)))
+        # every row's MoE in one pass over the experts (each expert widened once)
+        h_cat = np.concatenate([p[3] for p in pieces] + [p[1] for p in pre])
+        o_cat = np.concatenate([p[4] for p in pieces] + [p[3] for p in pre])
+        h_out, info = M.post_attention(h_cat, o_cat, lw)
+        margin_all = topk_margin(info["router_logits"], FULL.top_k)
+        i0 = 0
+        line = []
+        for rec, b, rows, h_in, o in pieces:
+            n = len(rows)
+            sl = slice(i0, i0 + n)
+            i0 += n
+            T = rec["T"]
+            g_idx = rec["experts"][l][b * T + rows]
+            g_gate = rec["gates"][l][b * T + rows]
+            o_idx, o_gate, margin = info["experts"][sl], info["gates"][sl], margin_all[sl]
+            ref = h_out[sl].copy()
+            excused = []
+            for r in range(n):
+                gs, os_ = set(g_idx[r].tolist()), set(o_idx[r].tolist())
+                if gs != os_:
+                    assert margin[r] < ROUTER_MARGIN, (rec["name"], l, b, int(rows[r]), sorted(gs ^ os_),
+                                                       float(margin[r]))
+                    excused.append(r)
+                    continue
+                og = dict(zip(o_idx[r].tolist(), o_gate[r].tolist()))
+                for e, gv in zip(g_idx[r].tolist(), g_gate[r].tolist()):
+                    assert abs(gv - og[e]) <= GATE_TOL, (rec["name"], l, b, int(rows[r]), e, gv, og[e])
             if excused:
-                h_att = h_in[rows] + o.reshape(len(rows), -1) @ lw["w_o"].T
+                ex = np.array(excused)
+                h_att = h_in[ex] + o[ex].reshape(len(ex), -1) @ lw["w_o"].T
                 xn2 = om.rms_norm(h_att, lw["ffn_norm"], FULL.rms_eps)
-                h_out = h_att + _moe_given_experts(M, xn2, lw, gidx.astype(np.int64))
-            got_out = hd[l + 1][r0 + rows].astype(np.float64)
-            per_row = np.linalg.norm(got_out - h_out, axis=1) / np.linalg.norm(h_out - h_in[rows], axis=1)
-            err = rel_l2(got_out - h_in[rows], h_out - h_in[rows])
-            assert err <= 2e-2, (l, b, err, np.round(per_row, 4).tolist(), excused)
+                ref[ex] = h_att + _moe_given_experts(xn2, lw, g_idx[ex].astype(np.int64))
+            got = rec["hidden"][l + 1][b * T + rows].astype(np.float64)
+            err = rel_l2(got, ref)
+            err_d = rel_l2(got - h_in, ref - h_in)
+            line.append(f"{rec['name']}[{b}] {err:.1e}/{err_d:.1e} x{len(excused)}")
+            assert err <= HIDDEN_TOL, (rec["name"], l, b, err, err_d)
+        for i, h, skip, o in pre:
+            n = len(h)
+            sl = slice(i0, i0 + n)
+            i0 += n
+            nskip = skip | (margin_all[sl] < ROUTER_MARGIN)
+            runs["prefix_state"][i][l + 1] = (h_out[sl], nskip)
+            line.append(f"{runs['prefixes'][i]['name']} skip {int(nskip.sum())}")
+        announce(f"layer {l}: " + "; ".join(line))
 
 
-def _check_sampler(got, b, T, seed, step, sp, stopped_expect=None):
-    """The sampler decisions of canvas b against the oracle on the GPU's logits."""
-    l32 = got["logits_dump"][b]
-    H = osmp.entropy(l32)
-    assert np.allclose(got["entropy"][b], H, rtol=1e-3)
-    tau, inv_tau = osmp.temperature(step, sp.tau_start, sp.tau_end, sp.max_steps)
-    xhat, _, _ = osmp.gumbel_argmax(l32, inv_tau, seed, step)
-    assert np.array_equal(got["xhat"][b], xhat)
-    assert np.array_equal(got["argmax"][b], np.argmax(l32, axis=-1))
-    lock = osmp.lock_mask(H, sp.lock_rule, sp.lock_thresh)
-    far = np.abs(H - sp.lock_thresh) > 1e-4
-    assert np.array_equal(got["locked"][b].astype(bool)[far], lock[far])
-    stop = step + 1 >= sp.max_steps or H.mean() < sp.stop_thresh
-    if stopped_expect is not None:
-        assert stop == stopped_expect
-    assert bool(got["stopped"][b]) == stop and got["steps"][b] == step + 1
-    if stop:
-        assert np.array_equal(got["tokens"][b], got["xhat"][b])
-    else:
-        noise = osmp.rerandomized_tokens(seed, step, T, FULL.vocab)
-        expect = np.where(got["locked"][b].astype(bool), got["xhat"][b], noise)
-        assert np.array_equal(got["tokens"][b], expect)
-
-
-def _check_logits_rows(M, got, rows_by_canvas, T):
-    for b, rows in rows_by_canvas.items():
-        logits = M.head(got["hidden_dump"][FULL.n_layers][b * T + rows].astype(np.float64))
-        assert rel_l2(got["logits_dump"][b][rows], logits) <= 1e-2, b
-
-
-def test_full_step_sampled_rows(full):
-    """full_step: steps 0 and 1 (step 1 consumes step 0's self-conditioning)."""
-    dm, M = full
-    wl = WORKLOADS["full_step"]
-    B, T, P = wl.batch, wl.canvas_len, wl.prefix_len
-    prefix = synth.tokens(SEED, "prefix", (1, P), FULL.vocab)
-    seeds = synth.row_seeds(SEED, B)
-    kv = dm.kv_cache(1, P)
-    ws = dm.workspace(B * T, P + T)
-    stream = torch.cuda.Stream()
-    announce("full_step: prefill 2048 tokens")
-    pre = dev(prefix)
-    torch.cuda.synchronize()   # the upload ran on the default stream
-    dg.dg_prefill_prefix(dm.handle, pre, 1, P, P, kv, ws, stream=stream)
-    sp = SamplerParams()
-    sampler, keep = dg.make_sampler(sp, seeds)
-    st = dm.canvas_state(B, T, dumps=True)
-    torch.cuda.synchronize()   # zero-filled on the default stream
-    dg.dg_init_canvas(dm.handle, dg.make_canvas(st), B, T, seeds, stream=stream)
-    stream.synchronize()
-    tok0 = host(st["tokens"])
-    rng = np.random.default_rng(7)
-    rows = {0: np.sort(rng.choice(T, 6, replace=False))}
-    announce("full_step: prefix KV of layer 0")
-    _check_prefix_layer0(M, kv, 1, P, prefix, np.sort(rng.choice(P, 16, replace=False)))
-    prev = None
-    for step in (0, 1):
-        announce(f"full_step: step {step} (graph replay on a side stream)")
-        dg.dg_denoise_step(dm.handle, kv, 1, P, P, B, T, dg.make_canvas(st), step, sampler, ws, stream=stream)
-        stream.synchronize()
-        got = {k: host(v) for k, v in st.items()}
-        announce(f"full_step: oracle checks of step {step}")
-        if step == 0:
-            h0 = M.canvas_input(tok0[0][rows[0]], None)
-        else:
-            s_prev = synth.bf16_bits_to_f32(prev["self_cond"][0][rows[0]].view(np.uint16))
-            h0 = M.canvas_input(prev["tokens"][0][rows[0]], s_prev)
-        assert rel_l2(got["hidden_dump"][0][rows[0]], h0) <= 1e-2
-        _check_layers(M, got, kv, 1, P, P, T, rows)
-        _check_logits_rows(M, got, rows, T)
-        _check_sampler(got, 0, T, int(seeds[0]), step, sp, stopped_expect=False)
-        s_next = M.soft_embedding(got["logits_dump"][0][rows[0]])
-        assert rel_l2(synth.bf16_bits_to_f32(got["self_cond"][0][rows[0]].view(np.uint16)), s_next) <= 1e-2
-        prev = got
-    del kv, ws, st
-    torch.cuda.empty_cache()
-
-
-def test_full_block_runs_the_step_budget(full):
-    """full_block: dg_generate_block on the full model.  With random weights
-    the entropy stays near ln V, nothing locks and the block takes all 48
-    steps; the last step's sampler decisions match the oracle bit for bit."""
-    dm, M = full
-    wl = WORKLOADS["full_block"]
-    B, T, P = wl.batch, wl.canvas_len, wl.prefix_len
-    prefix = synth.tokens(SEED, "prefix", (1, P), FULL.vocab)
-    seeds = synth.row_seeds(SEED + 1, B)
-    kv = dm.kv_cache(1, P)
-    ws = dm.workspace(B * T, P + T)
-    stream = torch.cuda.Stream()
-    pre = dev(prefix)
-    torch.cuda.synchronize()   # the upload ran on the default stream
-    dg.dg_prefill_prefix(dm.handle, pre, 1, P, P, kv, ws, stream=stream)
-    sp = SamplerParams()
-    sampler, keep = dg.make_sampler(sp, seeds)
-    st = dm.canvas_state(B, T)
-    st["logits_dump"] = torch.zeros(B, T, FULL.vocab, dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()   # zero-filled on the default stream
-    dg.dg_init_canvas(dm.handle, dg.make_canvas(st), B, T, seeds, stream=stream)
-    announce("full_block: generate_block (48 steps)")
-    dg.dg_generate_block(dm.handle, kv, 1, P, P, B, T, dg.make_canvas(st), sampler, ws, poll_every=8,
-                         stream=stream)
-    stream.synchronize()
-    got = {k: host(v) for k, v in st.items()}
-    assert got["steps"].tolist() == [sp.max_steps] and got["stopped"].tolist() == [1]
-    assert not got["locked"].any()
-    announce("full_block: oracle replay of the last step's sampler")
-    _check_sampler(got, 0, T, int(seeds[0]), sp.max_steps - 1, sp, stopped_expect=True)
-    del kv, ws, st
-    torch.cuda.empty_cache()
-
-
-def test_long_block_four_canvases_sampled_rows(full):
-    """long_block: 4 canvases over one shared 32768-token prefix, one step."""
-    dm, M = full
-    wl = WORKLOADS["long_block"]
-    B, T, P = wl.batch, wl.canvas_len, wl.prefix_len
-    assert wl.prefix_batch == 1
-    prefix = synth.tokens(SEED, "long_prefix", (1, P), FULL.vocab)
-    seeds = synth.row_seeds(SEED + 2, B)
-    kv = dm.kv_cache(1, P)
-    ws = dm.workspace(B * T, P + T)
-    stream = torch.cuda.Stream()
-    announce("long_block: prefill 32768 tokens")
-    pre = dev(prefix)
-    torch.cuda.synchronize()   # the upload ran on the default stream
-    dg.dg_prefill_prefix(dm.handle, pre, 1, P, P, kv, ws, stream=stream)
-    sp = SamplerParams()
-    sampler, keep = dg.make_sampler(sp, seeds)
-    st = dm.canvas_state(B, T, dumps=True)
-    torch.cuda.synchronize()   # zero-filled on the default stream
-    dg.dg_init_canvas(dm.handle, dg.make_canvas(st), B, T, seeds, stream=stream)
-    stream.synchronize()
-    tok0 = host(st["tokens"])
-    rng = np.random.default_rng(11)
-    rows = {b: np.sort(rng.choice(T, 3, replace=False)) for b in range(B)}
-    announce("long_block: prefix KV of layer 0")
-    _check_prefix_layer0(M, kv, 1, P, prefix, np.sort(rng.choice(P, 16, replace=False)))
-    announce("long_block: step 0 for 4 canvases")
-    dg.dg_denoise_step(dm.handle, kv, 1, P, P, B, T, dg.make_canvas(st), 0, sampler, ws, stream=stream)
-    stream.synchronize()
-    got = {k: host(v) for k, v in st.items()}
-    announce("long_block: oracle checks")
-    for b in range(B):
-        h0 = M.canvas_input(tok0[b][rows[b]], None)
-        assert rel_l2(got["hidden_dump"][0][b * T + rows[b]], h0) <= 1e-2
-    _check_layers(M, got, kv, 1, P, P, T, rows)
-    _check_logits_rows(M, got, rows, T)
-    for b in range(B):
-        _check_sampler(got, b, T, int(seeds[b]), 0, sp, stopped_expect=False)
-    del kv, ws, st
-    torch.cuda.empty_cache()
-
-
-def test_full_ar_steps(full):
+def test_full_ar_steps(runs):
     """Autoregressive steps of the full model after a 2048-token prompt, at
     positions 2048..2050 (the last two unaligned): the K/V each step writes
     in layer 0 match the oracle's projection of the token's embedding; on the
     GPU's own fp32 logits over the full vocabulary the sampled token and the
     argmax are the oracle sampler's, bit for bit, and the entropy agrees."""
-    dm, M = full
+    dm, M = runs["dm"], runs["M"]
     P0, n, tau = 2048, 3, 0.8
     P_max = P0 + 32
     prefix = synth.tokens(SEED, "prefix", (1, P0), FULL.vocab)
@@ -284,19 +413,22 @@ def test_full_ar_steps(full):
     ws = dm.workspace(256, P_max)
     stream = torch.cuda.Stream()
     announce("full ar: prefill 2048")
-    dg.dg_prefill_prefix(dm.handle, dev(prefix), 1, P0, P_max, kv, ws, stream=stream)
+    pre = dev(prefix)
+    torch.cuda.synchronize()
+    dg.dg_prefill_prefix(dm.handle, pre, 1, P0, P_max, kv, ws, stream=stream)
     tok = dev(np.array([int(prefix[0, -1])], np.int32))
     toks_in = [int(prefix[0, -1])]
     logits = torch.zeros(n, FULL.vocab, device="cuda")
     nxt = torch.zeros(n, dtype=torch.int32, device="cuda")
     amax = torch.zeros(n, dtype=torch.int32, device="cuda")
     ent = torch.zeros(n, device="cuda")
+    torch.cuda.synchronize()
     for i in range(n):
         announce(f"full ar: dg_ar_step at P={P0 + i}")
         dg.dg_ar_step(dm.handle, kv, 1, P0 + i, P_max, tok, tau, seeds, nxt[i:i + 1], ws, argmax=amax[i:i + 1],
                       entropy=ent[i:i + 1], logits_dump=logits[i:i + 1], stream=stream)
         tok = nxt[i:i + 1]
-    torch.cuda.synchronize()
+    stream.synchronize()
     lg, nx, am, H = host(logits), host(nxt), host(amax), host(ent)
     K, V = kv_layer(kv, FULL, 1, P_max, 0, 0, P_max)
     toks_in += [int(x) for x in nx[:-1]]
@@ -304,11 +436,12 @@ def test_full_ar_steps(full):
     lw = M.layer_dense(0)
     pos = np.arange(P0, P0 + n)
     _, k, v = M.qkv(M.embed(np.array(toks_in)), lw, pos)
-    assert rel_l2(K[P0:P0 + n], k) <= 1e-2
-    assert rel_l2(V[P0:P0 + n], v) <= 1e-2
+    assert rel_l2(K[P0:P0 + n], k) <= HIDDEN_TOL
+    assert rel_l2(V[P0:P0 + n], v) <= HIDDEN_TOL
     assert not K[P0 + n:].any() and not V[P0 + n:].any()
     for i in range(n):
         assert np.isfinite(lg[i]).all()
         t_g, a_g, H_g, _ = osmp.ar_sample(lg[i], tau, seeds[0], P0 + i)
         assert nx[i] == t_g and am[i] == a_g, i
         assert np.isclose(H[i], H_g, rtol=1e-4), i
+    del kv, ws

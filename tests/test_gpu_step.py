@@ -172,15 +172,17 @@ def test_layer_step_matches_oracle(name):
     assert rel_l2(out - hc, h_o - hc) <= 2e-2
 
 
-def test_ragged_append_extends_prefix_cache():
-    """An append that starts and ends inside 32-key tiles (40 tokens at
-    positions 37..76, encoded as a 32-row chunk and an 8-row chunk by a small
-    workspace) gives K/V within rel-L2 1e-2 of the oracle's prefill of the
-    whole sequence in every layer, and leaves positions before and after it
-    untouched."""
-    wl = WORKLOADS["tiny_step"]
-    m = wl.model
-    P0, n, P_max = 37, 40, 96
+@pytest.mark.parametrize("shape,n", [(TINY, 40), (TINY_SHARED, 34)], ids=["tiny", "tiny_shared"])
+def test_ragged_append_extends_prefix_cache(shape, n):
+    """An append that starts and ends inside 32-key tiles (n tokens at
+    position 37, encoded by a small workspace as a 32-row chunk and a tail
+    chunk of n - 32 rows) gives K/V within rel-L2 1e-2 of the oracle's prefill
+    of the whole sequence in every layer, and leaves positions before and
+    after it untouched.  With the shared FFN and a tail of 2 rows, the tail
+    pass runs the shared FFN as extra experts of the grouped products, in a
+    workspace planned for 32-row chunks."""
+    m = shape
+    P0, P_max = 37, 96
     P = P0 + n
     dm = DeviceModel(m, SEED)
     toks = synth.tokens(SEED, "ragged", (1, P), m.vocab)

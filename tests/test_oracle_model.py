@@ -131,6 +131,30 @@ def test_moe_sparse_dispatch_equals_dense_masked_sum():
     assert np.allclose(y, dense, rtol=1e-12, atol=1e-14)
 
 
+def test_gated_ffn_gate_and_up_paths_are_distinct():
+    # Closed form at saturated GELU arguments: gelu_tanh(20) = 20 and
+    # gelu_tanh(-20) = 0 to double precision, so with x = e_0 the hidden units
+    # are 20 * (x Wu^T)_0 and 0, whatever the second up row is.  Swapping the
+    # gate and up matrices, or dropping the GELU, changes the result; the
+    # [out, in] orientation of every matrix is exercised by f != d.
+    x = np.array([[1.0, 0.0, 0.0]])
+    wg = np.array([[20.0, 0.0, 0.0], [-20.0, 0.0, 0.0]])
+    wu = np.array([[-3.0, 1.0, 0.0], [7.0, 0.0, 1.0]])
+    wd = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, 5.0]])
+    y = om.gated_ffn(x, wg, wu, wd)
+    assert np.allclose(y, [[-60.0, 0.0, -120.0]], rtol=0, atol=1e-9)
+    assert not np.allclose(om.gated_ffn(x, wu, wg, wd), y, atol=1.0)
+    # a gate far below zero silences the unit for any up projection
+    for up in (-5.0, 0.5, 40.0):
+        wu2 = np.array([[up, 0.0, 0.0], [up, 0.0, 0.0]])
+        wg_off = np.array([[-20.0, 0.0, 0.0], [-20.0, 0.0, 0.0]])
+        assert np.abs(om.gated_ffn(x, wg_off, wu2, wd)).max() < 1e-9
+    # gelu_tanh itself at the special points: 0 -> 0, large |x| -> relu(x)
+    assert om.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert om.gelu_tanh(np.array([30.0]))[0] == 30.0
+    assert abs(om.gelu_tanh(np.array([-30.0]))[0]) < 1e-12
+
+
 def test_one_expert_top1_is_dense_ffn_and_shared_only():
     m = ModelShape(1, 64, 2, 1, 32, 1, 1, 96, 48, 0, 0)
     lw = synth.layer_weights(m, 6, 0)

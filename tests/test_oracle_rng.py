@@ -142,3 +142,73 @@ def test_uniform_index_power_of_two_is_top_bits():
         np.concatenate(rng.philox4x32(np.arange(40000, dtype=np.uint64), 0, 0, 1, 5, 6)), 50),
         minlength=50)
     assert stats.chisquare(counts).pvalue > 1e-4
+
+
+def test_weyl_constants_from_closed_forms():
+    # The key schedule adds the golden ratio's fractional part and sqrt(3) - 1,
+    # scaled to the word width and truncated (SC'11, section 3, Philox key
+    # schedule).  Derived here in exact integer arithmetic.
+    from math import isqrt
+    for params in (rng.PHILOX4x32, rng.PHILOX4x64):
+        w = params["w"]
+        # floor(2^w (sqrt(5) - 1) / 2): sqrt(5) * 2^w = isqrt(5 * 4^w) (floor)
+        phi = (isqrt(5 << (2 * w)) - (1 << w)) >> 1
+        # floor(2^w (sqrt(3) - 1))
+        s3 = isqrt(3 << (2 * w)) - (1 << w)
+        assert params["k"] == (phi, s3), (w, hex(phi), hex(s3))
+
+
+def _rocrand_kat_binary(tmp_path_factory):
+    """A host program built from ROCm's rocRAND Philox4x32-10 header: an
+    independent implementation of the generator (source shipped with ROCm)."""
+    import os
+    import shutil
+    import subprocess
+    inc = "/opt/rocm/include"
+    hdr = os.path.join(inc, "rocrand", "rocrand_philox4x32_10.h")
+    gxx = shutil.which("g++")
+    if not os.path.exists(hdr) or gxx is None:
+        pytest.skip("rocRAND header or g++ not available")
+    d = tmp_path_factory.mktemp("rocrand_kat")
+    src = d / "kat.cpp"
+    src.write_text(
+        "#include <rocrand/rocrand_philox4x32_10.h>\n"
+        "#include <cstdio>\n#include <cstdlib>\n"
+        "int main(int argc, char** argv) {\n"
+        "  for (int a = 1; a + 2 < argc; a += 3) {\n"
+        "    rocrand_device::philox4x32_10_engine e(strtoull(argv[a], 0, 0), strtoull(argv[a + 1], 0, 0),\n"
+        "                                            strtoull(argv[a + 2], 0, 0));\n"
+        "    for (int i = 0; i < 4; ++i) printf(\"%u \", e());\n"
+        "    printf(\"\\n\");\n"
+        "  }\n"
+        "}\n")
+    exe = d / "kat"
+    r = subprocess.run([gxx, "-O1", "-D__HIP_PLATFORM_AMD__", "-I", inc, str(src), "-o", str(exe)],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("rocRAND header does not build on the host: " + r.stderr[-300:])
+    return exe
+
+
+def test_philox4x32_matches_rocrand(tmp_path_factory):
+    # rocRAND's engine seeded with (seed, subsequence, offset) produces, as its
+    # first four words, Philox4x32-10 of counter (offset / 4 as two words,
+    # subsequence as two words) under key (seed low word, seed high word).
+    # This pins the 4x32 multipliers, which numpy's 4x64 generator does not.
+    import subprocess
+    exe = _rocrand_kat_binary(tmp_path_factory)
+    g = np.random.default_rng(5)
+    cases = [(0, 0, 0), (0x123456789, 5, 8), (2**64 - 1, 2**64 - 1, 4 * (2**64 // 4 - 1))]
+    for _ in range(40):
+        cases.append((int(g.integers(0, 2**63)) * 2 + 1, int(g.integers(0, 2**63)),
+                      4 * int(g.integers(0, 2**61))))
+    args = [str(x) for c in cases for x in c]
+    out = subprocess.run([str(exe)] + args, capture_output=True, text=True, check=True).stdout.split("\n")
+    for (seed, sub, off), line in zip(cases, out):
+        got = [int(x) for x in line.split()]
+        c = off // 4
+        ctr = [c & 0xFFFFFFFF, c >> 32, sub & 0xFFFFFFFF, sub >> 32]
+        key = [seed & 0xFFFFFFFF, seed >> 32]
+        assert got == rng.philox_generic(ctr, key), (seed, sub, off)
+        v = rng.philox4x32(*ctr, *key)
+        assert got == [int(x) for x in v]
