@@ -69,19 +69,20 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kh, workload):
-    """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source and on this workload."""
+def profile_record(kh, workload):
+    """The committed rocprofv3 record of the gate/up kernel (HBM bytes per
+    launch from the counter runs, mean duration from the kernel trace), if it
+    was taken on the current kernel source and on this workload."""
     p = os.path.join(ROOT, "profiles", "expert_gateup_full_step_counters.json")
     if not os.path.exists(p):
-        return None
+        return {}
     try:
         d = json.load(open(p))
     except Exception:
-        return None
+        return {}
     if d.get("kernel_source_sha256_16") != kh or d.get("workload") != workload:
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return {}
+    return d
 
 
 def cpu_baseline(m_full, seed):
@@ -125,8 +126,13 @@ def cpu_baseline(m_full, seed):
     t_head = time.perf_counter() - t0
     step_s = m_full.n_layers * t_layer + frac * t_head
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    try:
+        host_cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        host_cores = os.cpu_count() or 1
     return {
-        "value": round(T / (48 * step_s), 4), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+        "value": round(T / (48 * step_s), 4), "unit": "tok/s", "cores": int(threads), "host_cores": int(host_cores),
+        "kind": "oracle",
         "sample": (f"float64 numpy oracle: one full-width layer step (256 canvas rows, 2048-key prefix) "
                    f"{t_layer:.2f}s x {m_full.n_layers} layers + LM head/entropy/Gumbel/soft-embedding on 1/{frac} "
                    f"of the vocabulary {t_head:.2f}s x {frac} = {step_s:.1f}s per step, 48 steps per block"),
@@ -414,10 +420,12 @@ def main():
         bytes_l = gateup_bytes(m, B * T, float(np.mean(touched)))
         ach = bytes_l / (per_launch_ms * 1e-3) / 1e9
         kh = kernel_hash()
+        rec = profile_record(kh, wl.name)
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(kh, wl.name),
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": rec.get("hbm_bytes_per_launch"),
                 "kernel": "grouped expert gate/up GEMM (dg::gemm_kernel<4, true>)",
                 "bytes_per_launch": int(bytes_l), "avg_launch_ms": round(per_launch_ms, 4),
+                "rocprof_avg_launch_ms": rec.get("rocprof_avg_launch_ms"),
                 "kernel_source_sha256_16": kh}
 
     out = {

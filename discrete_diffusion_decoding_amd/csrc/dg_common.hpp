@@ -88,4 +88,23 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return 0.5f * x * (1.0f + t);
 }
 
+// Online-softmax merge of two partial statistics {max m, Z = sum e^(l - m),
+// A = sum e^(l - m)(l - m), argmax (int bits)} over disjoint sets of logits:
+// both sums are rescaled to the larger maximum M (A also gains (m - M) Z from
+// the shift); the argmax keeps the larger logit, ties to the lower index.  An
+// empty partial has m = -inf.
+__device__ __forceinline__ float4 softmax_stats_merge(float4 x, float4 y) {
+  if (y.x == -INFINITY) return x;
+  if (x.x == -INFINITY) return y;
+  const float M = fmaxf(x.x, y.x);
+  const float fx = __expf(x.x - M), fy = __expf(y.x - M);
+  float4 r;
+  r.x = M;
+  r.y = fx * x.y + fy * y.y;
+  r.z = fx * (x.z + (x.x - M) * x.y) + fy * (y.z + (y.x - M) * y.y);
+  const int xi = __float_as_int(x.w), yi = __float_as_int(y.w);
+  r.w = (y.x > x.x || (y.x == x.x && yi < xi)) ? y.w : x.w;
+  return r;
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }

@@ -7,7 +7,10 @@
 
 namespace dg {
 
-enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GEGLU_BF16 = 4 };
+// EPI_HEAD: the LM head's fp32 logits, plus per (row, column tile) softmax
+// statistics (max, sum e^(l - max), sum e^(l - max)(l - max), argmax) in
+// GemmArgs::stats (dense rows, no k split)
+enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GEGLU_BF16 = 4, EPI_HEAD = 5 };
 
 // C[r, n] (op)= sum_k A[row(r), k] * W_g[n, k] over row chunks ("items").
 // A: bf16 rows of pitch lda; row(r) = a_rows ? a_rows[r] : r.
@@ -47,6 +50,11 @@ struct GemmArgs {
   void* C;
   long ldc;
   long c_kstride;
+  // EPI_HEAD: float4 {max, Z, A, argmax (int bits)} of row r over the columns of
+  // tile t at stats[r * stats_pitch + t]; the tile width is that of the kernel
+  // chosen (head_tile_cols)
+  float4* stats;
+  long stats_pitch;
   const int32_t* flag;
 };
 
@@ -55,6 +63,11 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
 // ceil(M / 256)); epilogues EPI_STORE_F32 (split-K partials) and EPI_STORE_BF16
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s);
+// the LM head with its per-tile softmax statistics (EPI_HEAD): rows >= 192 on
+// the 256 x 256 kernel, fewer on the 64-row kernel with 128-wide tiles;
+// returns the tile width used for the statistics in *tile_cols
+hipError_t lm_head(const GemmArgs& a, int* tile_cols, hipStream_t s);
+inline int head_tile_cols(int rows) { return rows >= 192 ? 256 : 128; }
 constexpr int kFatRowChunk = 256;
 // the 256-row kernel addresses a tile with 32-bit byte offsets from its first row
 inline bool gemm_fat_pitch_ok(long lda, long ldw) {
@@ -128,12 +141,13 @@ hipError_t attention_merge(const bf16_t* opart, const float* mlpart, int splits,
                            bf16_t* out, const int32_t* flag, hipStream_t s);
 
 // router logits = sum over split-K partials of the hi rows [0, rows) and lo rows [rows, 2 rows)
-// idx / gate [rows][k + ns]: the top-k, then experts E .. E + ns - 1 with gate 1
+// idx / gate [rows][k + ns]: the top-k, then experts E .. E + ns - 1 with gate 1;
+// logit_dump (optional) [rows][E]: the summed logits
 hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate, int32_t* idx_dump,
-                       float* gate_dump, const int32_t* flag, hipStream_t s);
+                       float* gate_dump, float* logit_dump, const int32_t* flag, hipStream_t s);
 // at most 4 rows: router_topk then moe_permute (chunk >= rows) in one launch
 hipError_t router_topk_permute(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate,
-                               int32_t* idx_dump, float* gate_dump, int32_t* counts, int32_t* offsets,
+                               int32_t* idx_dump, float* gate_dump, float* logit_dump, int32_t* counts, int32_t* offsets,
                                int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
                                const int32_t* flag, hipStream_t s);
 // k values moe_combine takes
@@ -158,10 +172,13 @@ struct SampleArgs {
   uint64_t seeds[16];
   int vsplit;                       // vocab slices per row
   float* part;                      // [B*T][vsplit][8]
-  float* rowstat;                   // [B*T][2]: max, Z (softmax of the logits)
+  float4* rowstat;                  // [B*T] out (optional): max, Z, entropy, argmax (int bits)
+  // the softmax statistics computed by the vocabulary-tiled LM head (same
+  // layout as rowstat): when set, the partial pass keeps only the Gumbel
+  // maximum and the finishing pass takes entropy and argmax from here
+  const float4* rowstat_in;
   int32_t* tokens; uint8_t* locked; float* entropy; int32_t* xhat; int32_t* argmax;
   int32_t* stopped; int32_t* steps; int32_t* all_stopped;
-  int32_t* live;                    // [B] (optional): 1 if the row ran this step (not stopped on entry)
   const int32_t* flag;
 };
 // autoregressive next-token sample: B rows of V logits (row pitch ldl), one
@@ -178,9 +195,14 @@ struct ArSampleArgs {
 hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s);
 hipError_t sample_partial(const SampleArgs& a, hipStream_t s);
 hipError_t sample_finish(const SampleArgs& a, hipStream_t s);
+// per row: the LM head's tile statistics [rows][ntiles] (pitch `pitch`) merged
+// into rowstat {max, Z, entropy H = ln Z - A / Z, argmax}; live[b] = 1 for the
+// canvases b not stopped on entry (their rows run the step)
+hipError_t head_stats_finish(const float4* stats, long pitch, int ntiles, int rows, int T, float4* rowstat,
+                             const int32_t* stopped, int32_t* live, const int32_t* flag, hipStream_t s);
 // the soft-prediction embedding of the rows that ran this step (live[r / T] != 0);
 // rows of a canvas that had stopped before the step are left as they are
-hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,
+hipError_t softmax_probs(const float* logits, const float4* rowstat, int rows, int V, long ldl, bf16_t* P,
                          const int32_t* live, int T, const int32_t* flag, hipStream_t s);
 hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out,
                              const int32_t* live, int T, const int32_t* flag, hipStream_t s);

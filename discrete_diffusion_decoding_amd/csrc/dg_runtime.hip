@@ -211,8 +211,9 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // workspace plan
 struct Plan {
   size_t h, xn, qkv, q, kc, vc, rope, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
-      nitems, hbuf, ybuf, hs, ys, logits, spart, rowstat, live, P, separt, flag, pos, total;
+      nitems, hbuf, ybuf, hs, ys, logits, spart, hstats, rowstat, live, P, separt, flag, pos, total;
   int splits_max, vsplit, ksplit, kchunk;
+  long hstats_pitch;   // tiles per row of the LM head's statistics
 };
 
 static const int kMaxSplits = 16;
@@ -340,7 +341,9 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
     p.vsplit = vsplit_of(rows, (int)V);
     p.logits = take(R * V * 4);
     p.spart = take(R * p.vsplit * 8 * 4);
-    p.rowstat = take(R * 2 * 4);
+    p.hstats_pitch = cdiv(V, head_tile_cols(rows));
+    p.hstats = take(R * p.hstats_pitch * 16);
+    p.rowstat = take(R * 16);
     p.live = take(64 * 4);   // one flag per canvas (B <= 16)
     if (d.self_cond) {
       soft_split(d, rows, &p.ksplit, &p.kchunk);
@@ -375,6 +378,7 @@ struct Pass {
   float* hidden_dump;
   int32_t* expert_dump;
   float* gate_dump;
+  float* router_dump;
   bool final_norm;            // last combine writes the final-normed hidden into xn
   const int32_t* flag;
   const int32_t* pos_dev;     // prefill of one position read from the device (q0, pos0 unused)
@@ -608,11 +612,12 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       ProfScope psr_(m, DG_PROF_ROUTER, st);
       int32_t* edump = ps.expert_dump ? ps.expert_dump + (size_t)l * R * k : nullptr;
       float* gdump = ps.gate_dump ? ps.gate_dump + (size_t)l * R * k : nullptr;
+      float* rdump = ps.router_dump ? ps.router_dump + (size_t)l * R * E : nullptr;
       if (R <= 4) {   // decoding: one launch
-        DG_CK(router_topk_permute(rlp, R, E, k, ns, eidx, egate, edump, gdump, cnt, off, slot_of, slot_row, items,
+        DG_CK(router_topk_permute(rlp, R, E, k, ns, eidx, egate, edump, gdump, rdump, cnt, off, slot_of, slot_row, items,
                                   nitems, m->x_rows, ps.flag, st));
       } else {
-        DG_CK(router_topk(rlp, R, E, k, ns, eidx, egate, edump, gdump, ps.flag, st));
+        DG_CK(router_topk(rlp, R, E, k, ns, eidx, egate, edump, gdump, rdump, ps.flag, st));
         DG_CK(moe_permute(eidx, R, kx, Ex, cnt, off, slot_of, slot_row, items, nitems, m->x_rows, ps.flag, st));
       }
     }
@@ -696,25 +701,49 @@ extern "C" dg_status dg_forward_hidden(dg_model* m, const void* kv, int32_t Bp, 
   return DG_OK;
 }
 
+// Optional records of one pass of a prefill (prompt 0, positions pos ..
+// pos + n - 1): layer inputs, final hidden, routing.
+struct PrefillDump {
+  int pos = 0, n = 0;
+  float* hidden = nullptr;
+  int32_t* experts = nullptr;
+  float* gates = nullptr;
+  float* router = nullptr;
+};
+
 // causal encoding of positions P0 .. P0+n-1 of each of Bp prompts (inputs
 // [Bp][n]), against the cached K/V of positions 0 .. P0-1
 static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* hidden, int Bp, int P0, int n,
-                              int P_max, void* kv, void* ws, size_t ws_bytes, hipStream_t st) {
+                              int P_max, void* kv, void* ws, size_t ws_bytes, hipStream_t st,
+                              const PrefillDump& dump = PrefillDump()) {
   if (!m || !kv || !ws || (!tokens && !hidden)) return DG_ERR_ARG;
   if (Bp < 1 || n < 1 || P0 < 0 || P_max < P0 + n) return DG_ERR_ARG;
   if (P_max % 32) return DG_ERR_SHAPE;
   if (tokens && m->d.vocab == 0) return DG_ERR_ARG;
+  if (dump.n && (dump.n < 1 || dump.pos < P0 || dump.pos + dump.n > P0 + n)) return DG_ERR_ARG;
   const int P = P0 + n;
   // largest chunk whose workspace fits: all n rows (at most 4096), else a multiple of 32
   int chunk = 0;
   for (int c = std::min(n, 4096); c >= 1; c = c > 32 ? (c - 1) / 32 * 32 : 0)
     if (make_plan(m->d, c, P).total <= ws_bytes) { chunk = c; break; }
   if (chunk == 0) return DG_ERR_WORKSPACE;
+  if (dump.n > chunk) return DG_ERR_WORKSPACE;   // the recorded positions make one pass
   const Plan p = make_plan(m->d, chunk, P);
   const dg_model_desc& d = m->d;
   for (int bp = 0; bp < Bp; ++bp) {
-    for (int q0 = P0; q0 < P; q0 += chunk) {
-      const int R = std::min(chunk, P - q0);
+    // passes of at most `chunk` rows; with a record, its positions are one pass
+    const bool rec = bp == 0 && dump.n > 0;
+    for (int q0 = P0; q0 < P;) {
+      int R = std::min(chunk, P - q0);
+      bool here = false;
+      if (rec) {
+        if (q0 == dump.pos) {
+          R = dump.n;
+          here = true;
+        } else if (q0 < dump.pos) {
+          R = std::min(R, dump.pos - q0);
+        }
+      }
       if (tokens) {
         DG_CK(embed_rows(tokens + (size_t)bp * n + (q0 - P0), (const bf16_t*)m->w.embed, R, d.d_model,
                          at<float>(ws, p.h), nullptr, st));
@@ -723,16 +752,33 @@ static dg_status prefill_impl(dg_model* m, const int32_t* tokens, const float* h
                              (size_t)R * d.d_model * 4, hipMemcpyDeviceToDevice, st));
       }
       DG_CK(rmsnorm_rows(at<float>(ws, p.h), m->layers[0] + m->lay.attn_norm, R, d.d_model, d.rms_eps,
-                         at<bf16_t>(ws, p.xn), nullptr, nullptr, Partials{nullptr, 0, 0}, nullptr, nullptr, st));
+                         at<bf16_t>(ws, p.xn), nullptr, here ? dump.hidden : nullptr, Partials{nullptr, 0, 0},
+                         nullptr, nullptr, st));
       Pass ps{};
       ps.rows = R; ps.B = 1; ps.per_batch = R; ps.pos0 = q0; ps.prefill = true; ps.bp = bp; ps.q0 = q0;
       ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = 1; ps.P = 0; ps.P_max = P_max;
       ps.final_norm = false; ps.flag = nullptr;
+      if (here) {
+        ps.hidden_dump = dump.hidden; ps.expert_dump = dump.experts; ps.gate_dump = dump.gates;
+        ps.router_dump = dump.router;
+      }
       dg_status s = run_layers(m, p, ws, ps, st);
       if (s != DG_OK) return s;
+      q0 += R;
     }
   }
   return DG_OK;
+}
+
+extern "C" dg_status dg_prefill_dump(dg_model* m, const int32_t* tokens, int32_t Bp, int32_t P0, int32_t n,
+                                     int32_t P_max, void* kv, int32_t dump_pos, int32_t dump_n, float* hidden_dump,
+                                     int32_t* expert_dump, float* gate_dump, float* router_dump, void* ws,
+                                     size_t ws_bytes, dg_stream_t stream) {
+  if (!tokens || dump_n < 1) return DG_ERR_ARG;
+  PrefillDump dmp;
+  dmp.pos = dump_pos; dmp.n = dump_n; dmp.hidden = hidden_dump; dmp.experts = expert_dump; dmp.gates = gate_dump;
+  dmp.router = router_dump;
+  return prefill_impl(m, tokens, nullptr, Bp, P0, n, P_max, kv, ws, ws_bytes, (hipStream_t)stream, dmp);
 }
 
 extern "C" dg_status dg_prefill_prefix(dg_model* m, const int32_t* prefix, int32_t Bp, int32_t P, int32_t P_max,
@@ -889,7 +935,7 @@ static dg_status check_canvas(const dg_canvas* c, bool need_sc) {
 }
 
 static SampleArgs sample_args(const float* logits, int B, int T, int V, dg_canvas* c, int step_arg,
-                              const dg_sampler* sp, float* part, int vsplit, float* rowstat, int32_t* all_stopped,
+                              const dg_sampler* sp, float* part, int vsplit, float4* rowstat, int32_t* all_stopped,
                               const int32_t* flag) {
   SampleArgs a;
   memset(&a, 0, sizeof(a));
@@ -932,27 +978,43 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   ps.rows = R; ps.B = B; ps.per_batch = T; ps.pos0 = P; ps.prefill = false;
   ps.kv = (const bf16_t*)kv; ps.kv_Bp = Bp; ps.Bp = Bp; ps.P = P; ps.P_max = P_max;
   ps.hidden_dump = c->hidden_dump; ps.expert_dump = c->expert_dump; ps.gate_dump = c->gate_dump;
+  ps.router_dump = c->router_dump;
   ps.final_norm = true; ps.flag = flag;
   dg_status s = run_layers(m, p, ws, ps, st);
   if (s != DG_OK) return s;
-  // LM head: logits = rms(h) E^T
+  // Vocabulary-tiled LM head: logits = rms(h) E^T, and per (row, vocabulary
+  // tile) the online-softmax statistics {max, Z, A, argmax} from the fp32
+  // accumulators; one merge per row gives the entropy, the argmax and the
+  // softmax (max, Z) of the soft-prediction embedding.  The Gumbel-max pass
+  // over the logits (Philox-bound ALU work) runs on the side stream beside the
+  // memory-bound soft-prediction embedding; the finishing pass joins both.
   float* logits = c->logits_dump ? c->logits_dump : at<float>(ws, p.logits);
+  float4* hstats = at<float4>(ws, p.hstats);
+  int tile_cols = 0;
   {
     GemmArgs g = gargs();
     g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D;
-    g.C = logits; g.ldc = V; g.flag = flag;
+    g.M = R; g.C = logits; g.ldc = V; g.flag = flag; g.stats = hstats; g.stats_pitch = p.hstats_pitch;
     ProfScope ps_(m, DG_PROF_LMHEAD, st);
-    DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
+    DG_CK(lm_head(g, &tile_cols, st));
   }
-  float* rowstat = at<float>(ws, p.rowstat);
-  SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, rowstat,
-                              nullptr, flag);
+  float4* rowstat = at<float4>(ws, p.rowstat);
   int32_t* live = at<int32_t>(ws, p.live);
-  sa.live = live;
+  SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, nullptr,
+                              nullptr, flag);
+  sa.rowstat_in = rowstat;
+  bool forked = false;
+  if (!m->prof.on && side_stream(m)) {
+    DG_CK(hipEventRecord(m->ev_fork, st));
+    DG_CK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
+    DG_CK(sample_partial(sa, m->side));
+    DG_CK(hipEventRecord(m->ev_join, m->side));
+    forked = true;
+  }
   {
     ProfScope ps_(m, DG_PROF_SAMPLER, st);
-    DG_CK(sample_partial(sa, st));
-    DG_CK(sample_finish(sa, st));
+    DG_CK(head_stats_finish(hstats, p.hstats_pitch, cdiv(V, tile_cols), R, T, rowstat, c->stopped, live, flag, st));
+    if (!forked) DG_CK(sample_partial(sa, st));
   }
   if (d.self_cond) {
     ProfScope ps_(m, DG_PROF_SOFTEMB, st);
@@ -964,6 +1026,11 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     g.c_kstride = (long)R * D; g.flag = flag;
     DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
     DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, live, T, flag, st));
+  }
+  if (forked) DG_CK(hipStreamWaitEvent(st, m->ev_join, 0));
+  {
+    ProfScope ps_(m, DG_PROF_SAMPLER, st);
+    DG_CK(sample_finish(sa, st));
   }
   (void)all_stopped;
   return DG_OK;
@@ -1059,7 +1126,7 @@ extern "C" dg_status dg_generate_block(dg_model* m, const void* kv, int32_t Bp, 
 extern "C" size_t dg_sample_workspace_bytes(int32_t B, int32_t T, int32_t V) {
   if (B < 1 || T < 1 || V < 1) return 0;
   const int rows = B * T;
-  return al256((size_t)rows * vsplit_of(rows, V) * 8 * 4) + al256((size_t)rows * 2 * 4);
+  return al256((size_t)rows * vsplit_of(rows, V) * 8 * 4) + al256((size_t)rows * 16);
 }
 
 extern "C" dg_status dg_sample_logits(const float* logits, int32_t B, int32_t T, int32_t V, dg_canvas* canvas,
@@ -1075,7 +1142,7 @@ extern "C" dg_status dg_sample_logits(const float* logits, int32_t B, int32_t T,
   const int rows = B * T;
   const int vs = vsplit_of(rows, V);
   float* part = (float*)ws;
-  float* rowstat = at<float>(ws, al256((size_t)rows * vs * 8 * 4));
+  float4* rowstat = at<float4>(ws, al256((size_t)rows * vs * 8 * 4));
   SampleArgs sa = sample_args(logits, B, T, V, canvas, step, sp, part, vs, rowstat, nullptr, nullptr);
   hipStream_t st = (hipStream_t)stream;
   DG_CK(sample_partial(sa, st));

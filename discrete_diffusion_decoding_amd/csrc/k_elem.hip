@@ -425,7 +425,8 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t x) {
 // blocks, when they run as experts); the dumps hold the routed ones only.
 template <int NS, int NK>
 __global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, int ns, int32_t* idx, float* gate,
-                                                  int32_t* idx_dump, float* gate_dump, const int32_t* flag) {
+                                                  int32_t* idx_dump, float* gate_dump, float* logit_dump,
+                                                  const int32_t* flag) {
   if (flag && *flag) return;
   const int lane = threadIdx.x;
   const int r = blockIdx.x;
@@ -443,6 +444,7 @@ __global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, 
           l += rl.p[s * rl.stride + (long)(rows + r) * E + e];
         }
         key[j] = topk_key(h + l, e);
+        if (logit_dump) logit_dump[(long)r * E + e] = h + l;
       }
     }
   }
@@ -483,20 +485,20 @@ __global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, 
 }
 
 hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate, int32_t* idx_dump,
-                       float* gate_dump, const int32_t* flag, hipStream_t s) {
+                       float* gate_dump, float* logit_dump, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (E > 256 || k > E || ns < 0 || k + ns > 64 || rlog.n < 1 || rlog.n > 8) return hipErrorInvalidValue;
   const dim3 grid(rows), block(64);
 #define DG_TOPK_NS(NK)                                                                                   \
   switch (rlog.n) {                                                                                      \
-    case 1: hipLaunchKernelGGL((topk_kernel<1, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 2: hipLaunchKernelGGL((topk_kernel<2, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 3: hipLaunchKernelGGL((topk_kernel<3, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 4: hipLaunchKernelGGL((topk_kernel<4, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 5: hipLaunchKernelGGL((topk_kernel<5, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 6: hipLaunchKernelGGL((topk_kernel<6, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    case 7: hipLaunchKernelGGL((topk_kernel<7, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
-    default: hipLaunchKernelGGL((topk_kernel<8, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, flag); break; \
+    case 1: hipLaunchKernelGGL((topk_kernel<1, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    case 2: hipLaunchKernelGGL((topk_kernel<2, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    case 3: hipLaunchKernelGGL((topk_kernel<3, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    case 4: hipLaunchKernelGGL((topk_kernel<4, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    case 5: hipLaunchKernelGGL((topk_kernel<5, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    case 6: hipLaunchKernelGGL((topk_kernel<6, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    case 7: hipLaunchKernelGGL((topk_kernel<7, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
+    default: hipLaunchKernelGGL((topk_kernel<8, NK>), grid, block, 0, s, rlog, rows, E, ns, idx, gate, idx_dump, gate_dump, logit_dump, flag); break; \
   }
   switch (k) {
     case 1: DG_TOPK_NS(1) break;
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* idx, int n
 template <int NS, int NK>
 __global__ __launch_bounds__(256) void topk_permute_kernel(Partials rl, int rows, int E, int ns, int32_t* idx,
                                                            float* gate, int32_t* idx_dump, float* gate_dump,
-                                                           int32_t* counts, int32_t* offsets, int32_t* slot_of,
+                                                           float* logit_dump, int32_t* counts, int32_t* offsets, int32_t* slot_of,
                                                            int32_t* slot_row, int4* items, int32_t* n_items,
                                                            int chunk, const int32_t* flag) {
   if (flag && *flag) return;
@@ -622,6 +624,7 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(Partials rl, int rows
             l += rl.p[s2 * rl.stride + (long)(rows + r) * E + e];
           }
           key[j] = topk_key(h + l, e);
+          if (logit_dump) logit_dump[(long)r * E + e] = h + l;
         }
       }
     }
@@ -665,7 +668,7 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(Partials rl, int rows
 }
 
 hipError_t router_topk_permute(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate,
-                               int32_t* idx_dump, float* gate_dump, int32_t* counts, int32_t* offsets,
+                               int32_t* idx_dump, float* gate_dump, float* logit_dump, int32_t* counts, int32_t* offsets,
                                int32_t* slot_of, int32_t* slot_row, int4* items, int32_t* n_items, int chunk,
                                const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
@@ -674,7 +677,7 @@ hipError_t router_topk_permute(Partials rlog, int rows, int E, int k, int ns, in
     return hipErrorInvalidValue;
 #define DG_TP(NS_, NK_)                                                                                       \
   hipLaunchKernelGGL((topk_permute_kernel<NS_, NK_>), dim3(1), dim3(256), 0, s, rlog, rows, E, ns, idx, gate, \
-                     idx_dump, gate_dump, counts, offsets, slot_of, slot_row, items, n_items, chunk, flag)
+                     idx_dump, gate_dump, logit_dump, counts, offsets, slot_of, slot_row, items, n_items, chunk, flag)
 #define DG_TP_NS(NK_)                       \
   switch (rlog.n) {                         \
     case 1: DG_TP(1, NK_); break;           \

@@ -156,11 +156,12 @@ __global__ __launch_bounds__(256) void sample_partial_kernel(SampleArgs a) {
   // entries v and v + 256 alternate between two register sets: the loads of
   // the next entry are in flight while one is processed (indices clamped to
   // the slice, so every load is issued)
+  const bool stats = a.rowstat_in == nullptr;   // else the LM head has them
   const auto proc = [&](int v, const float* lv) {
     const dg_u32x4 w = dg_philox4x32_10((uint32_t)v, (uint32_t)pg, (uint32_t)s, 0u, k0, k1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      stat_push(st[j], lv[j], v);
+      if (stats) stat_push(st[j], lv[j], v);
       screen_push(sc[j], lv[j], inv_tau, w.x[j], v);
     }
   };
@@ -227,9 +228,7 @@ __global__ __launch_bounds__(1024) void sample_finish_kernel(SampleArgs a) {
   __shared__ float red[16];
   __shared__ int unstable;
   const int b = blockIdx.x;
-  const bool was_stopped = a.stopped && a.stopped[b];
-  if (a.live && threadIdx.x == 0) a.live[b] = was_stopped ? 0 : 1;
-  if (was_stopped) return;
+  if (a.stopped && a.stopped[b]) return;
   const int s = row_step(a, b);
   const uint64_t seed = a.seeds[b];
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
@@ -244,7 +243,13 @@ __global__ __launch_bounds__(1024) void sample_finish_kernel(SampleArgs a) {
       Stat y{p[0], p[1], p[2], p[3], __float_as_int(p[4]), p[5], __float_as_int(p[6])};
       stat_merge(t, y);
     }
-    H = logf(t.Z) - t.A / t.Z;
+    if (a.rowstat_in) {
+      const float4 rs = a.rowstat_in[r];
+      H = rs.z;
+      t.ai = __float_as_int(rs.w);
+    } else {
+      H = logf(t.Z) - t.A / t.Z;
+    }
     Hs[i] = H;
   }
   __syncthreads();
@@ -282,10 +287,7 @@ __global__ __launch_bounds__(1024) void sample_finish_kernel(SampleArgs a) {
     a.argmax[r] = t.ai;
     a.entropy[r] = H;
     a.locked[r] = lock ? 1 : 0;
-    if (a.rowstat) {
-      a.rowstat[r * 2] = t.m;
-      a.rowstat[r * 2 + 1] = t.Z;
-    }
+    if (a.rowstat) a.rowstat[r] = make_float4(t.m, t.Z, H, __int_as_float(t.ai));
   }
   if (i == 0) {
     a.stopped[b] = stop ? 1 : 0;
@@ -392,12 +394,50 @@ hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void probs_kernel(const float* logits, const float* rowstat, int V, long ldl,
+// The vocabulary-tiled LM head leaves {max, Z, A, argmax} per (row, tile); one
+// workgroup per row merges them (thread t takes tiles t, t + 256, ..., then a
+// tree over the threads).  The merge is the online-softmax update: rescale
+// both sums to the larger maximum; A gains (m - M) Z from the shift.
+__global__ __launch_bounds__(256) void head_stats_finish_kernel(const float4* stats, long pitch, int ntiles, int T,
+                                                                float4* rowstat, const int32_t* stopped,
+                                                                int32_t* live, const int32_t* flag) {
+  if (flag && *flag) return;
+  __shared__ float4 red[4];
+  const int r = blockIdx.x;
+  if (threadIdx.x == 0 && live && r % T == 0) live[r / T] = stopped[r / T] ? 0 : 1;
+  float4 t = make_float4(-INFINITY, 0.f, 0.f, __int_as_float(0x7FFFFFFF));
+  for (int j = threadIdx.x; j < ntiles; j += 256) t = softmax_stats_merge(t, stats[(long)r * pitch + j]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float4 y;
+    y.x = __shfl_xor(t.x, o, 64); y.y = __shfl_xor(t.y, o, 64); y.z = __shfl_xor(t.z, o, 64);
+    y.w = __shfl_xor(t.w, o, 64);
+    t = softmax_stats_merge(t, y);
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float4 u = red[0];
+    for (int w = 1; w < 4; ++w) u = softmax_stats_merge(u, red[w]);
+    rowstat[r] = make_float4(u.x, u.y, logf(u.y) - u.z / u.y, u.w);
+  }
+}
+
+hipError_t head_stats_finish(const float4* stats, long pitch, int ntiles, int rows, int T, float4* rowstat,
+                             const int32_t* stopped, int32_t* live, const int32_t* flag, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (T < 1 || ntiles < 1 || pitch < ntiles) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(head_stats_finish_kernel, dim3(rows), dim3(256), 0, s, stats, pitch, ntiles, T, rowstat, stopped,
+                     live, flag);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void probs_kernel(const float* logits, const float4* rowstat, int V, long ldl,
                                                     bf16_t* P, const int32_t* live, int T, const int32_t* flag) {
   if (flag && *flag) return;
   const int r = blockIdx.y;
-  if (live && !live[r / T]) return;   // rowstat of a row that did not run is stale
-  const float m = rowstat[r * 2], iz = 1.0f / rowstat[r * 2 + 1];
+  if (live && !live[r / T]) return;   // a canvas stopped before the step keeps its state
+  const float m = rowstat[r].x, iz = 1.0f / rowstat[r].y;
   const long v = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (v >= V) return;
   const float4 l = *reinterpret_cast<const float4*>(logits + r * ldl + v);
@@ -407,7 +447,7 @@ __global__ __launch_bounds__(256) void probs_kernel(const float* logits, const f
   *reinterpret_cast<uint2*>(P + (long)r * V + v) = o;
 }
 
-hipError_t softmax_probs(const float* logits, const float* rowstat, int rows, int V, long ldl, bf16_t* P,
+hipError_t softmax_probs(const float* logits, const float4* rowstat, int rows, int V, long ldl, bf16_t* P,
                          const int32_t* live, int T, const int32_t* flag, hipStream_t s) {
   if (V % 4 != 0 || ldl % 4 != 0 || T < 1) return hipErrorInvalidValue;
   dim3 grid((unsigned)((V / 4 + 255) / 256), rows);

@@ -103,4 +103,5 @@ class DeviceModel:
             st["hidden_dump"] = torch.zeros(m.n_layers + 1, R, m.d_model, dtype=torch.float32, device=dev)
             st["expert_dump"] = torch.zeros(m.n_layers, R, m.top_k, dtype=torch.int32, device=dev)
             st["gate_dump"] = torch.zeros(m.n_layers, R, m.top_k, dtype=torch.float32, device=dev)
+            st["router_dump"] = torch.zeros(m.n_layers, R, m.n_experts, dtype=torch.float32, device=dev)
         return st

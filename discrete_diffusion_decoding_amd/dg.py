@@ -52,7 +52,8 @@ class Canvas(C.Structure):
     _fields_ = [("tokens", C.c_void_p), ("locked", C.c_void_p), ("entropy", C.c_void_p),
                 ("xhat", C.c_void_p), ("argmax", C.c_void_p), ("self_cond", C.c_void_p),
                 ("stopped", C.c_void_p), ("steps", C.c_void_p), ("logits_dump", C.c_void_p),
-                ("hidden_dump", C.c_void_p), ("expert_dump", C.c_void_p), ("gate_dump", C.c_void_p)]
+                ("hidden_dump", C.c_void_p), ("expert_dump", C.c_void_p), ("gate_dump", C.c_void_p),
+                ("router_dump", C.c_void_p)]
 
 
 _lib = None
@@ -76,6 +77,7 @@ def lib():
             "dg_prefill_prefix": (st, [vp, vp, i32, i32, i32, vp, vp, sz, vp]),
             "dg_prefill_append": (st, [vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]),
             "dg_prefill_hidden": (st, [vp, vp, i32, i32, i32, vp, vp, sz, vp]),
+            "dg_prefill_dump": (st, [vp, vp, i32, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
             "dg_ar_step": (st, [vp, vp, i32, i32, i32, vp, C.c_float, C.POINTER(C.c_uint64), vp, vp, vp, vp,
                                 vp, sz, vp]),
             "dg_forward_hidden": (st, [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]),
@@ -165,6 +167,13 @@ def dg_prefill_prefix(h, prefix, Bp, P, P_max, kv, ws, stream=None):
 def dg_prefill_append(h, tokens, Bp, P0, n, P_max, kv, ws, stream=None):
     _ck(lib().dg_prefill_append(h, _ptr(tokens), Bp, P0, n, P_max, _ptr(kv), _ptr(ws),
                                 ws.numel() * ws.element_size(), _stream(stream)), "dg_prefill_append")
+
+
+def dg_prefill_dump(h, tokens, Bp, P0, n, P_max, kv, dump_pos, dump_n, ws, hidden_dump=None, expert_dump=None,
+                    gate_dump=None, router_dump=None, stream=None):
+    _ck(lib().dg_prefill_dump(h, _ptr(tokens), Bp, P0, n, P_max, _ptr(kv), dump_pos, dump_n, _ptr(hidden_dump),
+                              _ptr(expert_dump), _ptr(gate_dump), _ptr(router_dump), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "dg_prefill_dump")
 
 
 def dg_ar_step(h, kv, B, P, P_max, token, tau, seeds, nxt, ws, argmax=None, entropy=None, logits_dump=None,

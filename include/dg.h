@@ -130,6 +130,8 @@ typedef struct {
  *   hidden_dump  fp32 [n_layers + 1][B*T][d]: input of every layer, then the
  *                final hidden state (before the final norm)
  *   expert_dump  int32 [n_layers][B*T][top_k]; gate_dump fp32 same shape
+ *   router_dump  fp32 [n_layers][B*T][n_experts]: the router logits the top-k
+ *                chose from
  * A stopped row (stopped[b] != 0 on entry) is left unchanged. */
 typedef struct {
   int32_t* tokens;
@@ -144,6 +146,7 @@ typedef struct {
   float* hidden_dump;
   int32_t* expert_dump;
   float* gate_dump;
+  float* router_dump;
 } dg_canvas;
 
 typedef struct dg_model dg_model;
@@ -192,6 +195,20 @@ dg_status dg_prefill_hidden(dg_model* m, const float* prefix_hidden, int32_t Bp,
  * over the result needs P0 + n to be a multiple of 32. */
 dg_status dg_prefill_append(dg_model* m, const int32_t* tokens, int32_t Bp, int32_t P0, int32_t n, int32_t P_max,
                             void* kv, void* ws, size_t ws_bytes, dg_stream_t stream);
+
+/* dg_prefill_append that also records, for the positions dump_pos ..
+ * dump_pos + dump_n - 1 of prompt 0 (inside [P0, P0 + n)), the input of every
+ * layer and the final hidden state, hidden_dump fp32 [n_layers + 1][dump_n][d],
+ * and the routing of every layer: expert_dump int32 [n_layers][dump_n][top_k],
+ * gate_dump fp32 of the same shape, router_dump fp32 [n_layers][dump_n]
+ * [n_experts] (any of them may be NULL).  For parity checks of the prompt
+ * cache at the model's full depth.  The recorded positions are encoded as one
+ * pass, so dump_n must not exceed the largest pass the workspace allows
+ * (DG_ERR_WORKSPACE otherwise); the cache written is the same as
+ * dg_prefill_append's. */
+dg_status dg_prefill_dump(dg_model* m, const int32_t* tokens, int32_t Bp, int32_t P0, int32_t n, int32_t P_max,
+                          void* kv, int32_t dump_pos, int32_t dump_n, float* hidden_dump, int32_t* expert_dump,
+                          float* gate_dump, float* router_dump, void* ws, size_t ws_bytes, dg_stream_t stream);
 
 /* One autoregressive decoding step (the model still generates token by token:
  * arXiv abstract page; article section 5 compares a denoising step with this
