@@ -17,6 +17,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "dg.h"
@@ -1129,25 +1130,81 @@ extern "C" size_t dg_sample_workspace_bytes(int32_t B, int32_t T, int32_t V) {
   return al256((size_t)rows * vsplit_of(rows, V) * 8 * 4) + al256((size_t)rows * 16);
 }
 
-extern "C" dg_status dg_sample_logits(const float* logits, int32_t B, int32_t T, int32_t V, dg_canvas* canvas,
-                                      int32_t step, const dg_sampler* sp, void* ws, size_t ws_bytes,
-                                      dg_stream_t stream) {
-  if (!logits || !ws || step < 0) return DG_ERR_ARG;
+// argument checks of the sampler entry points (no device work)
+static dg_status check_sample_args(const float* logits, int B, int T, int V, const dg_canvas* canvas, int step,
+                                   const dg_sampler* sp) {
+  if (!logits || step < 0) return DG_ERR_ARG;
   if (B < 1 || T < 1 || V < 1) return DG_ERR_ARG;
   if (B > 16 || T % 4 || T > 1024) return DG_ERR_SHAPE;
   dg_status s = check_sampler(sp, B);
   if (s != DG_OK) return s;
-  if ((s = check_canvas(canvas, false)) != DG_OK) return s;
+  return check_canvas(canvas, false);
+}
+
+// the sampler's launches over scratch ws (at least dg_sample_workspace_bytes(B, T, V) bytes)
+static dg_status sample_logits_impl(const float* logits, int B, int T, int V, dg_canvas* canvas, int step,
+                                    const dg_sampler* sp, void* ws, size_t ws_bytes, hipStream_t st) {
+  dg_status s = check_sample_args(logits, B, T, V, canvas, step, sp);
+  if (s != DG_OK) return s;
+  if (!ws) return DG_ERR_ARG;
   if (ws_bytes < dg_sample_workspace_bytes(B, T, V)) return DG_ERR_WORKSPACE;
   const int rows = B * T;
   const int vs = vsplit_of(rows, V);
   float* part = (float*)ws;
   float4* rowstat = at<float4>(ws, al256((size_t)rows * vs * 8 * 4));
   SampleArgs sa = sample_args(logits, B, T, V, canvas, step, sp, part, vs, rowstat, nullptr, nullptr);
-  hipStream_t st = (hipStream_t)stream;
   DG_CK(sample_partial(sa, st));
   DG_CK(sample_finish(sa, st));
   return DG_OK;
+}
+
+extern "C" dg_status dg_sample_logits(const float* logits, int32_t B, int32_t T, int32_t V, dg_canvas* canvas,
+                                      int32_t step, const dg_sampler* sp, void* ws, size_t ws_bytes,
+                                      dg_stream_t stream) {
+  return sample_logits_impl(logits, B, T, V, canvas, step, sp, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// dg_sample_logits_noalloc: the sampler over a scratch area that the library
+// owns, for callers that cannot allocate.  The area is a file-scope device
+// array (one copy per GPU, held until the process ends).  In host code its
+// name stands for no device address: the address is fetched once per device
+// with hipGetSymbolAddress and only that address is handed to kernels.
+// The largest request the sampler accepts (B 16, T 1024) needs 768 KB.
+static constexpr size_t kSampleScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) unsigned char scratch[kSampleScratchBytes];
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// the scratch array's address on the current device (looked up on first use)
+static dg_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  DG_CK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return DG_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DG_CK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return DG_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DG_OK;
+}
+
+extern "C" size_t dg_sample_noalloc_max_bytes(void) { return kSampleScratchBytes; }
+
+extern "C" dg_status dg_sample_logits_noalloc(const float* logits, int32_t B, int32_t T, int32_t V,
+                                              dg_canvas* canvas, int32_t step, const dg_sampler* sp,
+                                              dg_stream_t stream) {
+  dg_status s = check_sample_args(logits, B, T, V, canvas, step, sp);
+  if (s != DG_OK) return s;
+  if (dg_sample_workspace_bytes(B, T, V) > kSampleScratchBytes) return DG_ERR_WORKSPACE;
+  void* ws = nullptr;
+  s = scratch_on_current_device(&ws);
+  if (s != DG_OK) return s;
+  return sample_logits_impl(logits, B, T, V, canvas, step, sp, ws, kSampleScratchBytes, (hipStream_t)stream);
 }
 
 extern "C" dg_status dg_init_canvas(const dg_model* m, dg_canvas* c, int32_t B, int32_t T,

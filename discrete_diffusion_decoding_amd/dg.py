@@ -88,6 +88,8 @@ def lib():
             "dg_sample_workspace_bytes": (sz, [i32, i32, i32]),
             "dg_sample_logits": (st, [vp, i32, i32, i32, C.POINTER(Canvas), i32, C.POINTER(Sampler),
                                       vp, sz, vp]),
+            "dg_sample_noalloc_max_bytes": (sz, []),
+            "dg_sample_logits_noalloc": (st, [vp, i32, i32, i32, C.POINTER(Canvas), i32, C.POINTER(Sampler), vp]),
             "dg_init_canvas": (st, [vp, C.POINTER(Canvas), i32, i32, C.POINTER(C.c_uint64), vp]),
             "dg_transpose_bf16": (st, [vp, vp, C.c_int64, C.c_int64, vp]),
             "dg_gemm_bf16": (st, [vp, C.c_int64, vp, C.c_int64, i32, i32, i32, vp, C.c_int64, vp]),
@@ -226,6 +228,15 @@ def dg_sample_workspace_bytes(B, T, V):
 def dg_sample_logits(logits, B, T, V, canvas: Canvas, step, sampler: Sampler, ws, stream=None):
     _ck(lib().dg_sample_logits(_ptr(logits), B, T, V, C.byref(canvas), step, C.byref(sampler), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(stream)), "dg_sample_logits")
+
+
+def dg_sample_noalloc_max_bytes():
+    return int(lib().dg_sample_noalloc_max_bytes())
+
+
+def dg_sample_logits_noalloc(logits, B, T, V, canvas: Canvas, step, sampler: Sampler, stream=None):
+    _ck(lib().dg_sample_logits_noalloc(_ptr(logits), B, T, V, C.byref(canvas), step, C.byref(sampler),
+                                       _stream(stream)), "dg_sample_logits_noalloc")
 
 
 def dg_init_canvas(h, canvas: Canvas, B, T, seeds, stream=None):

@@ -20,7 +20,8 @@
  * Conventions (all calls):
  *   - Device pointers point to memory the caller owns (weights, KV cache,
  *     canvas state, workspace).  The library allocates no device memory; it
- *     keeps host-side bookkeeping only.
+ *     keeps host-side bookkeeping only (and, for dg_sample_logits_noalloc
+ *     alone, one static device array of 1 MiB).
  *   - Calls are stream-ordered and asynchronous: they enqueue kernels on
  *     `stream` and return.  Results are valid after the caller synchronises.
  *   - Arguments are checked before anything is enqueued; on a negative status
@@ -263,6 +264,22 @@ dg_status dg_generate_block(dg_model* m, const void* kv, int32_t Bp, int32_t P, 
 size_t dg_sample_workspace_bytes(int32_t B, int32_t T, int32_t V);
 dg_status dg_sample_logits(const float* logits, int32_t B, int32_t T, int32_t V, dg_canvas* canvas, int32_t step,
                            const dg_sampler* sp, void* ws, size_t ws_bytes, dg_stream_t stream);
+
+/* The sampler of dg_sample_logits for callers that cannot allocate device
+ * memory (code under stream capture, serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the per-slice partials in a
+ * scratch area the library owns (a static device array of
+ * dg_sample_noalloc_max_bytes() = 1 MiB on each GPU it runs on, kept until
+ * the process ends).  Runs on the current device; `stream` must belong to it.
+ * No allocation of any kind.  Every call on one GPU shares that GPU's area, so
+ * calls that overlap on one GPU (different streams, or different host threads)
+ * race: order them.  Nothing in the area needs clearing between calls (every
+ * partial a call reads is written by that call).  Requests larger than the
+ * area return DG_ERR_WORKSPACE before any device work (none of the accepted
+ * shapes is: B <= 16, T <= 1024 needs at most 768 KB). */
+size_t dg_sample_noalloc_max_bytes(void);
+dg_status dg_sample_logits_noalloc(const float* logits, int32_t B, int32_t T, int32_t V, dg_canvas* canvas,
+                                   int32_t step, const dg_sampler* sp, dg_stream_t stream);
 
 /* Initial canvas: tokens[b][i] uniform over the vocabulary from Philox counter
  * (i, 0, 0xFFFFFFFF, 1) keyed by row_seeds[b]; also zeroes stopped, steps,

@@ -164,6 +164,25 @@ def test_gemm_rejects_bad_shapes_before_any_device_work():
     assert L.dg_gemm_bf16(p, 64, p, 128, 8, 64, 128, p, 64, None) == dg.DG_ERR_ARG   # lda < K
 
 
+def test_sample_noalloc_rejects_bad_arguments_before_any_device_work():
+    """The no-allocation sampler checks its arguments before it looks up its
+    scratch area (no GPU here: any device call would fail with DG_ERR_HIP)."""
+    L = dg.lib()
+    assert L.dg_sample_noalloc_max_bytes() == 1 << 20
+    # the largest accepted request fits the scratch area
+    assert L.dg_sample_workspace_bytes(16, 1024, 262144) <= L.dg_sample_noalloc_max_bytes()
+    p = C.c_void_p(0x4000)
+    sp, keep = dg.make_sampler(SamplerParams(), [1])
+    cv = dg.Canvas(*([0x8000] * 5 + [None] + [0x8000] * 2 + [None] * 4))   # no self_cond, no dumps
+    f = L.dg_sample_logits_noalloc
+    assert f(None, 1, 32, 2048, C.byref(cv), 0, C.byref(sp), None) == dg.DG_ERR_ARG
+    assert f(p, 0, 32, 2048, C.byref(cv), 0, C.byref(sp), None) == dg.DG_ERR_ARG
+    assert f(p, 1, 30, 2048, C.byref(cv), 0, C.byref(sp), None) == dg.DG_ERR_SHAPE
+    assert f(p, 17, 32, 2048, C.byref(cv), 0, C.byref(sp), None) == dg.DG_ERR_SHAPE
+    assert f(p, 1, 32, 2048, C.byref(cv), -1, C.byref(sp), None) == dg.DG_ERR_ARG
+    assert f(p, 1, 32, 2048, None, 0, C.byref(sp), None) == dg.DG_ERR_ARG
+
+
 def test_host_philox_equals_oracle_definition():
     g = np.random.default_rng(0)
     for _ in range(200):
