@@ -7,10 +7,7 @@
 
 namespace dg {
 
-// EPI_HEAD: the LM head's fp32 logits, plus per (row, column tile) softmax
-// statistics (max, sum e^(l - max), sum e^(l - max)(l - max), argmax) in
-// GemmArgs::stats (dense rows, no k split)
-enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GEGLU_BF16 = 4, EPI_HEAD = 5 };
+enum Epi { EPI_STORE_BF16 = 0, EPI_STORE_F32 = 1, EPI_GEGLU_BF16 = 4 };
 
 // C[r, n] (op)= sum_k A[row(r), k] * W_g[n, k] over row chunks ("items").
 // A: bf16 rows of pitch lda; row(r) = a_rows ? a_rows[r] : r.
@@ -50,11 +47,6 @@ struct GemmArgs {
   void* C;
   long ldc;
   long c_kstride;
-  // EPI_HEAD: float4 {max, Z, A, argmax (int bits)} of row r over the columns of
-  // tile t at stats[r * stats_pitch + t]; the tile width is that of the kernel
-  // chosen (head_tile_cols)
-  float4* stats;
-  long stats_pitch;
   const int32_t* flag;
 };
 
@@ -63,11 +55,6 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
 // ceil(M / 256)); epilogues EPI_STORE_F32 (split-K partials) and EPI_STORE_BF16
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s);
-// the LM head with its per-tile softmax statistics (EPI_HEAD): rows >= 192 on
-// the 256 x 256 kernel, fewer on the 64-row kernel with 128-wide tiles;
-// returns the tile width used for the statistics in *tile_cols
-hipError_t lm_head(const GemmArgs& a, int* tile_cols, hipStream_t s);
-inline int head_tile_cols(int rows) { return rows >= 192 ? 256 : 128; }
 constexpr int kFatRowChunk = 256;
 // the 256-row kernel addresses a tile with 32-bit byte offsets from its first row
 inline bool gemm_fat_pitch_ok(long lda, long ldw) {
@@ -195,17 +182,20 @@ struct ArSampleArgs {
 hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s);
 hipError_t sample_partial(const SampleArgs& a, hipStream_t s);
 hipError_t sample_finish(const SampleArgs& a, hipStream_t s);
-// per row: the LM head's tile statistics [rows][ntiles] (pitch `pitch`) merged
-// into rowstat {max, Z, entropy H = ln Z - A / Z, argmax}; live[b] = 1 for the
-// canvases b not stopped on entry (their rows run the step)
-hipError_t head_stats_finish(const float4* stats, long pitch, int ntiles, int rows, int T, float4* rowstat,
-                             const int32_t* stopped, int32_t* live, const int32_t* flag, hipStream_t s);
-// the soft-prediction embedding of the rows that ran this step (live[r / T] != 0);
-// rows of a canvas that had stopped before the step are left as they are
-hipError_t softmax_probs(const float* logits, const float4* rowstat, int rows, int V, long ldl, bf16_t* P,
-                         const int32_t* live, int T, const int32_t* flag, hipStream_t s);
-hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out,
-                             const int32_t* live, int T, const int32_t* flag, hipStream_t s);
+// The vocabulary in nslices slices of kchunk entries (the split of the
+// soft-prediction product's contraction).  Per (row, slice): the slice's
+// softmax statistics {max m_s, Z_s = sum e^(l - m_s), A_s = sum e^(l - m_s)(l - m_s),
+// argmax} into sstat [rows][nslices], and (P not null) the slice-scaled
+// probabilities P[r][v] = bf16(e^(l_v - m_s)).  Rows of canvases stopped on
+// entry (stopped[r / T]) are skipped.
+hipError_t softmax_slices(const float* logits, long ldl, int rows, int V, int kchunk, int nslices, int T,
+                          const int32_t* stopped, bf16_t* P, float4* sstat, const int32_t* flag, hipStream_t s);
+// Per row: the slice statistics merged (online softmax) into rowstat {max, Z,
+// entropy ln Z - A / Z, argmax}; with part (the soft-prediction product's
+// split-K partials [nslices][rows][d]), also out[r] = bf16(sum_s e^(m_s - M) / Z
+// part[s][r]).  Rows of stopped canvases are skipped.
+hipError_t softmax_finish(const float4* sstat, int nslices, int rows, int T, const int32_t* stopped,
+                          const float* part, int d, bf16_t* out, float4* rowstat, const int32_t* flag, hipStream_t s);
 hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* seeds, hipStream_t s);
 hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
 hipError_t fill_u16(uint16_t* p, uint16_t v, long n, hipStream_t s);

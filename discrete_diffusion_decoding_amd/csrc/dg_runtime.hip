@@ -212,9 +212,8 @@ extern "C" size_t dg_kv_bytes(const dg_model* m, int32_t Bp, int32_t P_max) {
 // workspace plan
 struct Plan {
   size_t h, xn, qkv, q, kc, vc, rope, opart, ml, o, dpart, xn2, xr, rlog, eidx, egate, cnt, off, slot_of, slot_row, items,
-      nitems, hbuf, ybuf, hs, ys, logits, spart, hstats, rowstat, live, P, separt, flag, pos, total;
+      nitems, hbuf, ybuf, hs, ys, logits, spart, sstat, rowstat, P, separt, flag, pos, total;
   int splits_max, vsplit, ksplit, kchunk;
-  long hstats_pitch;   // tiles per row of the LM head's statistics
 };
 
 static const int kMaxSplits = 16;
@@ -342,12 +341,11 @@ static Plan make_plan(const dg_model_desc& d, int rows, int keys) {
     p.vsplit = vsplit_of(rows, (int)V);
     p.logits = take(R * V * 4);
     p.spart = take(R * p.vsplit * 8 * 4);
-    p.hstats_pitch = cdiv(V, head_tile_cols(rows));
-    p.hstats = take(R * p.hstats_pitch * 16);
+    // vocabulary slices: the split of the soft-prediction product's contraction
+    soft_split(d, rows, &p.ksplit, &p.kchunk);
+    p.sstat = take(R * p.ksplit * 16);
     p.rowstat = take(R * 16);
-    p.live = take(64 * 4);   // one flag per canvas (B <= 16)
     if (d.self_cond) {
-      soft_split(d, rows, &p.ksplit, &p.kchunk);
       p.P = take(R * V * 2);
       p.separt = take((size_t)p.ksplit * R * D * 4);
     }
@@ -983,24 +981,24 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
   ps.final_norm = true; ps.flag = flag;
   dg_status s = run_layers(m, p, ws, ps, st);
   if (s != DG_OK) return s;
-  // Vocabulary-tiled LM head: logits = rms(h) E^T, and per (row, vocabulary
-  // tile) the online-softmax statistics {max, Z, A, argmax} from the fp32
-  // accumulators; one merge per row gives the entropy, the argmax and the
-  // softmax (max, Z) of the soft-prediction embedding.  The Gumbel-max pass
-  // over the logits (Philox-bound ALU work) runs on the side stream beside the
-  // memory-bound soft-prediction embedding; the finishing pass joins both.
+  // LM head: logits = rms(h) E^T (fp32, 256 x 256 tiles over the vocabulary).
+  // The softmax statistics then come per vocabulary slice (the slices of the
+  // soft-prediction product's split contraction), merged per row online: the
+  // entropy and argmax for the sampler, and the slice weights of s_next.  The
+  // Gumbel-max pass over the logits (Philox-bound ALU work) runs on the side
+  // stream beside the memory-bound slice statistics; the finishing pass joins
+  // both.  (Beside the soft-prediction product instead, it keeps that
+  // product's one-workgroup-per-CU tiles off the CUs it occupies: slower.)
   float* logits = c->logits_dump ? c->logits_dump : at<float>(ws, p.logits);
-  float4* hstats = at<float4>(ws, p.hstats);
-  int tile_cols = 0;
   {
     GemmArgs g = gargs();
     g.A = xn; g.lda = D; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = D; g.N = V; g.k_chunk = D;
-    g.M = R; g.C = logits; g.ldc = V; g.flag = flag; g.stats = hstats; g.stats_pitch = p.hstats_pitch;
+    g.C = logits; g.ldc = V; g.flag = flag;
     ProfScope ps_(m, DG_PROF_LMHEAD, st);
-    DG_CK(lm_head(g, &tile_cols, st));
+    DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
   }
   float4* rowstat = at<float4>(ws, p.rowstat);
-  int32_t* live = at<int32_t>(ws, p.live);
+  float4* sstat = at<float4>(ws, p.sstat);
   SampleArgs sa = sample_args(logits, B, T, V, c, step_arg, sp, at<float>(ws, p.spart), p.vsplit, nullptr,
                               nullptr, flag);
   sa.rowstat_in = rowstat;
@@ -1013,24 +1011,24 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     forked = true;
   }
   {
-    ProfScope ps_(m, DG_PROF_SAMPLER, st);
-    DG_CK(head_stats_finish(hstats, p.hstats_pitch, cdiv(V, tile_cols), R, T, rowstat, c->stopped, live, flag, st));
-    if (!forked) DG_CK(sample_partial(sa, st));
-  }
-  if (d.self_cond) {
-    ProfScope ps_(m, DG_PROF_SOFTEMB, st);
-    bf16_t* P_ = at<bf16_t>(ws, p.P);
-    DG_CK(softmax_probs(logits, rowstat, R, V, V, P_, live, T, flag, st));
-    GemmArgs g = gargs();
-    g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
-    g.k_split = p.ksplit; g.C = at<float>(ws, p.separt); g.ldc = D;
-    g.c_kstride = (long)R * D; g.flag = flag;
-    DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
-    DG_CK(reduce_soft_embed(at<float>(ws, p.separt), p.ksplit, R, D, (bf16_t*)c->self_cond, live, T, flag, st));
+    ProfScope ps_(m, d.self_cond ? DG_PROF_SOFTEMB : DG_PROF_SAMPLER, st);
+    bf16_t* P_ = d.self_cond ? at<bf16_t>(ws, p.P) : nullptr;
+    DG_CK(softmax_slices(logits, V, R, V, p.kchunk, p.ksplit, T, c->stopped, P_, sstat, flag, st));
+    float* part = nullptr;
+    if (d.self_cond) {
+      GemmArgs g = gargs();
+      g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
+      g.k_split = p.ksplit; g.C = at<float>(ws, p.separt); g.ldc = D;
+      g.c_kstride = (long)R * D; g.flag = flag;
+      DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
+      part = at<float>(ws, p.separt);
+    }
+    DG_CK(softmax_finish(sstat, p.ksplit, R, T, c->stopped, part, D, (bf16_t*)c->self_cond, rowstat, flag, st));
   }
   if (forked) DG_CK(hipStreamWaitEvent(st, m->ev_join, 0));
   {
     ProfScope ps_(m, DG_PROF_SAMPLER, st);
+    if (!forked) DG_CK(sample_partial(sa, st));
     DG_CK(sample_finish(sa, st));
   }
   (void)all_stopped;

@@ -46,75 +46,6 @@ constexpr int gemm_wg_per_cu() {
   return NS * (AR + BW) * 128 > 80 * 1024 ? 1 : (NS == 2 && (AR + BW) * 128 * NS <= 53 * 1024 ? 3 : 2);
 }
 
-// ---------------------------------------------------------------------------
-// Softmax statistics of an LM-head tile: the vocabulary-tiled head reduces its
-// fp32 accumulators per row into {max, sum e^(l - max), sum e^(l - max)(l - max),
-// argmax} of the tile's columns (online softmax and entropy, merged across
-// tiles by head_stats_merge_kernel).  A lane holds rows 16 m + 4 lg + i of its
-// m-fragments and columns col0 + 16 n + lr of its n-fragments: per row it
-// reduces its NN columns, then the 16 lanes that share the row, and lane
-// lr == 0 leaves the statistics of the wave's columns in red[cg][row].
-template <int NM, int NN>
-__device__ __forceinline__ void head_stats_partial(const floatx4 (&acc)[NM][NN], int rbase, int col0, int N,
-                                                   float4* red, int cg, int rows_per_tile) {
-  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v[NN];
-      float mx = -INFINITY;
-      int ix = 0x7FFFFFFF;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        const int col = col0 + 16 * n + lr;
-        v[n] = col < N ? acc[m][n][i] : -INFINITY;
-        if (v[n] > mx) {
-          mx = v[n];
-          ix = col;
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float om = __shfl_xor(mx, o, 64);
-        const int oi = __shfl_xor(ix, o, 64);
-        if (om > mx || (om == mx && oi < ix)) {
-          mx = om;
-          ix = oi;
-        }
-      }
-      float z = 0.f, a = 0.f;
-      if (mx != -INFINITY) {
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-          if (v[n] != -INFINITY) {
-            const float d = v[n] - mx;
-            const float e = __expf(d);
-            z += e;
-            a += e * d;
-          }
-        }
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        z += __shfl_xor(z, o, 64);
-        a += __shfl_xor(a, o, 64);
-      }
-      if (lr == 0) red[cg * rows_per_tile + rbase + 16 * m + 4 * lg + i] = make_float4(mx, z, a, __int_as_float(ix));
-    }
-  }
-}
-
-// the column groups of each row merged in column order, written for the tile
-__device__ __forceinline__ void head_stats_store(const float4* red, int ncg, int rows_per_tile, int nrows,
-                                                 float4* out, long pitch, int tile) {
-  for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
-    float4 t = red[r];
-    for (int cg = 1; cg < ncg; ++cg) t = softmax_stats_merge(t, red[cg * rows_per_tile + r]);
-    out[(long)r * pitch + tile] = t;
-  }
-}
-
 template <int EPI, bool ITEMS, int AR, int BW, int NS>
 __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kernel(GemmArgs g) {
   static_assert(AR == 32 || AR == 64 || (AR == 128 && !ITEMS), "activation tile of 32, 64 (or dense 128) rows");
@@ -375,21 +306,13 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
         const float v = acc[m][n][i];
         if (EPI == EPI_STORE_BF16) {
           reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(v);
-        } else if (EPI == EPI_STORE_F32 || EPI == EPI_HEAD) {
+        } else if (EPI == EPI_STORE_F32) {
           reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = v;
         } else {
           reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(gelu_tanh(v) * u[i]);
         }
       }
     }
-  }
-  if constexpr (EPI == EPI_HEAD && !ITEMS) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();   // every wave has read its last stage: the ring is free
-    float4* red = reinterpret_cast<float4*>(S0);   // [4 waves][AR rows]
-    head_stats_partial<NAF, NBF>(acc, 0, n_base + WPW * wave, g.N, red, wave, AR);
-    __syncthreads();
-    head_stats_store(red, 4, AR, nrows, g.stats + (long)r0 * g.stats_pitch, g.stats_pitch, tile);
   }
 }
 
@@ -909,36 +832,6 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
       }
     }
   }
-  if constexpr (EPI == EPI_HEAD) {
-    __syncthreads();   // every wave has read its last stage: the ring is free
-    float4* red = reinterpret_cast<float4*>(S0);   // [4 column quarters][256 rows]
-    head_stats_partial<8, 4>(acc, 128 * wm, n_base + 64 * wn, g.N, red, wn, 256);
-    __syncthreads();
-    head_stats_store(red, 4, 256, nrows, g.stats + (long)r0 * g.stats_pitch, g.stats_pitch, tile);
-  }
-}
-
-hipError_t lm_head(const GemmArgs& a, int* tile_cols, hipStream_t s) {
-  if (a.K % 64 != 0 || a.k_chunk != a.K || a.k_split != 1 || a.items || a.a_rows || !a.stats || a.M < 1)
-    return hipErrorInvalidValue;
-  if (a.lda % 8 != 0 || a.ldw % 8 != 0) return hipErrorInvalidValue;
-  const int tc = head_tile_cols(a.M);
-  if (a.stats_pitch < (a.N + tc - 1) / tc) return hipErrorInvalidValue;
-  *tile_cols = tc;
-  if (tc == 256) {
-    if (!gemm_fat2_pitch_ok(a.lda, a.ldw)) return hipErrorInvalidValue;
-    GemmArgs b = a;
-    b.items_max = (a.M + 255) / 256;
-    const long total = (long)b.items_max * ((a.N + 255) / 256);
-    hipLaunchKernelGGL(gemm_fat2_kernel<EPI_HEAD>, dim3(xcd_grid(total)), dim3(512), 0, s, b);
-    return hipGetLastError();
-  }
-  if (a.M <= kGemvRows) return hipErrorInvalidValue;   // the MFMA tile kernel: more than 4 rows
-  GemmArgs b = a;
-  b.tile_rows = 64;
-  b.tile_cols = 128;
-  b.ring = 3;
-  return launch_v<EPI_HEAD, false, 64, 128, 3>(b, s);
 }
 
 hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s) {

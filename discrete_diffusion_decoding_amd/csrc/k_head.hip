@@ -394,86 +394,145 @@ hipError_t ar_sample(const ArSampleArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// The vocabulary-tiled LM head leaves {max, Z, A, argmax} per (row, tile); one
-// workgroup per row merges them (thread t takes tiles t, t + 256, ..., then a
-// tree over the threads).  The merge is the online-softmax update: rescale
-// both sums to the larger maximum; A gains (m - M) Z from the shift.
-__global__ __launch_bounds__(256) void head_stats_finish_kernel(const float4* stats, long pitch, int ntiles, int T,
-                                                                float4* rowstat, const int32_t* stopped,
-                                                                int32_t* live, const int32_t* flag) {
-  if (flag && *flag) return;
-  __shared__ float4 red[4];
-  const int r = blockIdx.x;
-  if (threadIdx.x == 0 && live && r % T == 0) live[r / T] = stopped[r / T] ? 0 : 1;
-  float4 t = make_float4(-INFINITY, 0.f, 0.f, __int_as_float(0x7FFFFFFF));
-  for (int j = threadIdx.x; j < ntiles; j += 256) t = softmax_stats_merge(t, stats[(long)r * pitch + j]);
+// Softmax statistics per vocabulary slice and the soft-prediction embedding.
+// The slices are those of the soft-prediction product's split contraction, so
+// each slice's probabilities can be scaled by its own maximum: the product
+// sums e^(l_v - m_s) E_v over the slice, and the finishing pass weighs slice
+// s by e^(m_s - M) / Z (the online-softmax merge of the slices' statistics).
+
+// (max, argmax) of the 64 lanes of a wave, in every lane; ties to the lower index
+__device__ __forceinline__ void wave_argmax(float& mx, int& ix) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    float4 y;
-    y.x = __shfl_xor(t.x, o, 64); y.y = __shfl_xor(t.y, o, 64); y.z = __shfl_xor(t.z, o, 64);
-    y.w = __shfl_xor(t.w, o, 64);
-    t = softmax_stats_merge(t, y);
+    const float om = __shfl_xor(mx, o, 64);
+    const int oi = __shfl_xor(ix, o, 64);
+    const bool take = (om > mx) | ((om == mx) & (oi < ix));
+    mx = take ? om : mx;
+    ix = take ? oi : ix;
   }
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+}
+
+__global__ __launch_bounds__(256) void softmax_slice_kernel(const float* logits, long ldl, int V, int kchunk,
+                                                            int nslices, int T, const int32_t* stopped, bf16_t* P,
+                                                            float4* sstat, const int32_t* flag) {
+  if (flag && *flag) return;
+  __shared__ float smx[4], sz[4], sa[4];
+  __shared__ int six[4];
+  const int r = blockIdx.x / nslices, sl = blockIdx.x % nslices;
+  if (stopped && stopped[r / T]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int v0 = sl * kchunk, v1 = min(V, v0 + kchunk);   // multiples of 4
+  const float* l = logits + (long)r * ldl;
+  // the slice's maximum and argmax (entries in increasing order per thread)
+  float mx = -INFINITY;
+  int ix = 0x7FFFFFFF;
+  for (int v = v0 + 4 * tid; v < v1; v += 1024) {
+    const float4 x = *reinterpret_cast<const float4*>(l + v);
+    if (x.x > mx) { mx = x.x; ix = v; }
+    if (x.y > mx) { mx = x.y; ix = v + 1; }
+    if (x.z > mx) { mx = x.z; ix = v + 2; }
+    if (x.w > mx) { mx = x.w; ix = v + 3; }
+  }
+  wave_argmax(mx, ix);
+  if (lane == 0) { smx[wave] = mx; six[wave] = ix; }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float4 u = red[0];
-    for (int w = 1; w < 4; ++w) u = softmax_stats_merge(u, red[w]);
-    rowstat[r] = make_float4(u.x, u.y, logf(u.y) - u.z / u.y, u.w);
+  float M = smx[0];
+  int I = six[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    const bool take = (smx[w] > M) | ((smx[w] == M) & (six[w] < I));
+    M = take ? smx[w] : M;
+    I = take ? six[w] : I;
   }
+  // e^(l - M) summed, with its (l - M)-weighted sum (entropy), stored scaled
+  float z = 0.f, a = 0.f;
+  bf16_t* prow = P ? P + (long)r * V : nullptr;
+  for (int v = v0 + 4 * tid; v < v1; v += 1024) {
+    const float4 x = *reinterpret_cast<const float4*>(l + v);
+    const float d0 = x.x - M, d1 = x.y - M, d2 = x.z - M, d3 = x.w - M;
+    const float e0 = __expf(d0), e1 = __expf(d1), e2 = __expf(d2), e3 = __expf(d3);
+    z += (e0 + e1) + (e2 + e3);
+    a += (e0 * d0 + e1 * d1) + (e2 * d2 + e3 * d3);
+    if (prow) {
+      uint2 o;
+      o.x = (uint32_t)f2bf(e0) | ((uint32_t)f2bf(e1) << 16);
+      o.y = (uint32_t)f2bf(e2) | ((uint32_t)f2bf(e3) << 16);
+      *reinterpret_cast<uint2*>(prow + v) = o;
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    z += __shfl_xor(z, o, 64);
+    a += __shfl_xor(a, o, 64);
+  }
+  if (lane == 0) { sz[wave] = z; sa[wave] = a; }
+  __syncthreads();
+  if (tid == 0)
+    sstat[(long)r * nslices + sl] = make_float4(M, (sz[0] + sz[1]) + (sz[2] + sz[3]), (sa[0] + sa[1]) + (sa[2] + sa[3]),
+                                                __int_as_float(I));
 }
 
-hipError_t head_stats_finish(const float4* stats, long pitch, int ntiles, int rows, int T, float4* rowstat,
-                             const int32_t* stopped, int32_t* live, const int32_t* flag, hipStream_t s) {
+hipError_t softmax_slices(const float* logits, long ldl, int rows, int V, int kchunk, int nslices, int T,
+                          const int32_t* stopped, bf16_t* P, float4* sstat, const int32_t* flag, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (T < 1 || ntiles < 1 || pitch < ntiles) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(head_stats_finish_kernel, dim3(rows), dim3(256), 0, s, stats, pitch, ntiles, T, rowstat, stopped,
-                     live, flag);
+  if (V % 4 || kchunk % 4 || ldl % 4 || nslices < 1 || (long)kchunk * nslices < V || T < 1)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(softmax_slice_kernel, dim3((unsigned)(rows * nslices)), dim3(256), 0, s, logits, ldl, V,
+                     kchunk, nslices, T, stopped, P, sstat, flag);
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void probs_kernel(const float* logits, const float4* rowstat, int V, long ldl,
-                                                    bf16_t* P, const int32_t* live, int T, const int32_t* flag) {
+// Workgroup (r, y): wave 0 merges the row's slice statistics (lane s holds
+// slice s; a butterfly of the online-softmax merge), the weights
+// e^(m_s - M) / Z go to LDS, and every thread sums 4 columns of s_next over
+// the slices.  Workgroup (r, 0) also writes the row's statistics.
+__global__ __launch_bounds__(256) void softmax_finish_kernel(const float4* sstat, int nslices, int rows, int T,
+                                                             const int32_t* stopped, const float* part, int d,
+                                                             bf16_t* out, float4* rowstat, const int32_t* flag) {
   if (flag && *flag) return;
-  const int r = blockIdx.y;
-  if (live && !live[r / T]) return;   // a canvas stopped before the step keeps its state
-  const float m = rowstat[r].x, iz = 1.0f / rowstat[r].y;
-  const long v = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (v >= V) return;
-  const float4 l = *reinterpret_cast<const float4*>(logits + r * ldl + v);
+  __shared__ float w[64];
+  const int r = blockIdx.x;
+  if (stopped && stopped[r / T]) return;
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const float4 mine = s < nslices ? sstat[(long)r * nslices + s]
+                                    : make_float4(-INFINITY, 0.f, 0.f, __int_as_float(0x7FFFFFFF));
+    float4 t = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      float4 y;
+      y.x = __shfl_xor(t.x, o, 64); y.y = __shfl_xor(t.y, o, 64); y.z = __shfl_xor(t.z, o, 64);
+      y.w = __shfl_xor(t.w, o, 64);
+      t = softmax_stats_merge(t, y);
+    }
+    if (s < nslices) w[s] = __expf(mine.x - t.x) / t.y;
+    if (s == 0 && blockIdx.y == 0) rowstat[r] = make_float4(t.x, t.y, logf(t.y) - t.z / t.y, t.w);
+  }
+  if (!out) return;
+  __syncthreads();
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;
+  if (c >= d) return;
+  const long n = (long)rows * d;
+  const float* pp = part + (long)r * d + c;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nslices; ++s) {
+    const float4 v = *reinterpret_cast<const float4*>(pp + s * n);
+    const float ws = w[s];
+    acc.x += ws * v.x; acc.y += ws * v.y; acc.z += ws * v.z; acc.w += ws * v.w;
+  }
   uint2 o;
-  o.x = (uint32_t)f2bf(__expf(l.x - m) * iz) | ((uint32_t)f2bf(__expf(l.y - m) * iz) << 16);
-  o.y = (uint32_t)f2bf(__expf(l.z - m) * iz) | ((uint32_t)f2bf(__expf(l.w - m) * iz) << 16);
-  *reinterpret_cast<uint2*>(P + (long)r * V + v) = o;
+  o.x = (uint32_t)f2bf(acc.x) | ((uint32_t)f2bf(acc.y) << 16);
+  o.y = (uint32_t)f2bf(acc.z) | ((uint32_t)f2bf(acc.w) << 16);
+  *reinterpret_cast<uint2*>(out + (long)r * d + c) = o;
 }
 
-hipError_t softmax_probs(const float* logits, const float4* rowstat, int rows, int V, long ldl, bf16_t* P,
-                         const int32_t* live, int T, const int32_t* flag, hipStream_t s) {
-  if (V % 4 != 0 || ldl % 4 != 0 || T < 1) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((V / 4 + 255) / 256), rows);
-  hipLaunchKernelGGL(probs_kernel, grid, dim3(256), 0, s, logits, rowstat, V, ldl, P, live, T, flag);
-  return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void reduce_soft_kernel(const float* part, int ksplit, int rows, int d,
-                                                          bf16_t* out, const int32_t* live, int T,
-                                                          const int32_t* flag) {
-  if (flag && *flag) return;
-  const long n = (long)rows * d;
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  if (live && !live[(i / d) / T]) return;   // a canvas stopped before this step keeps its state
-  float acc = 0.f;
-  for (int k = 0; k < ksplit; ++k) acc += part[k * n + i];
-  out[i] = f2bf(acc);
-}
-
-hipError_t reduce_soft_embed(const float* part, int ksplit, int rows, int d, bf16_t* out, const int32_t* live,
-                             int T, const int32_t* flag, hipStream_t s) {
-  if (T < 1) return hipErrorInvalidValue;
-  const long n = (long)rows * d;
-  hipLaunchKernelGGL(reduce_soft_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, ksplit, rows, d,
-                     out, live, T, flag);
+hipError_t softmax_finish(const float4* sstat, int nslices, int rows, int T, const int32_t* stopped,
+                          const float* part, int d, bf16_t* out, float4* rowstat, const int32_t* flag, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (nslices < 1 || nslices > 64 || T < 1 || d % 4) return hipErrorInvalidValue;
+  const dim3 grid(rows, out ? (d / 4 + 255) / 256 : 1);
+  hipLaunchKernelGGL(softmax_finish_kernel, grid, dim3(256), 0, s, sstat, nslices, rows, T, stopped, part, d, out,
+                     rowstat, flag);
   return hipGetLastError();
 }
 
