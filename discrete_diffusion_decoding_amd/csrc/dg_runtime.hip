@@ -560,7 +560,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       DG_CK(rmsnorm_rows(h, lw(m, l, m->lay.ffn_norm), R, D, d.rms_eps, xn2, xr, nullptr, opp, nullptr, ps.flag,
                          st));
     }
-    // shared FFN: independent of the routed path, so (outside profiling) it runs
+    // shared FFN: independent of the routed path, so it runs
     // on the side stream, forked here and joined before the combine.  Its
     // kernels are enqueued after the router's: a captured graph then keeps the
     // routed path (the critical one) on the main queue, and only the shared
@@ -569,7 +569,7 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
     Partials ysp{ys, 0, (long)R * D};
     bool forked = false;
     hipStream_t ss = st;
-    if (fs && !ns && !m->prof.on && side_stream(m)) {
+    if (fs && !ns && side_stream(m)) {
       DG_CK(hipEventRecord(m->ev_fork, st));
       ss = m->side;
       forked = true;
@@ -1003,10 +1003,13 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
                               nullptr, flag);
   sa.rowstat_in = rowstat;
   bool forked = false;
-  if (!m->prof.on && side_stream(m)) {
+  if (side_stream(m)) {
     DG_CK(hipEventRecord(m->ev_fork, st));
     DG_CK(hipStreamWaitEvent(m->side, m->ev_fork, 0));
-    DG_CK(sample_partial(sa, m->side));
+    {
+      ProfScope ps_(m, DG_PROF_SAMPLER, m->side);
+      DG_CK(sample_partial(sa, m->side));
+    }
     DG_CK(hipEventRecord(m->ev_join, m->side));
     forked = true;
   }

@@ -24,6 +24,8 @@
 // lgkmcnt[11:8]).
 #include "dg_kernels.hpp"
 
+#include <type_traits>
+
 namespace dg {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -31,6 +33,19 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // s_waitcnt immediate (gfx9 layout): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
 // vmcnt_hi[15:14]; only the vector-memory count is waited for.
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Cache policy of the weight loads.  A weight tile that one workgroup alone
+// reads is loaded non-temporal (the nt bit of the load's cache-policy operand):
+// the L2 then gives its lines up first and keeps the activation tiles, which
+// every weight tile of the product re-reads.  A tile that several row chunks
+// share (dense products over more rows than one tile, experts of several
+// chunks) keeps the default policy, so the chunks that follow hit in L2.
+constexpr int kPolicyStream = 2;
+#define DG_LDS_LOAD(SRC, DST, NT)                                                              \
+  do {                                                                                         \
+    if (NT) __builtin_amdgcn_global_load_lds((const void*)(SRC), (lds_void_t*)(DST), 16, 0, kPolicyStream); \
+    else __builtin_amdgcn_global_load_lds((const void*)(SRC), (lds_void_t*)(DST), 16, 0, 0);   \
+  } while (0)
 
 // ITEMS: rows come from the expert work list (grouped expert products);
 // otherwise dense rows in AR-row chunks.  AR: activation rows per tile (32 or
@@ -72,6 +87,7 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
   constexpr int NCOL = GEGLU ? BW / 2 : BW;   // output columns per tile
   const int ntiles = (g.N + NCOL - 1) / NCOL;
   int item, tile, zk;
+  bool wnt;
   if (ITEMS) {
     // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the actual
     // (item, tile) units, tile-major within an item, so the gathered
@@ -92,6 +108,7 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
       // of one XCD share each weight tile
       const int wv = g.items[item].w;
       const int ci = wv >> 16, ce = wv & 0xFFFF;
+      wnt = __builtin_amdgcn_readfirstlane(ce) == 1;
       if (ce > 1) {
         const long p = (long)ci * per + rest;
         item = item - ci + (int)(p % ce);
@@ -107,6 +124,7 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
     const long rest = bidx / g.items_max;
     tile = (int)(rest % ntiles);
     zk = (int)(rest / ntiles);
+    wnt = g.items_max == 1;
   }
 
   int grp, r0, nrows;
@@ -161,8 +179,9 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
 #define DG_ISSUE(S, ST)                                                                          \
   do {                                                                                           \
     const int co_ = (ST) << 6;                                                                   \
-    _Pragma("unroll") for (int j = 0; j < GPW; ++j)                                              \
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + co_), (lds_void_t*)&S[(wave + 4 * j) * 512], 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < GPW; ++j) {                                            \
+      DG_LDS_LOAD(src[j] + co_, &S[(wave + 4 * j) * 512], j >= AR / 32 && kNT);                 \
+    }                                                                                            \
   } while (0)
 
   // ---- MFMA operand reads ------------------------------------------------------
@@ -221,7 +240,10 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
   } while (0)
   bf16x8 af[2][NAF], bf[2][NBF];
 
-  if (nst > 0) {
+  // the pipeline is built twice, with and without the streaming policy on
+  // the weight loads (an immediate of the load instruction)
+  auto pipeline = [&](auto nt_tag) {
+    constexpr bool kNT = decltype(nt_tag)::value;
     DG_ISSUE(S0, 0);
     if (NS > 2) DG_ISSUE(S1, min(1, nst - 1));
     if (NS > 3) DG_ISSUE(S2, min(2, nst - 1));
@@ -266,6 +288,10 @@ __global__ __launch_bounds__(256, (gemm_wg_per_cu<AR, BW, NS>())) void gemm_kern
       if (s + 3 < nst) DG_TAIL(S3);
       if (s + 4 < nst) DG_TAIL(S4);
     }
+  };
+  if (nst > 0) {
+    if (wnt) pipeline(std::true_type{});
+    else pipeline(std::false_type{});
   }
 #undef DG_TAIL
 #undef DG_ISSUE
@@ -584,6 +610,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
   const int ke = min(g.K, kb + g.k_chunk);
   const int nst = (ke - kb) >> 6;
   if (nst <= 0) return;
+  const bool wnt = g.items_max == 1;   // each weight tile is read by this workgroup only
 
   // DMA: wave w moves A row groups 4w..4w+3 and B row groups 2w, 2w+1 (8 rows
   // each).  Addresses = wave-uniform base (advanced per stage, kept in SGPRs)
@@ -611,7 +638,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
       __builtin_amdgcn_global_load_lds((const void*)(ab_ + aoff[j]), (lds_void_t*)&S[dst_a + 512 * j], 16, 0, 0); \
     _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                          \
-      __builtin_amdgcn_global_load_lds((const void*)(bb_ + boff[j]), (lds_void_t*)&S[dst_b + 512 * j], 16, 0, 0); \
+      DG_LDS_LOAD(bb_ + boff[j], &S[dst_b + 512 * j], kNT);                                                \
   } while (0)
 
   const int lr = lane & 15, lg = lane >> 4;
@@ -659,6 +686,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
   } while (0)
   bf16x8 af[2][4], bfr[2][4];
 
+  auto pipeline = [&](auto nt_tag) {
+  constexpr bool kNT = decltype(nt_tag)::value;
   DG_FISSUE(S0, 0);
   DG_FISSUE(S1, min(1, nst - 1));
   int s = 0;
@@ -677,6 +706,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fat_kernel(GemmArgs g) {
   } while (0)
   if (s < nst) DG_FTAIL(S0);
   if (s + 1 < nst) DG_FTAIL(S1);
+  };
+  if (wnt) pipeline(std::true_type{});
+  else pipeline(std::false_type{});
 #undef DG_FTAIL
 #undef DG_FISSUE
 #undef DG_FREAD
@@ -733,6 +765,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
   const int ke = min(g.K, kb + g.k_chunk);
   const int nst = (ke - kb) >> 6;
   if (nst <= 0) return;
+  const bool wnt = g.items_max == 1;   // each weight tile is read by this workgroup only
 
   // DMA: wave w moves A row groups 4w..4w+3 and B row groups 4w..4w+3 (8 rows
   // each); wave-uniform bases advance per stage, per-lane byte offsets are fixed.
@@ -755,7 +788,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
       __builtin_amdgcn_global_load_lds((const void*)(ab_ + aoff[j]), (lds_void_t*)&S[dst_a + 512 * j], 16, 0, 0); \
     _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
-      __builtin_amdgcn_global_load_lds((const void*)(bb_ + boff[j]), (lds_void_t*)&S[dst_b + 512 * j], 16, 0, 0); \
+      DG_LDS_LOAD(bb_ + boff[j], &S[dst_b + 512 * j], kNT);                                                \
   } while (0)
 
   const int lr = lane & 15, lg = lane >> 4;
@@ -798,6 +831,8 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);                                                                     \
   } while (0)
 
+  auto pipeline = [&](auto nt_tag) {
+  constexpr bool kNT = decltype(nt_tag)::value;
   DG_F2ISSUE(S0, 0);
   DG_F2ISSUE(S1, min(1, nst - 1));
   int s = 0;
@@ -811,6 +846,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
     DG_F2HALF(S0, 0);
     DG_F2HALF(S0, 1);
   }
+  };
+  if (wnt) pipeline(std::true_type{});
+  else pipeline(std::false_type{});
   __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the loop
 #undef DG_F2ISSUE
 #undef DG_F2HALF

@@ -302,7 +302,10 @@ dg_status dg_transpose_bf16(const void* in, void* out, int64_t rows, int64_t col
  * (for measurement; adds event records to the stream while enabled).
  * dg_profile_enable(m, 1) clears the records and starts recording;
  * dg_profile_read waits for the recorded events and returns the summed
- * elapsed milliseconds and the number of launch groups of class `cls`. */
+ * elapsed milliseconds and the number of launch groups of class `cls`.
+ * Launches keep their streams while recording (the shared FFN and the
+ * Gumbel pass run on the side stream), so classes on the two streams overlap
+ * in time and their sums may exceed the step's wall time. */
 enum {
   DG_PROF_DENSE = 0,          /* QKV and O projections, self-conditioning projection */
   DG_PROF_ATTN = 1,           /* attention partials + merge                          */
