@@ -357,6 +357,10 @@ def main():
     torch.cuda.synchronize()
     edh = ed.cpu().numpy()
     touched = [len(np.unique(edh[l])) for l in range(m.n_layers)]
+    # 64-row work items of the grouped expert products per layer (an expert
+    # with c rows is cut into ceil(c / 64) chunks)
+    items = [int(sum((c + 63) // 64 for c in np.bincount(edh[l].ravel(), minlength=m.n_experts)))
+             for l in range(m.n_layers)]
 
     step_idx = 1
     for _ in range(args.warmup):
@@ -426,6 +430,7 @@ def main():
                 "kernel": "grouped expert gate/up GEMM (dg::gemm_kernel<4, true>)",
                 "bytes_per_launch": int(bytes_l), "avg_launch_ms": round(per_launch_ms, 4),
                 "rocprof_avg_launch_ms": rec.get("rocprof_avg_launch_ms"),
+                "rocprof_avg_launch_ms_graph_replays": rec.get("rocprof_avg_launch_ms_graph_replays"),
                 "kernel_source_sha256_16": kh}
 
     out = {
@@ -444,6 +449,7 @@ def main():
                           else "mfma", "alg_bytes": int(alg_b), "alg_flops": int(alg_f),
                           "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms_per_step, 4)},
         "touched_experts_per_layer": float(np.mean(touched)),
+        "touched_experts_by_layer": touched, "expert_items_by_layer": items,
         "kernel_ms": kernel_ms, "prefill_ms": round(prefill_ms, 2), "setup_s": round(setup_s, 1),
         "multi_block": multi, "ar_decode": ar,
     }

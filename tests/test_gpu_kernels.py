@@ -28,7 +28,8 @@ def _bf16(x):
 # chunks, ragged weight tiles and single-stage K.
 @pytest.mark.parametrize("M,N,K", [(1, 128, 64), (2, 200, 1536), (3, 136, 4096), (4, 72, 2816), (1, 8, 704),
                                    (37, 200, 192), (256, 2816, 2816), (300, 1024, 704),
-                                   (64, 8, 256), (192, 72, 64), (260, 200, 192), (513, 136, 320)])
+                                   (64, 8, 256), (192, 72, 64), (260, 200, 192), (513, 136, 320),
+                                   (256, 520, 384), (200, 300, 4096)])
 def test_gemm_matches_float64(M, N, K):
     announce(f"gemm M={M} N={N} K={K}")
     g = np.random.default_rng(M * 7 + N)
