@@ -37,6 +37,7 @@ struct GemmArgs {
   int ring;        // and its LDS ring depth (64 wide: 4 | 5; 128 wide: 2 | 3)
   int few_rows;    // work-list products: a bound (1..kGemvRows) on the rows of every item, when one is
                    // known (decoding); 0 otherwise.  Dense products use M.
+  int waves8;      // dense store products: the 8-wave tile kernel (two waves per SIMD)
   // GEMV work lists only: items of group >= grp_x read Wx (GEGLU up: Wx2) +
   // (group - grp_x) * wx_gstride, rows ldwx apart (the shared FFN's blocks as
   // extra experts); Wx == nullptr: none

@@ -354,6 +354,213 @@ static hipError_t launch_v(GemmArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Dense store products on 8 waves (two per SIMD).  With one workgroup of 4
+// waves per CU (the 256 tiles of a 256-row projection), a stage's LDS reads run
+// at the latency-bound rate of 4 waves and each SIMD's MFMA chains wait on
+// them; 8 waves read LDS faster and a SIMD's two waves overlap one's reads with
+// the other's MFMAs.  The waves form a 2 x 4 grid: wave w multiplies activation
+// rows (AR / 2) (w / 4) .. + AR / 2 - 1 by weight rows (BW / 4) (w % 4) ..
+// + BW / 4 - 1, so each wave reads half of the stage's activation tile and a
+// quarter of its weight tile.  Ring, swizzle, DMA and waits as gemm_kernel.
+template <int AR, int BW, int NS>
+constexpr int gemm8_wg_per_cu() {
+  return NS * (AR + BW) * 128 > 80 * 1024 ? 1 : 2;
+}
+
+template <int EPI, int AR, int BW, int NS>
+__global__ __launch_bounds__(512, (gemm8_wg_per_cu<AR, BW, NS>())) void gemm8_kernel(GemmArgs g) {
+  static_assert(EPI == EPI_STORE_BF16 || EPI == EPI_STORE_F32, "plain stores");
+  static_assert(AR == 64 || AR == 128, "activation tile of 64 or 128 rows");
+  static_assert(BW == 64 || BW == 128, "weight tile of 64 or 128 rows");
+  static_assert(NS >= 2 && NS <= 5, "ring of 2..5 stages");
+  constexpr int SE = (AR + BW) * 64;   // stage: AR activation rows then BW weight rows, 64 bf16 each
+  constexpr int NG = (AR + BW) / 8;    // 8-row groups per stage (one 1 KB DMA each)
+  constexpr int GPW = NG / 8;          // groups per wave
+  constexpr int NAF = AR / 32;         // activation fragments per wave (half the tile)
+  constexpr int WPW = BW / 4;          // weight rows per wave
+  constexpr int NBF = WPW / 16;        // weight fragments per wave
+  static_assert(NG % 8 == 0 && (AR / 8) % 8 == 0, "groups split evenly over 8 waves, activation groups first");
+  static_assert(NS * SE * 2 * gemm8_wg_per_cu<AR, BW, NS>() <= 160 * 1024, "the ring fits the LDS of a CU");
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[SE];
+  __shared__ __attribute__((aligned(1024))) bf16_t S2[NS > 2 ? SE : 1];
+  __shared__ __attribute__((aligned(1024))) bf16_t S3[NS > 3 ? SE : 1];
+  __shared__ __attribute__((aligned(1024))) bf16_t S4[NS > 4 ? SE : 1];
+  if (g.flag && *g.flag) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int ntiles = (g.N + BW - 1) / BW;
+  const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
+  if (bidx < 0) return;
+  const int item = (int)(bidx % g.items_max);
+  const long rest = bidx / g.items_max;
+  const int tile = (int)(rest % ntiles);
+  const int zk = (int)(rest / ntiles);
+  const bool wnt = g.items_max == 1;   // each weight tile is read by this workgroup only
+  const int r0 = item * AR;
+  const int nrows = min(AR, g.M - r0);
+  if (nrows <= 0) return;
+  const int n_base = tile * BW;
+  const int kb = zk * g.k_chunk;
+  const int ke = min(g.K, kb + g.k_chunk);
+  const int nst = (ke - kb) >> 6;
+
+  // DMA rows: wave w moves groups w, w + 8, ...; lane l fills LDS slot l % 8
+  // of row l / 8 of its group with global 16-byte part (l % 8) ^ (row % 8)
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int part = lslot ^ lrow;
+  const bf16_t* src[GPW];
+#pragma unroll
+  for (int j = 0; j < GPW; ++j) {
+    const int gi = wave + 8 * j;
+    if (j < AR / 64) {   // gi < AR / 8: activation rows
+      const int row = gi * 8 + lrow;
+      src[j] = g.A + (long)(r0 + min(row, nrows - 1)) * g.lda + kb + part * 8;
+    } else {
+      const int row = (gi - AR / 8) * 8 + lrow;
+      src[j] = g.W + (long)min(n_base + row, g.N - 1) * g.ldw + kb + part * 8;
+    }
+  }
+#define DG_ISSUE8(S, ST)                                                                         \
+  do {                                                                                           \
+    const int co_ = (ST) << 6;                                                                   \
+    _Pragma("unroll") for (int j = 0; j < GPW; ++j)                                              \
+      DG_LDS_LOAD(src[j] + co_, &S[(wave + 8 * j) * 512], j >= AR / 64 && kNT);                  \
+  } while (0)
+
+  const int lr = lane & 15, lg = lane >> 4;
+  int aoff[NAF], boff[NBF];
+#pragma unroll
+  for (int m = 0; m < NAF; ++m) {
+    const int arow = (AR / 2) * wm + 16 * m + lr;
+    aoff[m] = arow * 64;
+  }
+#pragma unroll
+  for (int n = 0; n < NBF; ++n) boff[n] = AR * 64 + (WPW * wn + 16 * n + lr) * 64;
+  floatx4 acc[NAF][NBF];
+#pragma unroll
+  for (int m = 0; m < NAF; ++m)
+#pragma unroll
+    for (int n = 0; n < NBF; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 af[2][NAF], bf[2][NBF];
+  // activation row (AR / 2) wm + 16 m + lr has row % 8 == lr % 8 (AR / 2 and 16 are multiples of 8)
+#define DG_READ8(S)                                                                              \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                \
+    const int p_ = 4 * j + lg;                                                                   \
+    _Pragma("unroll") for (int n = 0; n < NBF; ++n)                                              \
+      bf[j][n] = *reinterpret_cast<const bf16x8*>(&S[boff[n] + ((p_ ^ (lr & 7)) << 3)]);         \
+    _Pragma("unroll") for (int m = 0; m < NAF; ++m)                                              \
+      af[j][m] = *reinterpret_cast<const bf16x8*>(&S[aoff[m] + ((p_ ^ (lr & 7)) << 3)]);         \
+  }
+#define DG_MMA8()                                                                                \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
+    _Pragma("unroll") for (int m = 0; m < NAF; ++m)                                              \
+      _Pragma("unroll") for (int n = 0; n < NBF; ++n) acc[m][n] = mfma16x16x32(af[j][m], bf[j][n], acc[m][n]);
+#define DG_ITER8(SI, CUR, NXT)                                                                   \
+  do {                                                                                           \
+    const int s_ = (SI);                                                                         \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * GPW));                                      \
+    __builtin_amdgcn_s_barrier();                                                                \
+    DG_READ8(CUR);                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    DG_ISSUE8(NXT, min(s_ + NS - 1, nst - 1));                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                           \
+    DG_MMA8();                                                                                   \
+  } while (0)
+#define DG_TAIL8(CUR)                                                                            \
+  do {                                                                                           \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                                   \
+    __builtin_amdgcn_s_barrier();                                                                \
+    DG_READ8(CUR);                                                                               \
+    DG_MMA8();                                                                                   \
+  } while (0)
+  auto pipeline = [&](auto nt_tag) {
+    constexpr bool kNT = decltype(nt_tag)::value;
+    DG_ISSUE8(S0, 0);
+    if (NS > 2) DG_ISSUE8(S1, min(1, nst - 1));
+    if (NS > 3) DG_ISSUE8(S2, min(2, nst - 1));
+    if (NS > 4) DG_ISSUE8(S3, min(3, nst - 1));
+    int s = 0;
+    if (NS == 2) {
+      for (; s + 2 <= nst; s += 2) {
+        DG_ITER8(s, S0, S1); DG_ITER8(s + 1, S1, S0);
+      }
+      if (s < nst) DG_TAIL8(S0);
+    } else if (NS == 3) {
+      for (; s + 3 <= nst; s += 3) {
+        DG_ITER8(s, S0, S2); DG_ITER8(s + 1, S1, S0); DG_ITER8(s + 2, S2, S1);
+      }
+      if (s < nst) DG_TAIL8(S0);
+      if (s + 1 < nst) DG_TAIL8(S1);
+    } else if (NS == 4) {
+      for (; s + 4 <= nst; s += 4) {
+        DG_ITER8(s, S0, S3); DG_ITER8(s + 1, S1, S0); DG_ITER8(s + 2, S2, S1); DG_ITER8(s + 3, S3, S2);
+      }
+      if (s < nst) DG_TAIL8(S0);
+      if (s + 1 < nst) DG_TAIL8(S1);
+      if (s + 2 < nst) DG_TAIL8(S2);
+    } else {
+      for (; s + 5 <= nst; s += 5) {
+        DG_ITER8(s, S0, S4); DG_ITER8(s + 1, S1, S0); DG_ITER8(s + 2, S2, S1); DG_ITER8(s + 3, S3, S2);
+        DG_ITER8(s + 4, S4, S3);
+      }
+      if (s < nst) DG_TAIL8(S0);
+      if (s + 1 < nst) DG_TAIL8(S1);
+      if (s + 2 < nst) DG_TAIL8(S2);
+      if (s + 3 < nst) DG_TAIL8(S3);
+    }
+  };
+  if (nst > 0) {
+    if (wnt) pipeline(std::true_type{});
+    else pipeline(std::false_type{});
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the loop
+#undef DG_TAIL8
+#undef DG_ISSUE8
+#undef DG_READ8
+#undef DG_MMA8
+#undef DG_ITER8
+
+#pragma unroll
+  for (int n = 0; n < NBF; ++n) {
+    const int col = n_base + WPW * wn + 16 * n + lr;
+    if (col >= g.N) continue;
+#pragma unroll
+    for (int m = 0; m < NAF; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = (AR / 2) * wm + 16 * m + 4 * lg + i;
+        if (rl >= nrows) continue;
+        const long off = (long)(r0 + rl) * g.ldc + col;
+        if (EPI == EPI_STORE_BF16) reinterpret_cast<bf16_t*>(g.C)[off] = f2bf(acc[m][n][i]);
+        else reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = acc[m][n][i];
+      }
+    }
+  }
+}
+
+template <int EPI, int AR, int BW, int NS>
+static hipError_t launch_v8(GemmArgs a, hipStream_t s) {
+  a.items_max = (a.M + AR - 1) / AR;
+  const long total = (long)a.items_max * ((a.N + BW - 1) / BW) * a.k_split;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm8_kernel<EPI, AR, BW, NS>), dim3(xcd_grid(total)), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int EPI>
+static hipError_t launch8(const GemmArgs& a, hipStream_t s) {
+  switch (a.tile_rows * 10000 + a.tile_cols * 10 + a.ring) {
+    case 640644: return launch_v8<EPI, 64, 64, 4>(a, s);
+    case 641283: return launch_v8<EPI, 64, 128, 3>(a, s);
+    case 1280643: return launch_v8<EPI, 128, 64, 3>(a, s);
+    case 1281283: return launch_v8<EPI, 128, 128, 3>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 // variant chosen by the caller: a.tile_rows (activation rows), a.tile_cols
 // (weight rows), a.ring (LDS ring depth)
 template <int EPI, bool ITEMS>
@@ -567,6 +774,13 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s) {
       case EPI_GEGLU_BF16: return it ? gemv_rows<EPI_GEGLU_BF16, true>(a, few, s) : gemv_rows<EPI_GEGLU_BF16, false>(a, few, s);
     }
     return hipErrorInvalidValue;
+  }
+  if (a.waves8 && !it) {
+    switch (epi) {
+      case EPI_STORE_BF16: return launch8<EPI_STORE_BF16>(a, s);
+      case EPI_STORE_F32: return launch8<EPI_STORE_F32>(a, s);
+      default: return hipErrorInvalidValue;
+    }
   }
   switch (epi) {
     case EPI_STORE_BF16: return it ? launch<EPI_STORE_BF16, true>(a, s) : launch<EPI_STORE_BF16, false>(a, s);
