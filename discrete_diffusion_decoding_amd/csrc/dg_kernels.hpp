@@ -56,6 +56,8 @@ hipError_t gemm(int epi, const GemmArgs& a, hipStream_t s);
 // ceil(M / 256)); epilogues EPI_STORE_F32 (split-K partials) and EPI_STORE_BF16
 hipError_t gemm_fat(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s);
+// C [M][N] fp32 split-K partials = A [M][K] W [K][N] (W K-major), 256 x 256 tiles
+hipError_t gemm_kn(const GemmArgs& a, hipStream_t s);
 constexpr int kFatRowChunk = 256;
 // the 256-row kernel addresses a tile with 32-bit byte offsets from its first row
 inline bool gemm_fat_pitch_ok(long lda, long ldw) {
@@ -201,6 +203,5 @@ hipError_t init_canvas(int32_t* tokens, int B, int T, int V, const uint64_t* see
 hipError_t fill_i32(int32_t* p, int32_t v, long n, hipStream_t s);
 hipError_t fill_u16(uint16_t* p, uint16_t v, long n, hipStream_t s);
 hipError_t set_step(int32_t* steps, const int32_t* stopped, int B, int step, hipStream_t s);
-hipError_t transpose_bf16(const bf16_t* in, bf16_t* out, long rows, long cols, hipStream_t s);
 
 }  // namespace dg

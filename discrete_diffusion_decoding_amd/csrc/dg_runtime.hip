@@ -172,7 +172,7 @@ extern "C" dg_status dg_model_create(const dg_model_desc* d, const dg_weights* w
   if (st != DG_OK) return st;
   if (!w || !out || !w->layers) return DG_ERR_ARG;
   if (d->vocab && (!w->embed || !w->final_norm)) return DG_ERR_ARG;
-  if (d->self_cond && (!w->self_cond_w || !w->self_cond_gate || !w->embed_t)) return DG_ERR_ARG;
+  if (d->self_cond && (!w->self_cond_w || !w->self_cond_gate)) return DG_ERR_ARG;
   for (int l = 0; l < d->n_layers; ++l)
     if (!w->layers[l]) return DG_ERR_ARG;
   dg_model* m = new dg_model();
@@ -253,13 +253,12 @@ static int choose_ksplit(long tiles_times_items, int K, int max_split, int* k_ch
 static const int kFatMinRows = 192;
 static bool fat_rows(int rows) { return rows >= kFatMinRows; }
 
-// Soft-embedding product (K = vocab): split so that ~256 (256-row tiles, one
-// per CU) or ~1024 (64-row tiles) workgroups share the contraction.
+// Soft-embedding product (K = vocab, 256 x 256 tiles of the K-major kernel):
+// split so that ~256 workgroups (one per CU, at most one round) share the
+// contraction.
 static void soft_split(const dg_model_desc& d, int rows, int* ksplit, int* kchunk) {
-  const bool fat = fat_rows(rows);
-  const int items = fat ? cdiv(d.d_model, 256) * cdiv(rows, kFatRowChunk) : cdiv(d.d_model, 64) * cdiv(rows, 64);
-  // 256 x 256 tiles run one workgroup per CU: at most one round of 256
-  int ks = std::max(1, std::min(32, fat ? 256 / items : cdiv(1024, items)));
+  const int items = cdiv(d.d_model, 256) * cdiv(rows, 256);
+  int ks = std::max(1, std::min(32, 256 / items));
   int kc = cdiv(cdiv(d.vocab, ks), 64) * 64;
   *kchunk = kc;
   *ksplit = cdiv(d.vocab, kc);
@@ -1027,11 +1026,12 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     DG_CK(softmax_slices(logits, V, R, V, p.kchunk, p.ksplit, T, c->stopped, P_, sstat, flag, st));
     float* part = nullptr;
     if (d.self_cond) {
+      // s_next partials per vocabulary slice: P~ [R][V] times E [V][d] as stored
       GemmArgs g = gargs();
-      g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed_t; g.ldw = V; g.K = V; g.N = D; g.k_chunk = p.kchunk;
+      g.A = P_; g.lda = V; g.W = (const bf16_t*)m->w.embed; g.ldw = D; g.K = V; g.N = D; g.k_chunk = p.kchunk;
       g.k_split = p.ksplit; g.C = at<float>(ws, p.separt); g.ldc = D;
-      g.c_kstride = (long)R * D; g.flag = flag;
-      DG_CK(dense_gemm(EPI_STORE_F32, g, R, st));
+      g.c_kstride = (long)R * D; g.flag = flag; g.M = R; g.items_max = cdiv(R, 256);
+      DG_CK(gemm_kn(g, st));
       part = at<float>(ws, p.separt);
     }
     DG_CK(softmax_finish(sstat, p.ksplit, R, T, c->stopped, part, D, (bf16_t*)c->self_cond, rowstat, flag, st));
@@ -1242,9 +1242,15 @@ extern "C" dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int
   return DG_OK;
 }
 
-extern "C" dg_status dg_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, dg_stream_t stream) {
-  if (!in || !out || rows < 1 || cols < 1) return DG_ERR_ARG;
-  DG_CK(transpose_bf16((const bf16_t*)in, (bf16_t*)out, rows, cols, (hipStream_t)stream));
+extern "C" dg_status dg_gemm_bf16_kn(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t M, int32_t N,
+                                     int32_t K, float* Cm, int64_t ldc, dg_stream_t stream) {
+  if (!A || !W || !Cm || M < 1 || N < 1 || K < 1 || lda < K || ldw < N || ldc < N) return DG_ERR_ARG;
+  if (K % 64 || N % 8 || lda % 8 || ldw % 8) return DG_ERR_SHAPE;
+  if (256L * lda * 2 >= 0x7FFFFFFFL || (64L * ldw + N) * 2 >= 0x7FFFFFFFL) return DG_ERR_SHAPE;
+  GemmArgs g = gargs();
+  g.A = (const bf16_t*)A; g.lda = lda; g.W = (const bf16_t*)W; g.ldw = ldw; g.K = K; g.N = N; g.k_chunk = K;
+  g.C = Cm; g.ldc = ldc; g.M = M; g.items_max = cdiv(M, 256);
+  DG_CK(gemm_kn(g, (hipStream_t)stream));
   return DG_OK;
 }
 

@@ -823,26 +823,4 @@ hipError_t fill_u16(uint16_t* p, uint16_t v, long n, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void transpose_kernel(const bf16_t* in, bf16_t* out, long rows, long cols) {
-  __shared__ bf16_t tile[32][33];
-  const long c0 = (long)blockIdx.x * 32, r0 = (long)blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int j = ty; j < 32; j += 8) {
-    const long r = r0 + j, c = c0 + tx;
-    if (r < rows && c < cols) tile[j][tx] = in[r * cols + c];
-  }
-  __syncthreads();
-  for (int j = ty; j < 32; j += 8) {
-    const long c = c0 + j, r = r0 + tx;
-    if (r < rows && c < cols) out[c * rows + r] = tile[tx][j];
-  }
-}
-
-hipError_t transpose_bf16(const bf16_t* in, bf16_t* out, long rows, long cols, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
-  hipLaunchKernelGGL(transpose_kernel, grid, dim3(256), 0, s, in, out, rows, cols);
-  return hipGetLastError();
-}
-
 }  // namespace dg

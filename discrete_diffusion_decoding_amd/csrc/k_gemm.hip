@@ -1086,6 +1086,184 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// C [M][N] (fp32; k slice zk at C + zk c_kstride) = A [M][K] W [K][N], the weight
+// stored K-major (rows of N contiguous values): the soft-prediction product
+// reads the tied embedding E [vocab][d] as stored, contracting over the
+// vocabulary, so no transposed copy of E is needed.  Square 256 x 256 tiles
+// and waves as gemm_fat2_kernel; the weight part of a stage is 64 rows of W
+// (k) x 256 columns (n), 512 bytes per row, whose 16-byte slots are XOR-
+// swizzled by 2 (k % 16).  The MFMA B operand (8 consecutive k of one column
+// per lane) comes from two transposed LDS reads (ds_read_b64_tr_b16): within
+// each 16 lanes, lane 4a + b receives element b of the 8-byte reads of lanes
+// a, a + 4, a + 8, a + 12, so lane 4a + j of 16-lane group G reads row
+// 8 G + j (then 8 G + 4 + j) at column 4 a of the fragment's 16: lane t ends
+// up with column t and rows 8 G .. 8 G + 7, the k-slots of the A operand's
+// 16-byte reads.  The eight rows of 32 lanes map to eight distinct slot pairs
+// of the 512-byte rows, so the reads are bank-conflict-free.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ int kn_swz(int row) { return 2 * (row & 15); }
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_kn_kernel(GemmArgs g) {
+  static_assert(EPI == EPI_STORE_F32, "split-K partials");
+  __shared__ __attribute__((aligned(1024))) bf16_t S0[kFat2Stage];
+  __shared__ __attribute__((aligned(1024))) bf16_t S1[kFat2Stage];
+  if (g.flag && *g.flag) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntiles = (g.N + 255) / 256;
+  const long bidx = xcd_logical_block((long)g.items_max * ntiles * g.k_split);
+  if (bidx < 0) return;
+  const int item = (int)(bidx % g.items_max);
+  const long rest = bidx / g.items_max;
+  const int tile = (int)(rest % ntiles);
+  const int zk = (int)(rest / ntiles);
+  const int r0 = item * 256;
+  const int nrows = min(256, g.M - r0);
+  if (nrows <= 0) return;
+  const int n_base = tile * 256;
+  const int kb = zk * g.k_chunk;
+  const int ke = min(g.K, kb + g.k_chunk);
+  const int nst = (ke - kb) >> 6;
+  if (nst <= 0) return;
+  const bool wnt = g.items_max == 1;   // each weight tile is read by this workgroup only
+
+  // DMA.  A: wave w moves row groups 4w..4w+3 (8 rows of 128 B each, as
+  // gemm_fat2_kernel).  W: wave w moves W rows 8w .. 8w + 7, two per
+  // instruction (lane l: row + l / 32, LDS slot l % 32 holding global part
+  // (l % 32) ^ kn_swz(row), clamped to the last 16 bytes of the row); a stage
+  // advances 64 rows of W.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int part = lslot ^ lrow;
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * wave + j) * 8 + lrow;   // 0..255
+    aoff[j] = (int)(((long)min(row, nrows - 1) * g.lda + part * 8) * 2);
+    const int wr = 8 * wave + 2 * j + (lane >> 5);   // 0..63
+    const int col = min(n_base + 8 * ((lane & 31) ^ kn_swz(wr)), g.N - 8);
+    boff[j] = (int)(((long)wr * g.ldw + col) * 2);
+  }
+  const char* abase = reinterpret_cast<const char*>(g.A + (long)r0 * g.lda + kb);
+  const char* bbase = reinterpret_cast<const char*>(g.W + (long)kb * g.ldw);
+  const long bstep = (long)64 * g.ldw * 2;   // bytes per stage of W rows
+  const int dst_a = (4 * wave) * 512, dst_b = kFat2A + (8 * wave) * 256;
+#define DG_KNISSUE(S, ST)                                                                                  \
+  do {                                                                                                     \
+    const char* ab_ = abase + ((long)(ST) << 7);                                                           \
+    const char* bb_ = bbase + (long)(ST) * bstep;                                                          \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
+      __builtin_amdgcn_global_load_lds((const void*)(ab_ + aoff[j]), (lds_void_t*)&S[dst_a + 512 * j], 16, 0, 0); \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                          \
+      DG_LDS_LOAD(bb_ + boff[j], &S[dst_b + 512 * j], kNT);                                                \
+  } while (0)
+
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wn = wave & 3, wm = wave >> 2;
+  // transposed B reads: lane 4 a + jr of group lg reads row 8 lg + jr (+ 4) at column 4 a
+  const int ta = lr & 3, tj = lr >> 2;
+  int bcol[4];   // element offset of this lane's 8-byte read within a W row, per 16-column block
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int c = 64 * wn + 16 * n + 4 * ta;
+    bcol[n] = c;   // part c / 8, half (c % 8) / 4
+  }
+  floatx4 acc[8][4];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 af[8], bfr[4];
+#define DG_KNB(S, ROW, C)                                                                                  \
+  __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                                                 \
+      (lds_v4i16_t*)&S[kFat2A + (ROW) * 256 + ((((C) >> 3) ^ kn_swz(ROW)) << 3) + ((C) & 4)])
+#define DG_KNHALF(S, J)                                                                                    \
+  do {                                                                                                     \
+    const int p_ = 4 * (J) + lg;                                                                           \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                                        \
+      const int arow = 128 * wm + 16 * m + lr;                                                             \
+      af[m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);                  \
+    }                                                                                                      \
+    const int r0_ = 32 * (J) + 8 * lg + tj;                                                                \
+    _Pragma("unroll") for (int n = 0; n < 4; ++n) {                                                        \
+      const v4i16_t lo_ = DG_KNB(S, r0_, bcol[n]);                                                         \
+      const v4i16_t hi_ = DG_KNB(S, r0_ + 4, bcol[n]);                                                     \
+      const v8i16_t both_ = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                    \
+      bfr[n] = __builtin_bit_cast(bf16x8, both_);                                                          \
+    }                                                                                                      \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m)                                                          \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bfr[n], acc[m][n]);    \
+  } while (0)
+#define DG_KNITER(SI, CUR)                                                                                 \
+  do {                                                                                                     \
+    const int s_ = (SI);                                                                                   \
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                                                             \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    DG_KNHALF(CUR, 0);                                                                                     \
+    DG_KNHALF(CUR, 1);                                                                                     \
+    __builtin_amdgcn_s_waitcnt(0xC07F);   /* lgkmcnt(0): this wave's reads of CUR are done */              \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+    DG_KNISSUE(CUR, min(s_ + 2, nst - 1));                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                                     \
+  } while (0)
+
+  auto pipeline = [&](auto nt_tag) {
+    constexpr bool kNT = decltype(nt_tag)::value;
+    DG_KNISSUE(S0, 0);
+    DG_KNISSUE(S1, min(1, nst - 1));
+    int s = 0;
+    for (; s + 2 <= nst; s += 2) {
+      DG_KNITER(s, S0);
+      DG_KNITER(s + 1, S1);
+    }
+    if (s < nst) {   // odd count: the last stage sits in S0; drain the ring
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      __builtin_amdgcn_s_barrier();
+      DG_KNHALF(S0, 0);
+      DG_KNHALF(S0, 1);
+    }
+  };
+  if (wnt) pipeline(std::true_type{});
+  else pipeline(std::false_type{});
+  __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the loop
+#undef DG_KNISSUE
+#undef DG_KNB
+#undef DG_KNHALF
+#undef DG_KNITER
+
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = n_base + 64 * wn + 16 * n + lr;
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 128 * wm + 16 * m + 4 * lg + i;
+        if (rl >= nrows) continue;
+        const long off = (long)(r0 + rl) * g.ldc + col;
+        reinterpret_cast<float*>(g.C)[(long)zk * g.c_kstride + off] = acc[m][n][i];
+      }
+    }
+  }
+}
+
+hipError_t gemm_kn(const GemmArgs& a, hipStream_t s) {
+  if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
+  if (a.lda % 8 != 0 || a.ldw % 8 != 0 || a.N % 8 != 0 || a.N < 8 || a.items || a.a_rows) return hipErrorInvalidValue;
+  // 32-bit per-lane offsets: 256 rows of A, 64 rows of W
+  if (256L * a.lda * 2 >= 0x7FFFFFFFL || (64L * a.ldw + a.N) * 2 >= 0x7FFFFFFFL) return hipErrorInvalidValue;
+  const long total = (long)a.items_max * ((a.N + 255) / 256) * a.k_split;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_kn_kernel<EPI_STORE_F32>, dim3(xcd_grid(total)), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t gemm_fat2(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.K % 64 != 0 || a.k_chunk % 64 != 0 || a.k_split < 1 || a.items_max < 1) return hipErrorInvalidValue;
   if (a.lda % 8 != 0 || a.ldw % 8 != 0 || a.items || a.a_rows) return hipErrorInvalidValue;

@@ -49,14 +49,10 @@ class DeviceModel:
             t = _dev_u16(arr.size, device)
             _upload(t, arr)
             self.glob[name] = t
-        if shape.self_cond:
-            et = _dev_u16(shape.vocab * shape.d_model, device)
-            dg.dg_transpose_bf16(self.glob["embed"], et, shape.vocab, shape.d_model)
-            self.glob["embed_t"] = et
         torch.cuda.synchronize()
         self._layer_ptrs = (C.c_void_p * shape.n_layers)(*[t.data_ptr() for t in self.layers])
         w = dg.Weights()
-        for name in ("embed", "embed_t", "final_norm", "self_cond_w", "self_cond_gate"):
+        for name in ("embed", "final_norm", "self_cond_w", "self_cond_gate"):
             setattr(w, name, self.glob[name].data_ptr() if name in self.glob else None)
         w.layers = C.cast(self._layer_ptrs, C.POINTER(C.c_void_p))
         self._w = w

@@ -37,7 +37,7 @@ class LayerLayout(C.Structure):
 
 
 class Weights(C.Structure):
-    _fields_ = [("embed", C.c_void_p), ("embed_t", C.c_void_p), ("final_norm", C.c_void_p),
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p),
                 ("self_cond_w", C.c_void_p), ("self_cond_gate", C.c_void_p),
                 ("layers", C.POINTER(C.c_void_p))]
 
@@ -91,8 +91,8 @@ def lib():
             "dg_sample_noalloc_max_bytes": (sz, []),
             "dg_sample_logits_noalloc": (st, [vp, i32, i32, i32, C.POINTER(Canvas), i32, C.POINTER(Sampler), vp]),
             "dg_init_canvas": (st, [vp, C.POINTER(Canvas), i32, i32, C.POINTER(C.c_uint64), vp]),
-            "dg_transpose_bf16": (st, [vp, vp, C.c_int64, C.c_int64, vp]),
             "dg_gemm_bf16": (st, [vp, C.c_int64, vp, C.c_int64, i32, i32, i32, vp, C.c_int64, vp]),
+            "dg_gemm_bf16_kn": (st, [vp, C.c_int64, vp, C.c_int64, i32, i32, i32, vp, C.c_int64, vp]),
             "dg_profile_enable": (st, [vp, i32]),
             "dg_set_graphs": (st, [vp, i32]),
             "dg_profile_read": (st, [vp, i32, C.POINTER(C.c_double), C.POINTER(C.c_int32)]),
@@ -244,8 +244,9 @@ def dg_init_canvas(h, canvas: Canvas, B, T, seeds, stream=None):
     _ck(lib().dg_init_canvas(h, C.byref(canvas), B, T, arr, _stream(stream)), "dg_init_canvas")
 
 
-def dg_transpose_bf16(src, dst, rows, cols, stream=None):
-    _ck(lib().dg_transpose_bf16(_ptr(src), _ptr(dst), rows, cols, _stream(stream)), "dg_transpose_bf16")
+def dg_gemm_bf16_kn(A, W, Cout, M, N, K, lda=None, ldw=None, ldc=None, stream=None):
+    _ck(lib().dg_gemm_bf16_kn(_ptr(A), lda or K, _ptr(W), ldw or N, M, N, K, _ptr(Cout), ldc or N,
+                              _stream(stream)), "dg_gemm_bf16_kn")
 
 
 def dg_gemm_bf16(A, W, Cout, M, N, K, lda=None, ldw=None, ldc=None, stream=None):

@@ -84,15 +84,14 @@ typedef struct {
   size_t total;
 } dg_layer_layout;
 
-/* Device weights (bf16).  embed [vocab][d] is the tied input embedding and LM
- * head; embed_t [d][vocab] its transpose (read by the soft-prediction
- * embedding; required when self_cond == 1, see dg_transpose_bf16);
- * final_norm [d]; self_cond_w [d][d]; self_cond_gate [d].  layers is a HOST
- * array of n_layers device pointers, each to a block laid out as
- * dg_layer_layout.  The pointers are borrowed until dg_model_destroy. */
+/* Device weights (bf16).  embed [vocab][d] is the tied input embedding, the
+ * LM head and (read as stored, contracting over the vocabulary) the matrix of
+ * the soft-prediction embedding; final_norm [d]; self_cond_w [d][d];
+ * self_cond_gate [d].  layers is a HOST array of n_layers device pointers,
+ * each to a block laid out as dg_layer_layout.  The pointers are borrowed
+ * until dg_model_destroy. */
 typedef struct {
   const void* embed;
-  const void* embed_t;
   const void* final_norm;
   const void* self_cond_w;
   const void* self_cond_gate;
@@ -295,8 +294,16 @@ dg_status dg_init_canvas(const dg_model* m, dg_canvas* canvas, int32_t B, int32_
 dg_status dg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t M, int32_t N, int32_t K,
                        float* C, int64_t ldc, dg_stream_t stream);
 
-/* out [cols][rows] = in [rows][cols]^T (bf16), e.g. embed -> embed_t. */
-dg_status dg_transpose_bf16(const void* in, void* out, int64_t rows, int64_t cols, dg_stream_t stream);
+/* C fp32 [M][N] (row pitch ldc) = A [M][K] (bf16, pitch lda) times W [K][N]
+ * (bf16, pitch ldw: the weight stored K-major, N values per row), the product
+ * the soft-prediction embedding forms with the tied embedding E [vocab][d] as
+ * stored (K = vocabulary, N = d).  256 x 256 tiles; the B operand is read
+ * from LDS with gfx950 transposed loads.  K a multiple of 64; N, lda and ldw
+ * multiples of 8; 256 lda and 64 ldw + N under 2^30 elements; else
+ * DG_ERR_SHAPE before any device work. */
+dg_status dg_gemm_bf16_kn(const void* A, int64_t lda, const void* W, int64_t ldw, int32_t M, int32_t N, int32_t K,
+                          float* C, int64_t ldc, dg_stream_t stream);
+
 
 /* Timing of kernel classes with HIP events recorded around their launches
  * (for measurement; adds event records to the stream while enabled).

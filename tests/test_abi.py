@@ -52,7 +52,7 @@ def test_layer_layout_matches_tensor_specs(shape):
 
 def _fake_weights(shape):
     ptrs = (C.c_void_p * shape.n_layers)(*([0x1000] * shape.n_layers))
-    w = dg.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, C.cast(ptrs, C.POINTER(C.c_void_p)))
+    w = dg.Weights(0x1000, 0x1000, 0x1000, 0x1000, C.cast(ptrs, C.POINTER(C.c_void_p)))
     return w, ptrs
 
 
@@ -71,7 +71,7 @@ def test_model_create_validates_shapes():
         with pytest.raises(dg.DgError) as e:
             dg.dg_model_create(s, w)
         assert e.value.status == dg.DG_ERR_SHAPE
-    w0 = dg.Weights(None, None, None, None, None, C.cast(keep, C.POINTER(C.c_void_p)))
+    w0 = dg.Weights(None, None, None, None, C.cast(keep, C.POINTER(C.c_void_p)))
     with pytest.raises(dg.DgError) as e:
         dg.dg_model_create(TINY, w0)
     assert e.value.status == dg.DG_ERR_ARG
@@ -162,6 +162,12 @@ def test_gemm_rejects_bad_shapes_before_any_device_work():
     assert L.dg_gemm_bf16(p, 132, p, 128, 256, 64, 128, p, 64, None) == dg.DG_ERR_SHAPE
     assert L.dg_gemm_bf16(p, 128, p, 130, 8, 64, 128, p, 64, None) == dg.DG_ERR_SHAPE
     assert L.dg_gemm_bf16(p, 64, p, 128, 8, 64, 128, p, 64, None) == dg.DG_ERR_ARG   # lda < K
+    # K-major weights: W [K][N]
+    assert L.dg_gemm_bf16_kn(p, 96, p, 64, 256, 64, 96, p, 64, None) == dg.DG_ERR_SHAPE   # K % 64
+    assert L.dg_gemm_bf16_kn(p, 128, p, 68, 256, 68, 128, p, 68, None) == dg.DG_ERR_SHAPE  # N % 8
+    assert L.dg_gemm_bf16_kn(p, 132, p, 64, 256, 64, 128, p, 64, None) == dg.DG_ERR_SHAPE  # lda % 8
+    assert L.dg_gemm_bf16_kn(p, 128, p, 56, 8, 64, 128, p, 64, None) == dg.DG_ERR_ARG      # ldw < N
+    assert L.dg_gemm_bf16_kn(p, 128, p, 64, 8, 64, 128, p, 32, None) == dg.DG_ERR_ARG      # ldc < N
 
 
 def test_sample_noalloc_rejects_bad_arguments_before_any_device_work():

@@ -43,6 +43,24 @@ def test_gemm_matches_float64(M, N, K):
     assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max() + 1e-6
 
 
+# The K-major product (the soft-prediction embedding's E [vocab][d] as stored):
+# ragged rows (one and several 256-row items), ragged 256-wide column tiles
+# (N a multiple of 8), one and many 64-row K stages, odd and even stage counts.
+@pytest.mark.parametrize("M,N,K", [(256, 2816, 704), (37, 200, 64), (300, 264, 192), (513, 520, 4096),
+                                   (256, 256, 2048), (64, 8, 320)])
+def test_gemm_kmajor_matches_float64(M, N, K):
+    announce(f"gemm K-major M={M} N={N} K={K}")
+    g = np.random.default_rng(M * 11 + N)
+    A = _bf16(g.standard_normal((M, K)).astype(np.float32))
+    W = _bf16((0.05 * g.standard_normal((K, N))).astype(np.float32))
+    out = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    dg.dg_gemm_bf16_kn(dev(A.view(np.int16)), dev(W.view(np.int16)), out, M, N, K)
+    ref = synth.bf16_bits_to_f32(A).astype(np.float64) @ synth.bf16_bits_to_f32(W).astype(np.float64)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max() + 1e-6
+
+
 def _canvas(B, T, V):
     st = {
         "tokens": torch.zeros(B, T, dtype=torch.int32, device="cuda"),
@@ -157,7 +175,7 @@ def test_init_canvas_bit_exact():
     st = _canvas(B, T, TINY.vocab)
     # dg_init_canvas needs only the vocabulary of a model: use a handle on fake weights
     ptrs = (C.c_void_p * TINY.n_layers)(*([0x1000] * TINY.n_layers))
-    w = dg.Weights(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, C.cast(ptrs, C.POINTER(C.c_void_p)))
+    w = dg.Weights(0x1000, 0x1000, 0x1000, 0x1000, C.cast(ptrs, C.POINTER(C.c_void_p)))
     h = dg.dg_model_create(TINY, w)
     st["stopped"].fill_(1)
     dg.dg_init_canvas(h, dg.make_canvas(st), B, T, seeds)
