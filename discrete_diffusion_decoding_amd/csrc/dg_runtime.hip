@@ -972,6 +972,9 @@ static dg_status step_impl(dg_model* m, const void* kv, int Bp, int P, int P_max
     g.ring = m->d_ring;
     g.A = (const bf16_t*)c->self_cond; g.lda = D; g.W = (const bf16_t*)m->w.self_cond_w; g.ldw = D; g.K = D;
     g.N = D; dense_rows(g, R);
+    if (R >= kWaves8MinRows) {   // as the O projection: 128-row tiles on the 8-wave kernel
+      g.tile_rows = 128; g.ring = 3; g.items_max = cdiv(R, 128); g.waves8 = 1;
+    }
     g.k_split = choose_ksplit((long)g.items_max * cdiv(D, 64), D, kMaxDenseSplit, &g.k_chunk);
     scp.n = g.k_split;
     g.C = at<float>(ws, p.dpart); g.ldc = D; g.c_kstride = (long)R * D; g.flag = flag;
