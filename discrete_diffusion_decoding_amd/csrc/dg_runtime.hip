@@ -253,6 +253,10 @@ static int choose_ksplit(long tiles_times_items, int K, int max_split, int* k_ch
 static const int kFatMinRows = 192;
 static bool fat_rows(int rows) { return rows >= kFatMinRows; }
 
+// dense store products of at least this many rows take the 8-wave tile kernel
+// (measured at 256 rows: 9.37 -> 9.28 ms per full step)
+static const int kWaves8MinRows = 128;
+
 // Soft-embedding product (K = vocab, 256 x 256 tiles of the K-major kernel):
 // split so that ~256 workgroups (one per CU, at most one round) share the
 // contraction.
@@ -276,6 +280,7 @@ static hipError_t dense_gemm(int epi, GemmArgs g, int M, hipStream_t st) {
     return gemm_fat(epi, g, st);
   }
   g.items_max = cdiv(M, kGemmRowChunk);
+  g.waves8 = M >= kWaves8MinRows && g.tile_rows == 64 && g.tile_cols == 64 && g.ring == 4;
   return gemm(epi, g, st);
 }
 
@@ -384,9 +389,6 @@ struct Pass {
 
 static const bf16_t* lw(const dg_model* m, int l, size_t off) { return m->layers[l] + off; }
 
-// dense store products of at least this many rows take the 8-wave tile kernel
-// (measured at 256 rows: 9.37 -> 9.28 ms per full step)
-static const int kWaves8MinRows = 128;
 
 static GemmArgs gargs() {
   GemmArgs g;
