@@ -124,6 +124,9 @@ WORKLOADS = {
     # full model, 32768-token shared prefix, 4 canvases, up to 48 steps.
     "long_block": Workload("long_block", FULL, batch=4, prefix_batch=1, prefix_len=32768,
                            canvas_len=256, steps=48, hidden_input=False),
+    # long_block with one 32768-token prompt per canvas (4 prompts, 4x the KV)
+    "long_block_bp4": Workload("long_block_bp4", FULL, batch=4, prefix_batch=4, prefix_len=32768,
+                               canvas_len=256, steps=48, hidden_input=False),
 }
 
 
