@@ -1093,19 +1093,20 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
 // vocabulary, so no transposed copy of E is needed.  Square 256 x 256 tiles
 // and waves as gemm_fat2_kernel; the weight part of a stage is 64 rows of W
 // (k) x 256 columns (n), 512 bytes per row, whose 16-byte slots are XOR-
-// swizzled by 2 (k % 16).  The MFMA B operand (8 consecutive k of one column
+// swizzled by 2 (k % 4) + 8 ((k / 8) % 2).  The MFMA B operand (8 consecutive k of one column
 // per lane) comes from two transposed LDS reads (ds_read_b64_tr_b16): within
 // each 16 lanes, lane 4a + b receives element b of the 8-byte reads of lanes
 // a, a + 4, a + 8, a + 12, so lane 4a + j of 16-lane group G reads row
 // 8 G + j (then 8 G + 4 + j) at column 4 a of the fragment's 16: lane t ends
 // up with column t and rows 8 G .. 8 G + 7, the k-slots of the A operand's
-// 16-byte reads.  The eight rows of 32 lanes map to eight distinct slot pairs
-// of the 512-byte rows, so the reads are bank-conflict-free.
+// 16-byte reads.  The eight rows that 32 lanes read (k % 4 and k / 8 vary)
+// sit in eight distinct slot pairs of a 256-byte bank row, so the reads are
+// bank-conflict-free.
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-__device__ __forceinline__ int kn_swz(int row) { return 2 * (row & 15); }
+__device__ __forceinline__ int kn_swz(int row) { return 2 * (row & 3) + 8 * ((row >> 3) & 1); }
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_kn_kernel(GemmArgs g) {
