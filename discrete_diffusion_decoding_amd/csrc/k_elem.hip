@@ -31,10 +31,16 @@ __device__ __forceinline__ void store_bf16x4(bf16_t* p, float4 v) {
   o.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
   *reinterpret_cast<uint2*>(p) = o;
 }
-__device__ __forceinline__ float4 load_bf16x4(const bf16_t* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
+__device__ __forceinline__ float4 unpack_bf16x4(uint2 u) {
   return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
                      __uint_as_float(u.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ float4 load_bf16x4(const bf16_t* p) {
+  return unpack_bf16x4(*reinterpret_cast<const uint2*>(p));
+}
+// the values a bf16x4 store of v would hold
+__device__ __forceinline__ float4 round_bf16x4(float4 v) {
+  return make_float4(bf2f(f2bf(v.x)), bf2f(f2bf(v.y)), bf2f(f2bf(v.z)), bf2f(f2bf(v.w)));
 }
 
 // ---------------------------------------------------------------------------
@@ -58,6 +64,8 @@ hipError_t embed_rows(const int32_t* tokens, const bf16_t* E, int rows, int d, f
 // ---------------------------------------------------------------------------
 // h += (gate ? sigmoid(gate) : 1) * sum_s part_s ; xn = bf16(rms(h) * w);
 // optional router hi/lo rows (xn2 and the bf16 residual of the fp32 value).
+// Every load of the row (residual, partials, gate, norm weight) is issued
+// before the first store, so the row costs one memory round trip.
 template <int NS>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w, int rows, int d, float eps,
                                                       bf16_t* out, bf16_t* split, float* dump, Partials part,
@@ -69,6 +77,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w,
   float4* x4 = reinterpret_cast<float4*>(h + (long)r * d);
   float4 v[DG_MAXC4];
   float4 ps[DG_MAXC4][NS > 0 ? NS : 1];
+  uint2 wr[DG_MAXC4], gr[DG_MAXC4];
 #pragma unroll
   for (int j = 0; j < DG_MAXC4; ++j) {
     const int c4 = threadIdx.x + 256 * j;
@@ -77,6 +86,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w,
 #pragma unroll
       for (int s = 0; s < NS; ++s)
         ps[j][s] = reinterpret_cast<const float4*>(part.p + s * part.stride + (long)r * d)[c4];
+      if (NS > 0 && pgate) gr[j] = *reinterpret_cast<const uint2*>(pgate + 4 * c4);
+      wr[j] = *reinterpret_cast<const uint2*>(w + 4 * c4);
     }
   }
   float ss = 0.f;
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w,
 #pragma unroll
         for (int s = 1; s < NS; ++s) acc = f4add(acc, ps[j][s]);
         if (pgate) {
-          const float4 gt = load_bf16x4(pgate + 4 * c4);
+          const float4 gt = unpack_bf16x4(gr[j]);
           acc = make_float4(sigmoidf_(gt.x) * acc.x, sigmoidf_(gt.y) * acc.y, sigmoidf_(gt.z) * acc.z,
                             sigmoidf_(gt.w) * acc.w);
         }
@@ -105,13 +116,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const bf16_t* w,
   for (int j = 0; j < DG_MAXC4; ++j) {
     const int c4 = threadIdx.x + 256 * j;
     if (c4 < d4) {
-      const float4 wv = load_bf16x4(w + 4 * c4);
+      const float4 wv = unpack_bf16x4(wr[j]);
       const float4 y = make_float4(v[j].x * inv * wv.x, v[j].y * inv * wv.y, v[j].z * inv * wv.z,
                                    v[j].w * inv * wv.w);
       store_bf16x4(out + (long)r * d + 4 * c4, y);
       if (split) {
         store_bf16x4(split + (long)r * d + 4 * c4, y);
-        const float4 hi = load_bf16x4(split + (long)r * d + 4 * c4);
+        const float4 hi = round_bf16x4(y);
         store_bf16x4(split + (long)(rows + r) * d + 4 * c4,
                      make_float4(y.x - hi.x, y.y - hi.y, y.z - hi.z, y.w - hi.w));
       }
@@ -310,8 +321,12 @@ hipError_t qk_norm_rope(const QkRopeArgs& a, hipStream_t s) {
 // Merge of key-split attention partials (scores kept in log2 units): block
 // (r, y) takes heads y hpb .. y hpb + hpb - 1 of row r; the split weights
 // 2^(m_s - M) / L of its heads are formed once in LDS, then each thread sums
-// its float4 columns over the splits.  Few rows (decoding) take 1024 / hd heads
-// per block, so that a thread makes one pass; many rows take every head.
+// its float4 columns over the splits.  The partial outputs do not depend on
+// the weights, so a thread's first kMergeAhead columns are loaded before the
+// (m, l) pairs are read: the block costs one memory round trip, not one per
+// column pass.  Few rows (decoding) take 1024 / hd heads per block, so that a
+// thread makes one pass; many rows take every head.
+constexpr int kMergeAhead = 4;
 template <int NSP>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16_t* op, const float* ml, int rows, int H, int hd,
                                                          int hpb, bf16_t* out, const int32_t* flag) {
@@ -320,7 +335,19 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16_t* op, const
   const int r = blockIdx.x;
   const int h0 = blockIdx.y * hpb, h1 = min(H, h0 + hpb);
   const long srow = (long)rows * H;
-  for (int h = h0 + threadIdx.x; h < h1; h += blockDim.x) {
+  const long rowoff = (long)r * H * hd;
+  const long sstride = srow * hd;
+  const int i0 = h0 * hd / 4 + (int)threadIdx.x, n4 = h1 * hd / 4;
+  uint2 pre[kMergeAhead][NSP];
+#pragma unroll
+  for (int g = 0; g < kMergeAhead; ++g) {
+    const int i4 = i0 + 256 * g;
+    if (i4 < n4) {
+#pragma unroll
+      for (int s = 0; s < NSP; ++s) pre[g][s] = *reinterpret_cast<const uint2*>(op + s * sstride + rowoff + 4 * i4);
+    }
+  }
+  for (int h = h0 + threadIdx.x; h < h1; h += 256) {
     const long base = (long)r * H + h;
     float mv[NSP], lv[NSP];
     float M = -INFINITY;
@@ -342,10 +369,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const bf16_t* op, const
     for (int s = 0; s < NSP; ++s) wts[h * NSP + s] = mv[s] * il;
   }
   __syncthreads();
-  const long rowoff = (long)r * H * hd;
-  const long sstride = srow * hd;
-  const int n4 = h1 * hd / 4;
-  for (int i4 = h0 * hd / 4 + threadIdx.x; i4 < n4; i4 += blockDim.x) {
+#pragma unroll
+  for (int g = 0; g < kMergeAhead; ++g) {
+    const int i4 = i0 + 256 * g;
+    if (i4 < n4) {
+      const int h = (4 * i4) / hd;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < NSP; ++s) acc = f4fma(wts[h * NSP + s], unpack_bf16x4(pre[g][s]), acc);
+      store_bf16x4(out + rowoff + 4 * i4, acc);
+    }
+  }
+  for (int i4 = i0 + 256 * kMergeAhead; i4 < n4; i4 += 256) {
     const int h = (4 * i4) / hd;
     float4 vals[NSP];
 #pragma unroll
@@ -423,29 +458,39 @@ __device__ __forceinline__ uint64_t wave_umax64(uint64_t x) {
 // Row r's slots: its NK routed experts (gates: softmax over their logits),
 // then ns always-on experts E .. E + ns - 1 with gate 1 (the shared FFN's
 // blocks, when they run as experts); the dumps hold the routed ones only.
+// One wave per row; sidx (may be null) takes a copy of the row's slots.
 template <int NS, int NK>
-__global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, int ns, int32_t* idx, float* gate,
-                                                  int32_t* idx_dump, float* gate_dump, float* logit_dump,
-                                                  const int32_t* flag) {
-  if (flag && *flag) return;
-  const int lane = threadIdx.x;
-  const int r = blockIdx.x;
+__device__ __forceinline__ void topk_wave_row(const Partials& rl, int rows, int E, int ns, int r, int32_t* idx,
+                                              float* gate, int32_t* idx_dump, float* gate_dump, float* logit_dump,
+                                              int32_t* sidx) {
+  const int lane = threadIdx.x & 63;
+  // every partial of the row is loaded before the first (dump) store
+  float hp[4][NS], lp[4][NS];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    if (64 * j < E && e < E) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        hp[j][s] = rl.p[s * rl.stride + (long)r * E + e];
+        lp[j][s] = rl.p[s * rl.stride + (long)(rows + r) * E + e];
+      }
+    }
+  }
   uint64_t key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     key[j] = 0;
-    if (64 * j < E) {   // uniform over the wave
-      const int e = lane + 64 * j;
-      if (e < E) {
-        float h = 0.f, l = 0.f;
+    const int e = lane + 64 * j;
+    if (64 * j < E && e < E) {
+      float h = 0.f, l = 0.f;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          h += rl.p[s * rl.stride + (long)r * E + e];
-          l += rl.p[s * rl.stride + (long)(rows + r) * E + e];
-        }
-        key[j] = topk_key(h + l, e);
-        if (logit_dump) logit_dump[(long)r * E + e] = h + l;
+      for (int s = 0; s < NS; ++s) {
+        h += hp[j][s];
+        l += lp[j][s];
       }
+      key[j] = topk_key(h + l, e);
+      if (logit_dump) logit_dump[(long)r * E + e] = h + l;
     }
   }
   float mine_v = 0.f, top_v = 0.f;
@@ -476,12 +521,22 @@ __global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, 
     const float gt = ex / den;
     idx[(long)r * ko + lane] = mine_e;
     gate[(long)r * ko + lane] = gt;
+    if (sidx) sidx[r * ko + lane] = mine_e;
     if (idx_dump) idx_dump[(long)r * NK + lane] = mine_e;
     if (gate_dump) gate_dump[(long)r * NK + lane] = gt;
   } else if (lane < ko) {
     idx[(long)r * ko + lane] = E + lane - NK;
     gate[(long)r * ko + lane] = 1.f;
+    if (sidx) sidx[r * ko + lane] = E + lane - NK;
   }
+}
+
+template <int NS, int NK>
+__global__ __launch_bounds__(64) void topk_kernel(Partials rl, int rows, int E, int ns, int32_t* idx, float* gate,
+                                                  int32_t* idx_dump, float* gate_dump, float* logit_dump,
+                                                  const int32_t* flag) {
+  if (flag && *flag) return;
+  topk_wave_row<NS, NK>(rl, rows, E, ns, blockIdx.x, idx, gate, idx_dump, gate_dump, logit_dump, nullptr);
 }
 
 hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* idx, float* gate, int32_t* idx_dump,
@@ -512,13 +567,17 @@ hipError_t router_topk(Partials rlog, int rows, int E, int k, int ns, int32_t* i
 }
 
 // ---------------------------------------------------------------------------
-// Expert permutation in one workgroup of 1024 threads (16 waves).
+// Expert permutation in one workgroup of NT threads.
 // Assignment a = row * k + j takes position p in its expert e from an LDS
 // counter (atomic add; the order of rows within an expert is arbitrary and
 // changes no result: every row of an expert GEMM depends on its own
 // activation row only, and the combine reads the k slots of a row in j
-// order), then goes to slot offsets[e] + p.  p is parked in slot_of[a] (this
-// thread's own write) until the offsets are known.
+// order), then goes to slot offsets[e] + p.  Assignments are taken in chunks
+// of kPermPB per thread whose loads are issued together (one memory round
+// trip per chunk); the first chunk's experts and positions stay in
+// registers, later chunks park p in slot_of[a] (this thread's own write)
+// until the offsets are known.
+constexpr int kPermPB = 8;
 template <int NT>
 __device__ __forceinline__ void permute_body(const int32_t* idx, int na, int k, int E, int32_t* counts,
                                              int32_t* offsets, int32_t* slot_of, int32_t* slot_row, int4* items,
@@ -527,9 +586,33 @@ __device__ __forceinline__ void permute_body(const int32_t* idx, int na, int k, 
   __shared__ int off[257];
   __shared__ int ibase[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int CH = kPermPB * NT;
+  int e0[kPermPB], p0[kPermPB];
+#pragma unroll
+  for (int j = 0; j < kPermPB; ++j) {
+    const int a = tid + NT * j;
+    e0[j] = a < na ? idx[a] : 0;
+  }
   if (tid < 256) cnt[tid] = 0;
   __syncthreads();
-  for (int a = tid; a < na; a += NT) slot_of[a] = atomicAdd(&cnt[idx[a]], 1);
+#pragma unroll
+  for (int j = 0; j < kPermPB; ++j) {
+    const int a = tid + NT * j;
+    p0[j] = a < na ? atomicAdd(&cnt[e0[j]], 1) : 0;
+  }
+  for (int a0 = CH; a0 < na; a0 += CH) {
+    int ev[kPermPB];
+#pragma unroll
+    for (int j = 0; j < kPermPB; ++j) {
+      const int a = a0 + tid + NT * j;
+      ev[j] = a < na ? idx[a] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPermPB; ++j) {
+      const int a = a0 + tid + NT * j;
+      if (a < na) slot_of[a] = atomicAdd(&cnt[ev[j]], 1);
+    }
+  }
   __syncthreads();
   // exclusive scans over the experts of the row counts and of the item counts:
   // waves 0-3 scan 64 experts each (shuffle scan), then add the wave totals
@@ -580,11 +663,32 @@ __device__ __forceinline__ void permute_body(const int32_t* idx, int na, int k, 
         items[i] = make_int4(e, off[e] + r, min(chunk, cnt[e] - r), (c << 16) | nc);
     }
   }
-  for (int a = tid; a < na; a += NT) {
-    const int e = idx[a];
-    const int slot = off[e] + slot_of[a];
-    slot_of[a] = slot;
-    slot_row[slot] = a / k;
+#pragma unroll
+  for (int j = 0; j < kPermPB; ++j) {
+    const int a = tid + NT * j;
+    if (a < na) {
+      const int slot = off[e0[j]] + p0[j];
+      slot_of[a] = slot;
+      slot_row[slot] = a / k;
+    }
+  }
+  for (int a0 = CH; a0 < na; a0 += CH) {
+    int ev[kPermPB], pv[kPermPB];
+#pragma unroll
+    for (int j = 0; j < kPermPB; ++j) {
+      const int a = a0 + tid + NT * j;
+      ev[j] = a < na ? idx[a] : 0;
+      pv[j] = a < na ? slot_of[a] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPermPB; ++j) {
+      const int a = a0 + tid + NT * j;
+      if (a < na) {
+        const int slot = off[ev[j]] + pv[j];
+        slot_of[a] = slot;
+        slot_row[slot] = a / k;
+      }
+    }
   }
 }
 
@@ -607,62 +711,9 @@ __global__ __launch_bounds__(256) void topk_permute_kernel(Partials rl, int rows
                                                            int chunk, const int32_t* flag) {
   if (flag && *flag) return;
   __shared__ int32_t sidx[4 * 64];
-  const int lane = threadIdx.x & 63, r = threadIdx.x >> 6;
+  const int r = threadIdx.x >> 6;
   const int ko = NK + ns;
-  if (r < rows) {
-    uint64_t key[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      key[j] = 0;
-      if (64 * j < E) {
-        const int e = lane + 64 * j;
-        if (e < E) {
-          float h = 0.f, l = 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < NS; ++s2) {
-            h += rl.p[s2 * rl.stride + (long)r * E + e];
-            l += rl.p[s2 * rl.stride + (long)(rows + r) * E + e];
-          }
-          key[j] = topk_key(h + l, e);
-          if (logit_dump) logit_dump[(long)r * E + e] = h + l;
-        }
-      }
-    }
-    float mine_v = 0.f, top_v = 0.f;
-    int mine_e = 0;
-#pragma unroll
-    for (int t = 0; t < NK; ++t) {
-      const uint64_t best = wave_umax64(max(max(key[0], key[1]), max(key[2], key[3])));
-      const int e = 0xFFFF - (int)(best & 0xFFFF);
-      const float v = topk_key_value(best);
-      if (t == 0) top_v = v;
-      if (lane == t) {
-        mine_v = v;
-        mine_e = e;
-      }
-      if ((e & 63) == lane) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if ((e >> 6) == j) key[j] = 0;
-      }
-    }
-    float ex = lane < NK ? expf(mine_v - top_v) : 0.f;
-    float den = ex;
-#pragma unroll
-    for (int o = 1; o < NK; o <<= 1) den += __shfl_xor(den, o, 64);
-    if (lane < NK) {
-      const float gt = ex / den;
-      sidx[r * ko + lane] = mine_e;
-      idx[(long)r * ko + lane] = mine_e;
-      gate[(long)r * ko + lane] = gt;
-      if (idx_dump) idx_dump[(long)r * NK + lane] = mine_e;
-      if (gate_dump) gate_dump[(long)r * NK + lane] = gt;
-    } else if (lane < ko) {
-      sidx[r * ko + lane] = E + lane - NK;
-      idx[(long)r * ko + lane] = E + lane - NK;
-      gate[(long)r * ko + lane] = 1.f;
-    }
-  }
+  if (r < rows) topk_wave_row<NS, NK>(rl, rows, E, ns, r, idx, gate, idx_dump, gate_dump, logit_dump, sidx);
   __syncthreads();
   permute_body<256>(sidx, rows * ko, ko, E + ns, counts, offsets, slot_of, slot_row, items, n_items, chunk);
 }
@@ -713,7 +764,10 @@ hipError_t moe_permute(const int32_t* idx, int rows, int k, int E, int32_t* coun
 
 // ---------------------------------------------------------------------------
 // h[r] += sum_s ys_s[r] + sum_j gate[r,j] * Y[slot[r,j]] (expert outputs Y in bf16,
-// as stored by the down projection), then the next RMSNorm.
+// as stored by the down projection), then the next RMSNorm.  Two memory round
+// trips per row: the slots and gates, then every other load of the row
+// (expert rows, shared partials, residual, next norm weight) before the
+// first store.
 template <int NS, int NK>
 __global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, const bf16_t* Y,
                                                       const int32_t* slot_of, const float* gate, int d,
@@ -732,22 +786,31 @@ __global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, con
   }
   float4* x4 = reinterpret_cast<float4*>(h + (long)r * d);
   float4 v[DG_MAXC4];
+  uint2 yr[DG_MAXC4][NK], wr[DG_MAXC4];
+  float4 pv[DG_MAXC4][NS > 0 ? NS : 1];
+#pragma unroll
+  for (int c = 0; c < DG_MAXC4; ++c) {
+    const int c4 = threadIdx.x + 256 * c;
+    if (c4 < d4) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) yr[c][j] = *reinterpret_cast<const uint2*>(Y + (long)sl[j] * d + 4 * c4);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) pv[c][s] = reinterpret_cast<const float4*>(ys.p + s * ys.stride + (long)r * d)[c4];
+      v[c] = x4[c4];
+      if (nw) wr[c] = *reinterpret_cast<const uint2*>(nw + 4 * c4);
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < DG_MAXC4; ++c) {
     const int c4 = threadIdx.x + 256 * c;
     if (c4 < d4) {
-      float4 yv[NK], pv[NS > 0 ? NS : 1];
-#pragma unroll
-      for (int j = 0; j < NK; ++j) yv[j] = load_bf16x4(Y + (long)sl[j] * d + 4 * c4);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) pv[s] = reinterpret_cast<const float4*>(ys.p + s * ys.stride + (long)r * d)[c4];
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int j = 0; j < NK; ++j) acc = f4fma(gt[j], yv[j], acc);
+      for (int j = 0; j < NK; ++j) acc = f4fma(gt[j], unpack_bf16x4(yr[c][j]), acc);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) acc = f4add(acc, pv[s]);
-      v[c] = f4add(x4[c4], acc);
+      for (int s = 0; s < NS; ++s) acc = f4add(acc, pv[c][s]);
+      v[c] = f4add(v[c], acc);
       x4[c4] = v[c];
       ss += f4dot(v[c]);
     }
@@ -760,7 +823,7 @@ __global__ __launch_bounds__(256) void combine_kernel(float* h, Partials ys, con
     const int c4 = threadIdx.x + 256 * c;
     if (c4 < d4) {
       if (nw) {
-        const float4 wv = load_bf16x4(nw + 4 * c4);
+        const float4 wv = unpack_bf16x4(wr[c]);
         store_bf16x4(xn + (long)r * d + 4 * c4, make_float4(v[c].x * inv * wv.x, v[c].y * inv * wv.y,
                                                             v[c].z * inv * wv.z, v[c].w * inv * wv.w));
       }
