@@ -592,13 +592,23 @@ static dg_status run_layers(const dg_model* m, const Plan& p, void* ws, const Pa
       GemmArgs g2 = gargs();
       g2.ring = m->d_ring;
       g2.A = hs; g2.lda = fs; g2.W = lw(m, l, m->lay.w_down_sh); g2.ldw = fs; g2.K = fs; g2.N = D;
-      dense_rows(g2, R);
-      g2.tile_rows = 128; g2.ring = 3; g2.items_max = cdiv(R, 128);   // as the O projection
-      g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, g2.tile_cols), fs, kMaxDenseSplit, &g2.k_chunk);
-      ysp.n = g2.k_split;
       g2.C = ys; g2.ldc = D; g2.c_kstride = (long)R * D; g2.flag = ps.flag;
-      g2.waves8 = R >= kWaves8MinRows;
-      DG_CK(gemm(EPI_STORE_F32, g2, ss));
+      if (forked && fat_rows(R) && gemm_fat_pitch_ok(fs, fs)) {
+        // beside the expert products, a few long workgroups (256 x 128 output
+        // tiles, no k split: 22 at 256 rows) hold fewer of the slots those
+        // products could fill than hundreds of short split-K ones; the join is
+        // far off, so their length costs nothing (full step 9.29 -> 9.16 ms)
+        g2.M = R; g2.items_max = cdiv(R, kFatRowChunk); g2.k_split = 1; g2.k_chunk = fs;
+        ysp.n = 1;
+        DG_CK(gemm_fat(EPI_STORE_F32, g2, ss));
+      } else {
+        dense_rows(g2, R);
+        g2.tile_rows = 128; g2.ring = 3; g2.items_max = cdiv(R, 128);   // as the O projection
+        g2.k_split = choose_ksplit((long)g2.items_max * cdiv(D, g2.tile_cols), fs, kMaxDenseSplit, &g2.k_chunk);
+        ysp.n = g2.k_split;
+        g2.waves8 = R >= kWaves8MinRows;
+        DG_CK(gemm(EPI_STORE_F32, g2, ss));
+      }
       if (forked) DG_CK(hipEventRecord(m->ev_join, ss));
       return DG_OK;
     };
