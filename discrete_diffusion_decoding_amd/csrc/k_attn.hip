@@ -15,8 +15,12 @@
 // Key / value tiles (32 keys) stream through a 4-deep LDS ring by direct
 // global->LDS DMA: K rows [32][hd] and V^T rows [hd][32 keys] (the V^T caches
 // are stored tile-major, so a tile's V^T is one contiguous block), 16-byte slots
-// XOR-swizzled (K: slot ^ kswz(key), V^T: slot ^ vswz(dim)) so that every 8
-// and every 16 lanes of an MFMA operand read hit distinct banks.
+// XOR-swizzled (K: slot ^ kswz(key), V^T: slot ^ vswz(dim)) so that the 16
+// lanes that one LDS pass of a 16-byte read serves hit distinct banks.  The
+// V^T swizzle was chosen by measurement: over the 16 rows (64 bytes each) that
+// a pass reads, the choice of 32-byte half has to follow row bits 2 and 3 (a
+// bank-conflict counter probe of all 256 linear swizzles of the row's low 4
+// bits: 96 read conflict-free, the rest 2- or 4-way).
 //
 // Each fragment computes S^T = K Q^T with keys as the MFMA M dimension.  The
 // K fragment of block kf reads key row 8 (r / 4) + 4 kf + r % 4 for MFMA row
@@ -43,7 +47,7 @@ constexpr int waitcnt_vm_attn(int n) { return (n & 15) | (7 << 4) | (15 << 8) | 
 // slot swizzles: K row `key` (0..31 in the tile) of a head_dim with ck 16-byte
 // slots, and V^T row `dim`
 __device__ __forceinline__ int kswz(int key, int ck) { return ((key & 3) | ((key >> 1) & 12)) & (ck - 1); }
-__device__ __forceinline__ int vswz(int dim) { return ((dim >> 1) ^ (dim >> 3)) & 3; }
+__device__ __forceinline__ int vswz(int dim) { return (dim >> 1) & 3; }
 
 // sum / max over the four lanes l % 16 + 16 i of a wave (gfx950 row swaps)
 __device__ __forceinline__ float xrow_max(float v) {
