@@ -412,6 +412,11 @@ __device__ __forceinline__ void wave_argmax(float& mx, int& ix) {
   }
 }
 
+// A thread's entries of its slice (float4 entries 4 tid + 1024 j) are loaded in
+// one batch and kept in registers for both passes when the slice holds at most
+// kSliceRegs of them per thread (REG); otherwise each pass streams them.
+constexpr int kSliceRegs = 16;
+template <bool REG>
 __global__ __launch_bounds__(256) void softmax_slice_kernel(const float* logits, long ldl, int V, int kchunk,
                                                             int nslices, int T, const int32_t* stopped, bf16_t* P,
                                                             float4* sstat, const int32_t* flag) {
@@ -423,15 +428,32 @@ __global__ __launch_bounds__(256) void softmax_slice_kernel(const float* logits,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int v0 = sl * kchunk, v1 = min(V, v0 + kchunk);   // multiples of 4
   const float* l = logits + (long)r * ldl;
+  constexpr int NR = REG ? kSliceRegs : 1;
+  float4 xr[NR];
+  if (REG) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int v = v0 + 4 * tid + 1024 * j;
+      if (v < v1) xr[j] = *reinterpret_cast<const float4*>(l + v);
+    }
+  }
   // the slice's maximum and argmax (entries in increasing order per thread)
   float mx = -INFINITY;
   int ix = 0x7FFFFFFF;
-  for (int v = v0 + 4 * tid; v < v1; v += 1024) {
-    const float4 x = *reinterpret_cast<const float4*>(l + v);
+  auto scan = [&](const float4 x, int v) {
     if (x.x > mx) { mx = x.x; ix = v; }
     if (x.y > mx) { mx = x.y; ix = v + 1; }
     if (x.z > mx) { mx = x.z; ix = v + 2; }
     if (x.w > mx) { mx = x.w; ix = v + 3; }
+  };
+  if (REG) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int v = v0 + 4 * tid + 1024 * j;
+      if (v < v1) scan(xr[j], v);
+    }
+  } else {
+    for (int v = v0 + 4 * tid; v < v1; v += 1024) scan(*reinterpret_cast<const float4*>(l + v), v);
   }
   wave_argmax(mx, ix);
   if (lane == 0) { smx[wave] = mx; six[wave] = ix; }
@@ -447,8 +469,7 @@ __global__ __launch_bounds__(256) void softmax_slice_kernel(const float* logits,
   // e^(l - M) summed, with its (l - M)-weighted sum (entropy), stored scaled
   float z = 0.f, a = 0.f;
   bf16_t* prow = P ? P + (long)r * V : nullptr;
-  for (int v = v0 + 4 * tid; v < v1; v += 1024) {
-    const float4 x = *reinterpret_cast<const float4*>(l + v);
+  auto accumulate = [&](const float4 x, int v) {
     const float d0 = x.x - M, d1 = x.y - M, d2 = x.z - M, d3 = x.w - M;
     const float e0 = __expf(d0), e1 = __expf(d1), e2 = __expf(d2), e3 = __expf(d3);
     z += (e0 + e1) + (e2 + e3);
@@ -459,6 +480,15 @@ __global__ __launch_bounds__(256) void softmax_slice_kernel(const float* logits,
       o.y = (uint32_t)f2bf(e2) | ((uint32_t)f2bf(e3) << 16);
       *reinterpret_cast<uint2*>(prow + v) = o;
     }
+  };
+  if (REG) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) {
+      const int v = v0 + 4 * tid + 1024 * j;
+      if (v < v1) accumulate(xr[j], v);
+    }
+  } else {
+    for (int v = v0 + 4 * tid; v < v1; v += 1024) accumulate(*reinterpret_cast<const float4*>(l + v), v);
   }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -477,8 +507,12 @@ hipError_t softmax_slices(const float* logits, long ldl, int rows, int V, int kc
   if (rows <= 0) return hipSuccess;
   if (V % 4 || kchunk % 4 || ldl % 4 || nslices < 1 || (long)kchunk * nslices < V || T < 1)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(softmax_slice_kernel, dim3((unsigned)(rows * nslices)), dim3(256), 0, s, logits, ldl, V,
-                     kchunk, nslices, T, stopped, P, sstat, flag);
+  if (kchunk <= 1024 * kSliceRegs)
+    hipLaunchKernelGGL(softmax_slice_kernel<true>, dim3((unsigned)(rows * nslices)), dim3(256), 0, s, logits, ldl, V,
+                       kchunk, nslices, T, stopped, P, sstat, flag);
+  else
+    hipLaunchKernelGGL(softmax_slice_kernel<false>, dim3((unsigned)(rows * nslices)), dim3(256), 0, s, logits, ldl,
+                       V, kchunk, nslices, T, stopped, P, sstat, flag);
   return hipGetLastError();
 }
 
