@@ -17,10 +17,9 @@
 // are stored tile-major, so a tile's V^T is one contiguous block), 16-byte slots
 // XOR-swizzled (K: slot ^ kswz(key), V^T: slot ^ vswz(dim)) so that the 16
 // lanes that one LDS pass of a 16-byte read serves hit distinct banks.  The
-// V^T swizzle was chosen by measurement: over the 16 rows (64 bytes each) that
-// a pass reads, the choice of 32-byte half has to follow row bits 2 and 3 (a
-// bank-conflict counter probe of all 256 linear swizzles of the row's low 4
-// bits: 96 read conflict-free, the rest 2- or 4-way).
+// V^T swizzle was chosen by measurement (a bank-conflict counter probe of all
+// 256 linear swizzles of the row's low 4 bits over the 16 rows of 64 bytes
+// that a pass reads: 96 read conflict-free, the rest 2- or 4-way).
 //
 // Each fragment computes S^T = K Q^T with keys as the MFMA M dimension.  The
 // K fragment of block kf reads key row 8 (r / 4) + 4 kf + r % 4 for MFMA row
