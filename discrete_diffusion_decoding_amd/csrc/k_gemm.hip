@@ -1015,18 +1015,32 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 af[8], bfr[4];
-#define DG_F2HALF(S, J)                                                                                    \
+  // A stage's operand reads run ahead of its MFMAs: the 12 reads of k half 0
+  // are issued at once, and each activation fragment of k half 1 is read
+  // into the registers of the same fragment of half 0 as soon as that
+  // fragment's 4 MFMAs are issued (half 1's weight fragments at the start),
+  // so only the first reads of a stage stall the MFMA chain.
+  bf16x8 af[8], bf0[4], bf1[4];
+#define DG_F2RA(S, J, M) \
+  (*reinterpret_cast<const bf16x8*>(&S[(128 * wm + 16 * (M) + lr) * 64 + (((4 * (J) + lg) ^ (lr & 7)) << 3)]))
+#define DG_F2RB(S, J, N) (*reinterpret_cast<const bf16x8*>(&S[boffr[N] + (((4 * (J) + lg) ^ (lr & 7)) << 3)]))
+#define DG_F2STAGEMM(S)                                                                                    \
   do {                                                                                                     \
-    const int p_ = 4 * (J) + lg;                                                                           \
+    _Pragma("unroll") for (int n = 0; n < 4; ++n) bf0[n] = DG_F2RB(S, 0, n);                               \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) af[m] = DG_F2RA(S, 0, m);                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);                                                    \
     _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                                        \
-      const int arow = 128 * wm + 16 * m + lr;                                                             \
-      af[m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);                  \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bf0[n], acc[m][n]);    \
+      if (m == 0) {                                                                                        \
+        _Pragma("unroll") for (int n = 0; n < 4; ++n) bf1[n] = DG_F2RB(S, 1, n);                           \
+      }                                                                                                    \
+      af[m] = DG_F2RA(S, 1, m);                                                                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                                   \
+      if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);                                       \
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                              \
     }                                                                                                      \
-    _Pragma("unroll") for (int n = 0; n < 4; ++n)                                                          \
-      bfr[n] = *reinterpret_cast<const bf16x8*>(&S[boffr[n] + ((p_ ^ (lr & 7)) << 3)]);                    \
     _Pragma("unroll") for (int m = 0; m < 8; ++m)                                                          \
-      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bfr[n], acc[m][n]);    \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bf1[n], acc[m][n]);    \
   } while (0)
   // stage s is read when at most stage s+1 (8 loads per lane) is pending; its
   // buffer is refilled (stage s+2, clamped to the last stage, so every
@@ -1036,8 +1050,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
     const int s_ = (SI);                                                                                   \
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                                                             \
     __builtin_amdgcn_s_barrier();                                                                          \
-    DG_F2HALF(CUR, 0);                                                                                     \
-    DG_F2HALF(CUR, 1);                                                                                     \
+    DG_F2STAGEMM(CUR);                                                                                     \
     __builtin_amdgcn_s_waitcnt(0xC07F);   /* lgkmcnt(0): this wave's reads of CUR are done */              \
     __builtin_amdgcn_s_barrier();                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
@@ -1057,15 +1070,16 @@ __global__ __launch_bounds__(512, 1) void gemm_fat2_kernel(GemmArgs g) {
   if (s < nst) {   // odd count: the last stage sits in S0; drain the ring
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    DG_F2HALF(S0, 0);
-    DG_F2HALF(S0, 1);
+    DG_F2STAGEMM(S0);
   }
   };
   if (wnt) pipeline(std::true_type{});
   else pipeline(std::false_type{});
   __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the loop
 #undef DG_F2ISSUE
-#undef DG_F2HALF
+#undef DG_F2RA
+#undef DG_F2RB
+#undef DG_F2STAGEMM
 #undef DG_F2ITER
 
 #pragma unroll
@@ -1178,34 +1192,45 @@ __global__ __launch_bounds__(512, 1) void gemm_kn_kernel(GemmArgs g) {
   for (int a = 0; a < 8; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 af[8], bfr[4];
+  // operand reads run ahead of the MFMAs as in gemm_fat2_kernel
+  bf16x8 af[8], bf0[4], bf1[4];
 #define DG_KNB(S, ROW, C)                                                                                  \
   __builtin_amdgcn_ds_read_tr16_b64_v4i16(                                                                 \
       (lds_v4i16_t*)&S[kFat2A + (ROW) * 256 + ((((C) >> 3) ^ kn_swz(ROW)) << 3) + ((C) & 4)])
-#define DG_KNHALF(S, J)                                                                                    \
+#define DG_KNRA(S, J, M) \
+  (*reinterpret_cast<const bf16x8*>(&S[(128 * wm + 16 * (M) + lr) * 64 + (((4 * (J) + lg) ^ (lr & 7)) << 3)]))
+#define DG_KNRB(S, J, DST)                                                                                 \
   do {                                                                                                     \
-    const int p_ = 4 * (J) + lg;                                                                           \
-    _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                                        \
-      const int arow = 128 * wm + 16 * m + lr;                                                             \
-      af[m] = *reinterpret_cast<const bf16x8*>(&S[arow * 64 + ((p_ ^ (arow & 7)) << 3)]);                  \
-    }                                                                                                      \
     const int r0_ = 32 * (J) + 8 * lg + tj;                                                                \
     _Pragma("unroll") for (int n = 0; n < 4; ++n) {                                                        \
       const v4i16_t lo_ = DG_KNB(S, r0_, bcol[n]);                                                         \
       const v4i16_t hi_ = DG_KNB(S, r0_ + 4, bcol[n]);                                                     \
       const v8i16_t both_ = __builtin_shufflevector(lo_, hi_, 0, 1, 2, 3, 4, 5, 6, 7);                    \
-      bfr[n] = __builtin_bit_cast(bf16x8, both_);                                                          \
+      DST[n] = __builtin_bit_cast(bf16x8, both_);                                                          \
+    }                                                                                                      \
+  } while (0)
+#define DG_KNSTAGEMM(S)                                                                                    \
+  do {                                                                                                     \
+    DG_KNRB(S, 0, bf0);                                                                                    \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) af[m] = DG_KNRA(S, 0, m);                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);                                                    \
+    _Pragma("unroll") for (int m = 0; m < 8; ++m) {                                                        \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bf0[n], acc[m][n]);    \
+      if (m == 0) DG_KNRB(S, 1, bf1);                                                                      \
+      af[m] = DG_KNRA(S, 1, m);                                                                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                                                   \
+      if (m == 0) __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);                                       \
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                              \
     }                                                                                                      \
     _Pragma("unroll") for (int m = 0; m < 8; ++m)                                                          \
-      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bfr[n], acc[m][n]);    \
+      _Pragma("unroll") for (int n = 0; n < 4; ++n) acc[m][n] = mfma16x16x32(af[m], bf1[n], acc[m][n]);    \
   } while (0)
 #define DG_KNITER(SI, CUR)                                                                                 \
   do {                                                                                                     \
     const int s_ = (SI);                                                                                   \
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                                                             \
     __builtin_amdgcn_s_barrier();                                                                          \
-    DG_KNHALF(CUR, 0);                                                                                     \
-    DG_KNHALF(CUR, 1);                                                                                     \
+    DG_KNSTAGEMM(CUR);                                                                                     \
     __builtin_amdgcn_s_waitcnt(0xC07F);   /* lgkmcnt(0): this wave's reads of CUR are done */              \
     __builtin_amdgcn_s_barrier();                                                                          \
     __builtin_amdgcn_sched_barrier(0);                                                                     \
@@ -1225,8 +1250,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kn_kernel(GemmArgs g) {
     if (s < nst) {   // odd count: the last stage sits in S0; drain the ring
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       __builtin_amdgcn_s_barrier();
-      DG_KNHALF(S0, 0);
-      DG_KNHALF(S0, 1);
+      DG_KNSTAGEMM(S0);
     }
   };
   if (wnt) pipeline(std::true_type{});
@@ -1234,7 +1258,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kn_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(0);   // no DMA into LDS outlives the loop
 #undef DG_KNISSUE
 #undef DG_KNB
-#undef DG_KNHALF
+#undef DG_KNRA
+#undef DG_KNRB
+#undef DG_KNSTAGEMM
 #undef DG_KNITER
 
 #pragma unroll
