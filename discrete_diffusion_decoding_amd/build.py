@@ -2,7 +2,12 @@
 
 Every .hip under csrc/ is compiled to an object in parallel and linked into
 discrete_diffusion_decoding_amd/libdg.so.  Always rebuilds (a few seconds per
-file once the headers are cached by the compiler)."""
+file once the headers are cached by the compiler).
+
+build_host_asan() builds the same sources with AddressSanitizer on the host
+half of the compilation only (the GPU code is compiled as usual) into
+_build_asan/libdg_asan.so, for CPU tests of the host runtime: it is loaded
+with the sanitizer runtime preloaded and never ships."""
 from __future__ import annotations
 
 import os
@@ -41,9 +46,13 @@ def sources() -> list:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, obj_dir: str) -> str:
+# host-side AddressSanitizer: each -fsanitize= goes to the host compilation only
+HOST_ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def _compile(src: str, obj_dir: str, extra=()) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines()
                     if "packed-fp32-ops" not in l)
@@ -54,21 +63,44 @@ def _compile(src: str, obj_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    obj_dir = os.path.join(PKG, "_build")
+def _build(obj_dir: str, out: str, extra=(), verbose: bool = True) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
+
+
+def build(verbose: bool = True) -> str:
+    return _build(os.path.join(PKG, "_build"), LIB, (), verbose)
+
+
+def build_host_asan(verbose: bool = True) -> str:
+    """The library with AddressSanitizer on its host code.  The sanitizer
+    runtime is not linked in: load the library into a process started with
+    asan_runtime() in LD_PRELOAD."""
+    d = os.path.join(PKG, "_build_asan")
+    return _build(d, os.path.join(d, "libdg_asan.so"), HOST_ASAN_FLAGS, verbose)
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime."""
+    base = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "llvm", "lib", "clang")
+    for root in (base, "/opt/rocm/llvm/lib/clang"):
+        if os.path.isdir(root):
+            for v in sorted(os.listdir(root), reverse=True):
+                p = os.path.join(root, v, "lib", "linux", "libclang_rt.asan-x86_64.so")
+                if os.path.exists(p):
+                    return p
+    raise RuntimeError("the clang AddressSanitizer runtime (libclang_rt.asan-x86_64.so) was not found")
 
 
 if __name__ == "__main__":

@@ -11,7 +11,9 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
+# DG_LIBRARY may name another build of the same sources (the host-sanitizer
+# build that the CPU tests load); by default the in-tree libdg.so
+_LIB_PATH = os.environ.get("DG_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdg.so")
 
 DG_OK, DG_ERR_ARG, DG_ERR_SHAPE, DG_ERR_WORKSPACE, DG_ERR_HIP, DG_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 
