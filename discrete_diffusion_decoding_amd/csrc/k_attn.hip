@@ -64,6 +64,7 @@ __device__ __forceinline__ float xrow_sum(float v) {
 
 template <int HD, int GQ, int NW, int NF>
 __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
+  constexpr int APD = HD / 16 < 8 ? HD / 16 : 8;   // V^T blocks read ahead of the P V MFMAs
   constexpr int KS = HD / 32;          // 32-wide contraction steps of S over hd
   constexpr int NFD = HD / 16;         // 16-wide blocks of O over hd
   constexpr int CK = HD / 8;           // 16-byte slots per K row
@@ -251,12 +252,21 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_kernel(AttnArgs a) {
     _Pragma("unroll") for (int j = 0; j < NF; ++j) l_run[j] += ps_[j];                             \
   } while (0)
 
-// O += P V with V^T of the tile in stage S
+// O += P V with V^T of the tile in stage S.  The reads run APD blocks ahead of
+// the MFMAs (sched_group_barrier keeps that order): the compiler otherwise read
+// two V^T blocks, waited for them, and issued their MFMAs, exposing an LDS
+// round trip every two MFMAs
 #define DG_APV(S, PF)                                                                              \
   do {                                                                                             \
+    bf16x8 vb_[NFD];                                                                               \
+    _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf)                                             \
+      vb_[nf] = *reinterpret_cast<const bf16x8*>(&S[voff[nf & 1] + 512 * nf]);                     \
+    _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf)                                             \
+      _Pragma("unroll") for (int j = 0; j < NF; ++j) O[j][nf] = mfma16x16x32(PF[j], vb_[nf], O[j][nf]); \
+    __builtin_amdgcn_sched_group_barrier(0x100, APD, 0);                                           \
     _Pragma("unroll") for (int nf = 0; nf < NFD; ++nf) {                                           \
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&S[voff[nf & 1] + 512 * nf]);             \
-      _Pragma("unroll") for (int j = 0; j < NF; ++j) O[j][nf] = mfma16x16x32(PF[j], vb, O[j][nf]); \
+      __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);                                          \
+      if (nf + APD < NFD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                       \
     }                                                                                              \
   } while (0)
 
